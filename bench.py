@@ -1,0 +1,466 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged KV-cache attention step on one MI355X.
+
+A step is one pass of the whole hot path over one batch:
+slot addressing -> append of the step's new K/V rows -> decode attention
+(split-K partials + combine) and/or varlen prefill, per layer.  The default
+workload is the bandwidth-bound decode: 256 sequences with context
+U[1024, 8192], 32 query / 8 KV heads, head_dim 128, page 32, random page
+order, split-K on.  Inputs (pools, tables, queries, new rows) are resident
+in HBM before the timed region starts.
+
+Prints ONE JSON line.  ``value`` is the step's algorithmic HBM traffic
+divided by the measured step time (GB/s); ``roofline`` reports the
+dominant kernel (the split-K decode kernel) against the 8 TB/s HBM peak,
+timed with HIP events on the stream it runs on.  ``cpu_baseline`` times the
+CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+
+DESCRIPTIONS = {
+    "tiny_decode": "4 decode seqs, ctx {5,17,32,63}, Hq/Hkv/D 2/1/64, page 16, 32-page pool",
+    "qwen3_decode": "32 decode seqs, ctx U[128,1024], Hq/Hkv/D 32/8/128, page 32",
+    "mixed_step": "8 prompts U[64,256] + 56 decoders ctx U[256,2048], 32/8/128, page 32",
+    "large_decode": "256 decode seqs, ctx U[1024,8192], Hq/Hkv/D 32/8/128, page 32, split-K",
+    "window_shared": "64 decoders ctx U[512,4096] + 4 chunks of 128 after U[512,4096], "
+                     "8/1/256, page 32, window 512, 2 layers sharing the pool",
+    "long_prefill": "16 prompts U[1024,4096], 32/8/128, page 32 (prefill only)",
+}
+
+
+def _log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _src_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_kv_attention_mapped_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work
+# ---------------------------------------------------------------------------
+def decode_key_lens(wl):
+    L = wl.total_lens[:wl.n_decode].astype(np.int64)
+    return np.minimum(L, wl.window) if wl.window > 0 else L
+
+
+def decode_kernel_bytes(wl) -> int:
+    """K/V rows attended + q + table entries + lengths (the split kernel's inputs)."""
+    le = decode_key_lens(wl)
+    kv = int(le.sum()) * wl.num_kv_heads * wl.head_dim * 2 * 2
+    q = wl.n_decode * wl.num_q_heads * wl.head_dim * 2
+    # pages holding allowed keys (window start page to the last page)
+    L = wl.total_lens[:wl.n_decode].astype(np.int64)
+    first = np.maximum(0, L - wl.window) if wl.window > 0 else np.zeros_like(L)
+    pages = -(-L // wl.page_size) - first // wl.page_size
+    return kv + q + 4 * int(pages.sum()) + 4 * wl.n_decode
+
+
+def decode_bytes(wl) -> int:
+    return decode_kernel_bytes(wl) + wl.n_decode * wl.num_q_heads * wl.head_dim * 2  # + out
+
+
+def append_bytes(wl) -> int:
+    T = int(wl.new_lens.sum())
+    return 2 * 2 * T * wl.num_kv_heads * wl.head_dim * 2 + 4 * T + 4 * T  # rows r+w, slots w+r
+
+
+def prefill_flops(wl) -> int:
+    """4 * D * Hq * (number of (row, key) pairs the masks allow)."""
+    pairs = 0
+    for s in wl.prefill_ids():
+        lq, lk = int(wl.new_lens[s]), int(wl.total_lens[s])
+        pos = np.arange(lk - lq, lk)
+        cnt = pos + 1
+        if wl.window > 0:
+            cnt = np.minimum(cnt, wl.window)
+        pairs += int(cnt.sum())
+    return 4 * wl.head_dim * wl.num_q_heads * pairs
+
+
+def prefill_bytes(wl) -> int:
+    s = wl.prefill_ids()
+    tq = int(wl.new_lens[s].sum())
+    kv = int(wl.total_lens[s].sum()) * wl.num_kv_heads * wl.head_dim * 2 * 2
+    return kv + 2 * tq * wl.num_q_heads * wl.head_dim * 2
+
+
+# ---------------------------------------------------------------------------
+# the step on the GPU
+# ---------------------------------------------------------------------------
+class Step:
+    def __init__(self, wl, torch, P):
+        self.wl, self.torch, self.P = wl, torch, P
+        dev = torch.device("cuda")
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)  # noqa: E731
+        bits = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).to(dev)  # noqa: E731
+        shape = (wl.num_kv_heads, wl.num_slots, wl.head_dim)
+        self.k_pool = torch.full(shape, 0x7FC0, dtype=torch.int16, device=dev)
+        self.v_pool = torch.full(shape, 0x7FC0, dtype=torch.int16, device=dev)
+        self.bt = i32(wl.block_tables)
+        # cached context, written once (not timed)
+        for i in range(0, wl.num_seqs, 32):
+            sub = np.arange(i, min(wl.num_seqs, i + 32))
+            wl.cache_all_kv(sub)
+            k, v, lq, lk = wl.packed_tokens("prefix", sub)
+            nk, nv, _, _ = wl.packed_tokens("new", sub)
+            self._keep_new = getattr(self, "_keep_new", []) + [(nk, nv)]
+            for s in sub:
+                wl._kv_cache.pop(int(s), None)
+            if k.shape[0]:
+                slots = P.slot_mapping(i32(wl.block_tables[sub]), i32(wl.cu_lens(lq)),
+                                       i32(wl.cu_lens(lk)), page_size=wl.page_size,
+                                       num_pages=wl.num_pages, total_tokens=k.shape[0])
+                P.append(bits(k), bits(v), slots, self.k_pool, self.v_pool)
+        torch.cuda.synchronize()
+        nk = np.concatenate([a for a, _ in self._keep_new])
+        nv = np.concatenate([b for _, b in self._keep_new])
+        del self._keep_new
+        # this step's new rows and their addressing inputs
+        self.k_new, self.v_new = bits(nk), bits(nv)
+        self.T = nk.shape[0]
+        self.cu_new_q = i32(wl.cu_lens(wl.new_lens))
+        self.cu_new_k = i32(wl.cu_lens(wl.total_lens))
+        self.slots = torch.empty(self.T, dtype=torch.int32, device=dev)
+        # decode
+        self.B = wl.n_decode
+        if self.B:
+            lens = wl.decode_seq_lens()
+            self.seq_lens = i32(lens)
+            self.max_len = int(lens.max())
+            self.bt_dec = i32(wl.block_tables[:self.B])
+            self.S, self.pps = P.decode_plan(self.B, wl.num_kv_heads, wl.page_size, self.max_len,
+                                             wl.window)
+            hq, d = wl.num_q_heads, wl.head_dim
+            self.part = (torch.empty((self.B, hq, self.S), dtype=torch.float32, device=dev),
+                         torch.empty((self.B, hq, self.S), dtype=torch.float32, device=dev),
+                         torch.empty((self.B, hq, self.S, d), dtype=torch.float32, device=dev))
+            self.out_dec = torch.empty((self.B, hq, d), dtype=torch.bfloat16, device=dev)
+        # prefill
+        self.N = wl.n_prefill
+        if self.N:
+            seqs = wl.prefill_ids()
+            self.bt_pre = i32(wl.block_tables[seqs])
+            self.cu_q = i32(wl.prefill_cu_q())
+            self.cu_k = i32(wl.prefill_cu_k())
+            self.max_q = int(wl.new_lens[seqs].max())
+            self.max_k = int(wl.total_lens[seqs].max())
+            self.out_pre = torch.empty((wl.total_q(), wl.num_q_heads, wl.head_dim),
+                                       dtype=torch.bfloat16, device=dev)
+        self.q = []
+        for layer in range(wl.num_layers):
+            qd, qp = wl.queries(layer)
+            self.q.append((bits(qd), bits(qp)))
+
+    def run(self, ev=None):
+        """One step.  ``ev`` = (before, after) events bracketing the layer-0 decode kernel."""
+        P, wl = self.P, self.wl
+        P.slot_mapping(self.bt, self.cu_new_q, self.cu_new_k, page_size=wl.page_size,
+                       num_pages=wl.num_pages, total_tokens=self.T, out=self.slots)
+        P.append(self.k_new, self.v_new, self.slots, self.k_pool, self.v_pool)
+        for layer in range(wl.num_layers):
+            qd, qp = self.q[layer]
+            if self.B:
+                if ev is not None and layer == 0:
+                    ev[0].record()
+                if self.S > 1:
+                    P.decode_split(qd, self.k_pool, self.v_pool, self.bt_dec, self.seq_lens,
+                                   self.max_len, page_size=wl.page_size, num_splits=self.S,
+                                   pages_per_split=self.pps, scale=wl.scale, window=wl.window,
+                                   out=self.part)
+                    if ev is not None and layer == 0:
+                        ev[1].record()
+                    P.decode_combine(*self.part, out=self.out_dec)
+                else:
+                    P.decode(qd, self.k_pool, self.v_pool, self.bt_dec, self.seq_lens,
+                             self.max_len, page_size=wl.page_size, scale=wl.scale,
+                             window=wl.window, num_splits=1, out=self.out_dec)
+                    if ev is not None and layer == 0:
+                        ev[1].record()
+            if self.N:
+                P.prefill_varlen(qp, self.k_pool, self.v_pool, self.bt_pre, self.cu_q, self.cu_k,
+                                 self.max_q, self.max_k, page_size=wl.page_size, scale=wl.scale,
+                                 window=wl.window, out=self.out_pre)
+
+    def run_prefill(self):
+        wl = self.wl
+        self.P.prefill_varlen(self.q[0][1], self.k_pool, self.v_pool, self.bt_pre, self.cu_q,
+                              self.cu_k, self.max_q, self.max_k, page_size=wl.page_size,
+                              scale=wl.scale, window=wl.window, out=self.out_pre)
+
+
+def step_bytes(wl) -> int:
+    b = append_bytes(wl)
+    if wl.n_decode:
+        b += wl.num_layers * decode_bytes(wl)
+    if wl.n_prefill:
+        b += wl.num_layers * prefill_bytes(wl)
+    return b
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline (bounded sample)
+# ---------------------------------------------------------------------------
+def cpu_baseline(wl, budget_s: float, max_seqs: int):
+    """Time the oracle on whole sequences of the workload until ``budget_s``.
+
+    Each sampled sequence gets a pool of its own holding just its pages (the
+    pages keep their relative order), filled with its cached context outside
+    the timed region; the timed part is that sequence's share of the step:
+    slot mapping + append of its new token + float64 decode attention.
+    """
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    cores = len(os.sched_getaffinity(0))
+    rng = np.random.default_rng(7)
+    ids = wl.decode_ids() if wl.n_decode else wl.prefill_ids()
+    order = rng.permutation(ids)[:max_seqs]
+    wl.cache_all_kv(order)
+    qd, qp = wl.queries(0)
+    done, t_total = [], 0.0
+    for s in order:
+        s = int(s)
+        npg = -(-int(wl.total_lens[s]) // wl.page_size)
+        phys = wl.block_tables[s, :npg]
+        bt = np.argsort(np.argsort(phys)).astype(np.int32)[None, :]
+        shape = (wl.num_kv_heads, npg * wl.page_size, wl.head_dim)
+        kp = np.full(shape, 0x7FC0, np.uint16)
+        vp = kp.copy()
+        k, v, lq, lk = wl.packed_tokens("prefix", [s])
+        if k.shape[0]:
+            kp, vp = oracle.append(kp, vp, k, v, oracle.slot_mapping(
+                bt, wl.cu_lens(lq), wl.cu_lens(lk), wl.page_size))
+        nk, nv, lq, lk = wl.packed_tokens("new", [s])
+        t0 = time.perf_counter()
+        slots = oracle.slot_mapping(bt, wl.cu_lens(lq), wl.cu_lens(lk), wl.page_size)
+        kp, vp = oracle.append(kp, vp, nk, nv, slots)
+        if s < wl.n_decode:
+            oracle.decode(qd[[s]], kp, vp, bt, wl.total_lens[[s]], wl.page_size, wl.scale,
+                          wl.window)
+        t_total += time.perf_counter() - t0
+        done.append(s)
+        if t_total > budget_s:
+            break
+    wl.drop_kv()
+    sub = _subset(wl, done)
+    bytes_done = append_bytes(sub) + (decode_bytes(sub) if sub.n_decode else 0)
+    return {
+        "value": round(bytes_done / t_total / 1e9, 6),
+        "unit": "GB/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": (f"{len(done)} of {wl.num_seqs} sequences of {wl.name}, each timed for its "
+                   f"share of the step (slot mapping + append + float64 decode attention); "
+                   f"{t_total:.1f} s of oracle work; {cores} host cores available, "
+                   f"BLAS threads {blas_threads}"),
+        "seconds": round(t_total, 3),
+        "tokens_per_s": round(len(done) / t_total, 4),
+    }
+
+
+def _subset(wl, seqs):
+    import copy
+    sub = copy.copy(wl)
+    seqs = np.asarray(sorted(seqs))
+    dec = seqs[seqs < wl.n_decode]
+    pre = seqs[seqs >= wl.n_decode]
+    keep = np.concatenate([dec, pre])
+    sub.prefix_lens = wl.prefix_lens[keep]
+    sub.new_lens = wl.new_lens[keep]
+    sub.block_tables = wl.block_tables[keep]
+    sub.n_decode, sub.n_prefill = len(dec), len(pre)
+    return sub
+
+
+# ---------------------------------------------------------------------------
+# measured traffic (rocprofv3 counters, recorded under profiles/)
+# ---------------------------------------------------------------------------
+def recorded_traffic(config: str, src_hash: str):
+    path = os.path.join(ROOT, "profiles", f"{config}_decode_split_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != src_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+def prefill_measure(torch, P, iters=20, warmup=5):
+    import workloads as W
+    wl = W.make("long_prefill")
+    st = Step(wl, torch, P)
+    for _ in range(warmup):
+        st.run_prefill()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        st.run_prefill()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / iters
+    fl = prefill_flops(wl)
+    tf = fl / (ms * 1e-3) / 1e12
+    del st
+    torch.cuda.empty_cache()
+    return {"workload": "long_prefill: " + DESCRIPTIONS["long_prefill"], "ms_per_call": round(ms, 4),
+            "tflops": round(tf, 2), "peak_tflops": BF16_PEAK_TFLOPS,
+            "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4), "flops_per_call": fl}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="large_decode", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the long-prefill MFMA measurement")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if world != 1:
+        print(json.dumps({"error": "single-GPU build: launch without a multi-rank launcher"}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_attention_mapped_amd as P
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(1)
+    P.lib()
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n, "launches": 3}), flush=True)
+        return
+
+    wl = W.make(args.config)
+    _log(f"[bench] setting up {args.config}: {DESCRIPTIONS[args.config]}")
+    t0 = time.perf_counter()
+    st = Step(wl, torch, P)
+    _log(f"[bench] set-up done in {time.perf_counter() - t0:.1f} s; warmup {args.warmup}, steps {args.steps}")
+
+    for _ in range(args.warmup):
+        st.run()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        st.run(evs[i] if st.B else None)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+    _log(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step")
+
+    sb = step_bytes(wl)
+    value = sb / (ms_step * 1e-3) / 1e9
+    out = {
+        "metric": "paged-decode achieved HBM GB/s (% of peak) + decode tokens/s; prefill MFMA %",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: {DESCRIPTIONS[args.config]}",
+                   "seed": wl.seed, "step_bytes": sb},
+        "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+    }
+    if st.B:
+        kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        kb = decode_kernel_bytes(wl)
+        ach = kb / (kern_ms * 1e-3) / 1e9
+        src_hash = _src_hash("decode.hip", "common.h")
+        traffic = recorded_traffic(args.config, src_hash)
+        out["decode_tokens_per_s"] = round(st.B / (ms_step * 1e-3), 1)
+        out["decode_plan"] = {"num_splits": st.S, "pages_per_split": st.pps}
+        out["roofline"] = {
+            "kernel": "decode_kernel (split-K partials)" if st.S > 1 else "decode_kernel (direct)",
+            "bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "avg_kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": kb,
+            "kernel_source_sha256_16": src_hash,
+        }
+    if st.N and not st.B:
+        fl = prefill_flops(wl) * wl.num_layers
+        tf = fl / (ms_step * 1e-3) / 1e12
+        out["roofline"] = {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tf, 3),
+                           "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    del st
+    torch.cuda.empty_cache()
+
+    if not args.no_prefill and args.config != "long_prefill":
+        _log("[bench] long-prefill MFMA measurement")
+        out["prefill"] = prefill_measure(torch, P)
+    if not args.no_cpu_baseline:
+        _log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s)")
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, 64)
+    out["gpu"] = torch.cuda.get_device_name(0)
+    out["host"] = platform.node()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,223 @@
+/*
+ * pkv.h -- paged KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * A stateless C ABI.  Every buffer is caller-owned device memory on the
+ * current HIP device; the library allocates nothing, never synchronises and
+ * never reads device memory from the host.  All work is enqueued on the
+ * caller's stream and is asynchronous.  Calls are thread-safe.
+ *
+ * Data types.  bf16 values travel as their 16-bit patterns (uint16_t).
+ * Tables and lengths are int32.  Output rows are rounded to bf16 with
+ * round-to-nearest-even.
+ *
+ * Pool layout.  K and V each live in one tensor [Hkv, num_pages*page_size, D]
+ * (row-major): for every KV head, all pages back to back, a page being
+ * page_size consecutive token rows of D elements.  This is the single
+ * contiguous cache with a (sequence, logical block) -> physical page table
+ * that the rollout-engine pages describe (scripts/benchmarks commit log
+ * 1847125, flex_attention paged-KV engine entry, "Why this works" item 1).
+ * Pool row ("slot") s of head h starts at element (h*num_slots + s)*D.
+ *
+ * Block tables.  int32 [num_seqs, max_pages_per_seq], row-major; entry
+ * [b][j] is the physical page holding logical tokens j*page_size ..
+ * (j+1)*page_size-1 of sequence b.  Entries past ceil(len/page_size) are
+ * never read.
+ *
+ * Masks.  Attention is causal.  window > 0 adds the sliding rule
+ * q_pos - kv_pos < window, a strict less-than; window <= 0 is pure causal
+ * (commit log 1847125, the entry that builds one block mask per attention
+ * regime).  Query head h reads KV head h / (Hq/Hkv).
+ *
+ * Supported shapes: head_dim in {64, 128, 256}; page_size in {16, 32};
+ * Hq a multiple of Hkv with Hq/Hkv <= 8.  Anything else returns
+ * PKV_ERR_UNSUPPORTED before any HIP call.
+ *
+ * Errors.  Problems the host can see (null pointers, shapes, sizes) return
+ * a status before anything is enqueued.  Contents of device arrays (slot
+ * numbers, table entries, lengths) are the caller's contract and cannot be
+ * checked without a synchronisation: kernels skip or clamp anything out of
+ * range so that no access leaves the buffers, but the results for such rows
+ * are unspecified.  A failed launch returns PKV_ERR_HIP.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t pkv_status;
+
+enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL_ARG = 1,             /* a required pointer is NULL                     */
+  PKV_ERR_BAD_SHAPE = 2,            /* a size or count is out of range or inconsistent */
+  PKV_ERR_UNSUPPORTED = 3,          /* head_dim / page_size / grouping not built       */
+  PKV_ERR_WORKSPACE_TOO_SMALL = 4,  /* split-K workspace smaller than required         */
+  PKV_ERR_HIP = 5                   /* a kernel launch failed                          */
+};
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* pkv_status_string(pkv_status s);
+
+/*
+ * Slot addressing: the physical pool row of every new token.
+ *
+ * Sequence j contributes Lq_j = cu_seq_lens_q[j+1]-cu_seq_lens_q[j] new
+ * tokens and holds Lk_j = cu_seq_lens_k[j+1]-cu_seq_lens_k[j] tokens once
+ * they are cached; its token r is logical position p = Lk_j - Lq_j + r and
+ * goes to slot block_tables[j][p/page_size]*page_size + p%page_size.  This
+ * is the address of the engine's in-kernel cache write (commit log 1847125,
+ * flex_attention paged-KV engine entry, "Files"); the packing follows the
+ * varlen cu_seq_lens convention (CB sync-driver commit 5f3e1c9,
+ * "qwen3_grpo_unified.py fixes").
+ *
+ *   block_tables   int32 [num_seqs, max_pages_per_seq]     (device, read)
+ *   cu_seq_lens_q  int32 [num_seqs+1], [0] = 0              (device, read)
+ *   cu_seq_lens_k  int32 [num_seqs+1], [0] = 0              (device, read)
+ *   slot_mapping   int32 [total_tokens] = cu_seq_lens_q[num_seqs] (device, written)
+ *
+ * A token whose page index or table entry is out of range gets slot -1
+ * (which pkv_append skips).  total_tokens may be 0 (nothing is enqueued).
+ */
+pkv_status pkv_slot_mapping(const int32_t* block_tables, int32_t max_pages_per_seq,
+                            const int32_t* cu_seq_lens_q, const int32_t* cu_seq_lens_k,
+                            int32_t num_seqs, int32_t total_tokens,
+                            int32_t page_size, int32_t num_pages,
+                            int32_t* slot_mapping, hipStream_t stream);
+
+/*
+ * Append: bit-exact copy of new K/V rows into their pool slots,
+ * k_pool[h, slot_mapping[t], :] = k_new[t, h, :] (and V), for every KV head.
+ *
+ *   k_new, v_new   bf16 [num_tokens, num_kv_heads, head_dim]   (device, read)
+ *   slot_mapping   int32 [num_tokens]; a slot < 0 or >= num_slots is skipped
+ *   k_pool, v_pool bf16 [num_kv_heads, num_slots, head_dim]    (device, written)
+ *
+ * Two tokens with the same slot in one call give an unspecified row.
+ * num_tokens may be 0.
+ */
+pkv_status pkv_append(const uint16_t* k_new, const uint16_t* v_new,
+                      const int32_t* slot_mapping, int32_t num_tokens,
+                      int32_t num_kv_heads, int32_t head_dim,
+                      uint16_t* k_pool, uint16_t* v_pool, int64_t num_slots,
+                      hipStream_t stream);
+
+/*
+ * Decode planning.  pkv_decode splits each row's keys into num_splits
+ * partitions of pages_per_split logical pages (flash-decoding); the plan
+ * depends only on host scalars.  num_splits_requested = 0 picks a count from
+ * the grid size; 1 disables splitting.  Writes the plan through the two
+ * output pointers (either may be NULL).
+ */
+pkv_status pkv_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t page_size,
+                           int32_t max_seq_len, int32_t window, int32_t num_splits_requested,
+                           int32_t* num_splits, int32_t* pages_per_split);
+
+/* Bytes of split-K workspace pkv_decode needs for this plan (0 when it does not split). */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t num_kv_heads, int32_t page_size, int32_t max_seq_len,
+                                  int32_t window, int32_t num_splits_requested);
+
+/*
+ * Decode attention: one query row per sequence, GQA over the paged pool.
+ * Row b sits at position seq_lens[b]-1 and attends keys 0..seq_lens[b]-1
+ * (its own new token included, appended beforehand), restricted by the
+ * window when window > 0.  The engine's decode step runs this attention
+ * over physical pages through the block table (commit log 1847125,
+ * flex_attention paged-KV engine entry, "Why this works" items 1-2).
+ *
+ *   q              bf16 [num_seqs, num_q_heads, head_dim]       (device, read)
+ *   k_pool, v_pool bf16 [num_kv_heads, num_pages*page_size, head_dim]
+ *   block_tables   int32 [num_seqs, max_pages_per_seq]
+ *   seq_lens       int32 [num_seqs]; 0 <= len <= min(max_seq_len, max_pages_per_seq*page_size)
+ *   scale          score multiplier (typically 1/sqrt(head_dim))
+ *   workspace      device scratch of pkv_decode_workspace_bytes(...) bytes;
+ *                  may be NULL when that is 0
+ *   out            bf16 [num_seqs, num_q_heads, head_dim]       (device, written)
+ *
+ * A row with no key (seq_lens[b] == 0) is written as zeros.  Results are
+ * deterministic and independent of the physical page order.
+ */
+pkv_status pkv_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                      const int32_t* block_tables, int32_t max_pages_per_seq,
+                      const int32_t* seq_lens, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t page_size, int32_t num_pages, int32_t max_seq_len,
+                      float scale, int32_t window, int32_t num_splits,
+                      void* workspace, size_t workspace_bytes,
+                      uint16_t* out, hipStream_t stream);
+
+/*
+ * Decode, split-K half: for split s of row b, over the allowed keys on
+ * logical pages [p0 + s*pages_per_split, p0 + (s+1)*pages_per_split) where
+ * p0 is the page of the row's first allowed key (0 without a window),
+ * writes in float32
+ *   part_m[b, h, s]    = log2(e) * max_i x_i          (-inf if the split is empty)
+ *   part_l[b, h, s]    = sum_i exp(x_i - max)         (0 if empty)
+ *   part_acc[b, h, s, :] = sum_i exp(x_i - max) v_i   (0 if empty)
+ * with x_i = scale * (k_i . q).  Arrays: part_m, part_l [num_seqs,
+ * num_q_heads, num_splits]; part_acc [num_seqs, num_q_heads, num_splits,
+ * head_dim].  Splits beyond a row's pages are written as empty.
+ * num_splits * pages_per_split must cover the longest row's key pages.
+ */
+pkv_status pkv_decode_split(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                            const int32_t* block_tables, int32_t max_pages_per_seq,
+                            const int32_t* seq_lens, int32_t num_seqs,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t page_size, int32_t num_pages, int32_t max_seq_len,
+                            float scale, int32_t window,
+                            int32_t num_splits, int32_t pages_per_split,
+                            float* part_m, float* part_l, float* part_acc,
+                            hipStream_t stream);
+
+/*
+ * Decode, combine half: merges the partials of pkv_decode_split in a fixed
+ * split order, out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s with
+ * M = max_s m_s; a row whose splits are all empty is written as zeros.
+ *   out  bf16 [num_seqs, num_q_heads, head_dim]
+ */
+pkv_status pkv_decode_combine(const float* part_m, const float* part_l, const float* part_acc,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                              int32_t num_splits, uint16_t* out, hipStream_t stream);
+
+/*
+ * Varlen causal prefill over the paged pool.  Query rows of num_seqs
+ * sequences are packed back to back: rows cu_seq_lens_q[j] ..
+ * cu_seq_lens_q[j+1]-1 belong to sequence j, whose K/V are its first
+ * Lk_j = cu_seq_lens_k[j+1]-cu_seq_lens_k[j] cached tokens (this step's
+ * rows appended beforehand).  Row r of sequence j sits at position
+ * Lk_j - Lq_j + r (bottom-right alignment, so a chunk after a cached prefix
+ * sees the prefix).  The cu_seq_lens_q/k and host max_seqlen_q/k arguments
+ * follow the varlen interface the CB paged kernel takes on every forward
+ * (CB sync-driver commit 5f3e1c9, "qwen3_grpo_unified.py fixes"; benchmarks
+ * README, "Flash Attention 4 on Blackwell (sm_100)" item 2).
+ *
+ *   q              bf16 [total_q, num_q_heads, head_dim]        (device, read)
+ *   block_tables   int32 [num_seqs, max_pages_per_seq]
+ *   cu_seq_lens_q  int32 [num_seqs+1], cu_seq_lens_k int32 [num_seqs+1]
+ *   max_seqlen_q   >= every Lq_j (host); max_seqlen_k >= every Lk_j (host)
+ *   out            bf16 [total_q, num_q_heads, head_dim]        (device, written)
+ *
+ * Caller contract: 0 <= Lq_j <= Lk_j <= max_pages_per_seq*page_size.
+ */
+pkv_status pkv_prefill_varlen(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                              const int32_t* block_tables, int32_t max_pages_per_seq,
+                              const int32_t* cu_seq_lens_q, const int32_t* cu_seq_lens_k,
+                              int32_t num_seqs, int32_t total_q,
+                              int32_t max_seqlen_q, int32_t max_seqlen_k,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t page_size, int32_t num_pages,
+                              float scale, int32_t window,
+                              uint16_t* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

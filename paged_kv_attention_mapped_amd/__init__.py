@@ -1,0 +1,275 @@
+"""Paged KV-cache attention for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of ``libpkv.so`` (declared in
+``include/pkv.h``).  It only marshals arguments: every step of the path runs
+in the HIP kernels of that library.  Torch provides device memory (tensors)
+and the stream (the current torch stream); bf16 data may be passed as
+``torch.bfloat16`` or as its 16-bit patterns in ``torch.int16``/``uint16``.
+
+The library is loaded after torch so that both use torch's HIP runtime.
+If it has not been built (``python -m paged_kv_attention_mapped_amd.build``),
+every call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "PkvError",
+    "append",
+    "decode",
+    "decode_combine",
+    "decode_plan",
+    "decode_split",
+    "decode_workspace_bytes",
+    "exported_symbols",
+    "lib",
+    "lib_path",
+    "prefill_varlen",
+    "slot_mapping",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+EXPORTS = (
+    "pkv_status_string",
+    "pkv_slot_mapping",
+    "pkv_append",
+    "pkv_decode_plan",
+    "pkv_decode_workspace_bytes",
+    "pkv_decode",
+    "pkv_decode_split",
+    "pkv_decode_combine",
+    "pkv_prefill_varlen",
+)
+
+
+class PkvError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed with status {status} ({msg})")
+        self.status = status
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+_SIGS = {
+    "pkv_status_string": ([_I32], ctypes.c_char_p),
+    "pkv_slot_mapping": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _P], _I32),
+    "pkv_append": ([_P, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P], _I32),
+    "pkv_decode_plan": ([_I32, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
+    "pkv_decode_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
+    "pkv_decode": ([_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                    _F, _I32, _I32, _P, _SZ, _P, _P], _I32),
+    "pkv_decode_split": ([_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                          _F, _I32, _I32, _I32, _P, _P, _P, _P], _I32),
+    "pkv_decode_combine": ([_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P], _I32),
+    "pkv_prefill_varlen": ([_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                            _I32, _I32, _I32, _F, _I32, _P, _P], _I32),
+}
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded ``libpkv.so`` (loaded on first use; raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(
+                f"{_LIB_PATH} is missing: build it with "
+                "`python -m paged_kv_attention_mapped_amd.build` (there is no fallback path)")
+        handle = ctypes.CDLL(_LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def exported_symbols():
+    """Names of the C ABI entry points the loaded library exports."""
+    h = lib()
+    return [n for n in EXPORTS if hasattr(h, n)]
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _check(fn: str, status: int):
+    if status != 0:
+        msg = lib().pkv_status_string(status).decode()
+        raise PkvError(fn, status, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _bf16(t, name):
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name}: expected bf16 data (bfloat16 or 16-bit patterns), got {t.dtype}")
+
+
+def _i32(t, name):
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name}: expected int32, got {t.dtype}")
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def slot_mapping(block_tables, cu_seq_lens_q, cu_seq_lens_k, *, page_size, num_pages,
+                 total_tokens, out=None, stream=None):
+    """Pool row of every new token (``pkv_slot_mapping``); returns int32 [total_tokens]."""
+    _i32(block_tables, "block_tables"); _i32(cu_seq_lens_q, "cu_q"); _i32(cu_seq_lens_k, "cu_k")
+    if out is None:
+        out = torch.empty(total_tokens, dtype=torch.int32, device=block_tables.device)
+    _dev(block_tables, cu_seq_lens_q, cu_seq_lens_k, out)
+    num_seqs = cu_seq_lens_q.numel() - 1
+    _check("pkv_slot_mapping", lib().pkv_slot_mapping(
+        _ptr(block_tables), block_tables.shape[1], _ptr(cu_seq_lens_q), _ptr(cu_seq_lens_k),
+        num_seqs, total_tokens, page_size, num_pages, _ptr(out), _stream(stream)))
+    return out
+
+
+def append(k_new, v_new, slot_mapping, k_pool, v_pool, stream=None):
+    """Bit-exact copy of ``[T, Hkv, D]`` rows into ``[Hkv, num_slots, D]`` pools (``pkv_append``)."""
+    _bf16(k_new, "k_new"); _bf16(v_new, "v_new"); _bf16(k_pool, "k_pool"); _bf16(v_pool, "v_pool")
+    _i32(slot_mapping, "slot_mapping")
+    _dev(k_new, v_new, slot_mapping, k_pool, v_pool)
+    T, hkv, d = k_new.shape
+    if v_new.shape != k_new.shape or k_pool.shape != v_pool.shape:
+        raise ValueError("shape mismatch")
+    if k_pool.shape[0] != hkv or k_pool.shape[2] != d or slot_mapping.numel() < T:
+        raise ValueError("pool / slot_mapping shape mismatch")
+    _check("pkv_append", lib().pkv_append(
+        _ptr(k_new), _ptr(v_new), _ptr(slot_mapping), T, hkv, d, _ptr(k_pool), _ptr(v_pool),
+        k_pool.shape[1], _stream(stream)))
+
+
+def decode_plan(num_seqs, num_kv_heads, page_size, max_seq_len, window=0, num_splits=0):
+    """``(num_splits, pages_per_split)`` that ``decode`` uses (``pkv_decode_plan``)."""
+    s, p = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("pkv_decode_plan", lib().pkv_decode_plan(
+        num_seqs, num_kv_heads, page_size, max_seq_len, window, num_splits,
+        ctypes.byref(s), ctypes.byref(p)))
+    return s.value, p.value
+
+
+def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, num_kv_heads, page_size,
+                           max_seq_len, window=0, num_splits=0):
+    return int(lib().pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, num_kv_heads,
+                                                page_size, max_seq_len, window, num_splits))
+
+
+def _pool_shape(k_pool, page_size):
+    hkv, slots, d = k_pool.shape
+    if slots % page_size:
+        raise ValueError("pool rows must be a multiple of page_size")
+    return hkv, slots // page_size, d
+
+
+def decode(q, k_pool, v_pool, block_tables, seq_lens, max_seq_len, *, page_size, scale=None,
+           window=0, num_splits=0, workspace=None, out=None, stream=None):
+    """GQA decode attention over the paged pool (``pkv_decode``); returns bf16 [B, Hq, D]."""
+    _bf16(q, "q"); _bf16(k_pool, "k_pool"); _bf16(v_pool, "v_pool")
+    _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
+    B, hq, d = q.shape
+    hkv, num_pages, d2 = _pool_shape(k_pool, page_size)
+    if d2 != d or v_pool.shape != k_pool.shape or block_tables.shape[0] < B or seq_lens.numel() < B:
+        raise ValueError("shape mismatch")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=q.device)
+    need = decode_workspace_bytes(B, hq, d, hkv, page_size, max_seq_len, window, num_splits)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _dev(q, k_pool, v_pool, block_tables, seq_lens, out, workspace)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pkv_decode", lib().pkv_decode(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
+        _ptr(seq_lens), B, hq, hkv, d, page_size, num_pages, max_seq_len, float(scale), window,
+        num_splits, _ptr(workspace), wsb, _ptr(out), _stream(stream)))
+    return out
+
+
+def decode_split(q, k_pool, v_pool, block_tables, seq_lens, max_seq_len, *, page_size,
+                 num_splits, pages_per_split, scale=None, window=0, out=None, stream=None):
+    """Split-K partials (``pkv_decode_split``): returns ``(m, l, acc)`` float32."""
+    _bf16(q, "q"); _bf16(k_pool, "k_pool"); _bf16(v_pool, "v_pool")
+    _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
+    B, hq, d = q.shape
+    hkv, num_pages, _ = _pool_shape(k_pool, page_size)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out is None:
+        dev = q.device
+        out = (torch.empty((B, hq, num_splits), dtype=torch.float32, device=dev),
+               torch.empty((B, hq, num_splits), dtype=torch.float32, device=dev),
+               torch.empty((B, hq, num_splits, d), dtype=torch.float32, device=dev))
+    m, l, acc = out
+    _dev(q, k_pool, v_pool, block_tables, seq_lens, m, l, acc)
+    _check("pkv_decode_split", lib().pkv_decode_split(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
+        _ptr(seq_lens), B, hq, hkv, d, page_size, num_pages, max_seq_len, float(scale), window,
+        num_splits, pages_per_split, _ptr(m), _ptr(l), _ptr(acc), _stream(stream)))
+    return m, l, acc
+
+
+def decode_combine(m, l, acc, out=None, stream=None):
+    """Merge split-K partials (``pkv_decode_combine``); returns bf16 [B, Hq, D]."""
+    B, hq, S, d = acc.shape
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=acc.device)
+    _dev(m, l, acc, out)
+    _check("pkv_decode_combine", lib().pkv_decode_combine(
+        _ptr(m), _ptr(l), _ptr(acc), B, hq, d, S, _ptr(out), _stream(stream)))
+    return out
+
+
+def prefill_varlen(q, k_pool, v_pool, block_tables, cu_seq_lens_q, cu_seq_lens_k,
+                   max_seqlen_q, max_seqlen_k, *, page_size, scale=None, window=0, out=None,
+                   stream=None):
+    """Varlen causal prefill over the paged pool (``pkv_prefill_varlen``); returns bf16 [Tq, Hq, D]."""
+    _bf16(q, "q"); _bf16(k_pool, "k_pool"); _bf16(v_pool, "v_pool")
+    _i32(block_tables, "block_tables"); _i32(cu_seq_lens_q, "cu_q"); _i32(cu_seq_lens_k, "cu_k")
+    Tq, hq, d = q.shape
+    hkv, num_pages, _ = _pool_shape(k_pool, page_size)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out is None:
+        out = torch.empty((Tq, hq, d), dtype=torch.bfloat16, device=q.device)
+    _dev(q, k_pool, v_pool, block_tables, cu_seq_lens_q, cu_seq_lens_k, out)
+    n = cu_seq_lens_q.numel() - 1
+    _check("pkv_prefill_varlen", lib().pkv_prefill_varlen(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
+        _ptr(cu_seq_lens_q), _ptr(cu_seq_lens_k), n, Tq, max_seqlen_q, max_seqlen_k, hq, hkv, d,
+        page_size, num_pages, float(scale), window, _ptr(out), _stream(stream)))
+    return out

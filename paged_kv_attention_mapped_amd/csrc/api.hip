@@ -1,0 +1,278 @@
+// C ABI: host-side validation, split-K planning and kernel dispatch.
+// Every check here runs before anything is enqueued, and nothing here
+// touches device memory from the host or synchronises.
+#include <math.h>
+
+#include "../../include/pkv.h"
+#include "common.h"
+
+using namespace pkv;
+
+namespace {
+
+bool supported_dim(int d) { return d == 64 || d == 128 || d == 256; }
+bool supported_ps(int ps) { return ps == 16 || ps == 32; }
+
+pkv_status check_heads(int hq, int hkv) {
+  if (hq <= 0 || hkv <= 0) return PKV_ERR_BAD_SHAPE;
+  if (hq % hkv != 0) return PKV_ERR_BAD_SHAPE;
+  if (hq / hkv > 8) return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+pkv_status hip_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_HIP; }
+
+constexpr int kTargetWorkgroups = 1024;  // enough to fill 256 CUs several times over
+constexpr int kMaxPagesPerSplit = 32;
+constexpr int kMinPagesPerSplit = 4;
+
+// Pages a row's allowed keys can span.
+int64_t key_pages(int page_size, int max_seq_len, int window) {
+  int64_t pages = (max_seq_len + (int64_t)page_size - 1) / page_size;
+  if (window > 0) {
+    const int64_t wp = (window - 1 + (int64_t)page_size - 1) / page_size + 1;
+    if (wp < pages) pages = wp;
+  }
+  return pages < 1 ? 1 : pages;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_string(pkv_status s) {
+  switch (s) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL_ARG: return "null argument";
+    case PKV_ERR_BAD_SHAPE: return "bad shape";
+    case PKV_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PKV_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case PKV_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+pkv_status pkv_slot_mapping(const int32_t* block_tables, int32_t max_pages_per_seq,
+                            const int32_t* cu_seq_lens_q, const int32_t* cu_seq_lens_k,
+                            int32_t num_seqs, int32_t total_tokens, int32_t page_size,
+                            int32_t num_pages, int32_t* slot_mapping, hipStream_t stream) {
+  if (num_seqs < 0 || total_tokens < 0 || max_pages_per_seq <= 0 || num_pages <= 0)
+    return PKV_ERR_BAD_SHAPE;
+  if (page_size <= 0) return PKV_ERR_BAD_SHAPE;
+  if ((int64_t)num_pages * page_size > INT32_MAX) return PKV_ERR_BAD_SHAPE;
+  if (num_seqs == 0 || total_tokens == 0) return PKV_OK;
+  if (!block_tables || !cu_seq_lens_q || !cu_seq_lens_k || !slot_mapping) return PKV_ERR_NULL_ARG;
+  return hip_status(launch_slot_mapping(block_tables, max_pages_per_seq, cu_seq_lens_q,
+                                        cu_seq_lens_k, num_seqs, total_tokens, page_size,
+                                        num_pages, slot_mapping, stream));
+}
+
+pkv_status pkv_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* slot_mapping,
+                      int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                      uint16_t* k_pool, uint16_t* v_pool, int64_t num_slots,
+                      hipStream_t stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_slots <= 0) return PKV_ERR_BAD_SHAPE;
+  if (!supported_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_pool || !v_pool) return PKV_ERR_NULL_ARG;
+  return hip_status(launch_append(k_new, v_new, slot_mapping, num_tokens, num_kv_heads, head_dim,
+                                  k_pool, v_pool, num_slots, stream));
+}
+
+pkv_status pkv_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t page_size,
+                           int32_t max_seq_len, int32_t window, int32_t num_splits_requested,
+                           int32_t* num_splits, int32_t* pages_per_split) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || max_seq_len < 0 || num_splits_requested < 0)
+    return PKV_ERR_BAD_SHAPE;
+  if (!supported_ps(page_size)) return PKV_ERR_UNSUPPORTED;
+  const int64_t pages = key_pages(page_size, max_seq_len, window);
+  int64_t pps, s;
+  if (num_splits_requested > 0) {
+    s = num_splits_requested;
+    pps = (pages + s - 1) / s;
+  } else {
+    pps = pages < kMaxPagesPerSplit ? pages : kMaxPagesPerSplit;
+    const int64_t rows = (int64_t)num_seqs * num_kv_heads;
+    while (pps > kMinPagesPerSplit && rows * ((pages + pps - 1) / pps) < kTargetWorkgroups) {
+      pps = (pps + 1) / 2;
+      if (pps < kMinPagesPerSplit) pps = kMinPagesPerSplit;
+    }
+    s = (pages + pps - 1) / pps;
+  }
+  if (s > 65535) return PKV_ERR_UNSUPPORTED;
+  if (num_splits) *num_splits = (int32_t)s;
+  if (pages_per_split) *pages_per_split = (int32_t)pps;
+  return PKV_OK;
+}
+
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                  int32_t num_kv_heads, int32_t page_size, int32_t max_seq_len,
+                                  int32_t window, int32_t num_splits_requested) {
+  int32_t s = 0, pps = 0;
+  if (pkv_decode_plan(num_seqs, num_kv_heads, page_size, max_seq_len, window,
+                      num_splits_requested, &s, &pps) != PKV_OK)
+    return 0;
+  if (s <= 1 || num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  const size_t cells = (size_t)num_seqs * num_q_heads * s;
+  return cells * ((size_t)head_dim + 2) * sizeof(float);
+}
+
+static pkv_status check_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                               const int32_t* block_tables, int32_t max_pages_per_seq,
+                               const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                               int32_t num_pages, int32_t max_seq_len) {
+  if (num_seqs < 0 || max_pages_per_seq <= 0 || num_pages <= 0 || max_seq_len < 0)
+    return PKV_ERR_BAD_SHAPE;
+  pkv_status st = check_heads(num_q_heads, num_kv_heads);
+  if (st != PKV_OK) return st;
+  if (!supported_dim(head_dim) || !supported_ps(page_size)) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)max_pages_per_seq * page_size > INT32_MAX) return PKV_ERR_BAD_SHAPE;
+  if (num_seqs > 65535) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PKV_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens) return PKV_ERR_NULL_ARG;
+  return PKV_OK;
+}
+
+static DecodeArgs decode_args(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                              const int32_t* block_tables, int32_t max_pages_per_seq,
+                              const int32_t* seq_lens, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t page_size, int32_t num_pages,
+                              float scale, int32_t window, int32_t splits, int32_t pps) {
+  DecodeArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.part_m = a.part_l = a.part_acc = nullptr;
+  a.out = nullptr;
+  a.head_stride = (int64_t)num_pages * page_size * head_dim;
+  a.max_pages = max_pages_per_seq;
+  a.num_pages = num_pages;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.num_splits = splits;
+  a.pages_per_split = pps;
+  a.window = window;
+  a.scale_log2 = scale * kLog2e;
+  return a;
+}
+
+pkv_status pkv_decode_split(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                            const int32_t* block_tables, int32_t max_pages_per_seq,
+                            const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                            int32_t num_pages, int32_t max_seq_len, float scale, int32_t window,
+                            int32_t num_splits, int32_t pages_per_split, float* part_m,
+                            float* part_l, float* part_acc, hipStream_t stream) {
+  pkv_status st = check_decode(q, k_pool, v_pool, block_tables, max_pages_per_seq, seq_lens,
+                               num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                               num_pages, max_seq_len);
+  if (st != PKV_OK) return st;
+  if (num_splits <= 0 || num_splits > 65535 || pages_per_split <= 0) return PKV_ERR_BAD_SHAPE;
+  if ((int64_t)num_splits * pages_per_split < key_pages(page_size, max_seq_len, window))
+    return PKV_ERR_BAD_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!part_m || !part_l || !part_acc) return PKV_ERR_NULL_ARG;
+  DecodeArgs a = decode_args(q, k_pool, v_pool, block_tables, max_pages_per_seq, seq_lens,
+                             num_q_heads, num_kv_heads, head_dim, page_size, num_pages, scale,
+                             window, num_splits, pages_per_split);
+  a.part_m = part_m;
+  a.part_l = part_l;
+  a.part_acc = part_acc;
+  return hip_status(launch_decode(a, num_seqs, head_dim, page_size, true, stream));
+}
+
+pkv_status pkv_decode_combine(const float* part_m, const float* part_l, const float* part_acc,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                              int32_t num_splits, uint16_t* out, hipStream_t stream) {
+  if (num_seqs < 0 || num_q_heads <= 0 || num_splits <= 0) return PKV_ERR_BAD_SHAPE;
+  if (!supported_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)num_seqs * num_q_heads > INT32_MAX / 4) return PKV_ERR_BAD_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!part_m || !part_l || !part_acc || !out) return PKV_ERR_NULL_ARG;
+  return hip_status(launch_combine(part_m, part_l, part_acc, num_seqs, num_q_heads, head_dim,
+                                   num_splits, out, stream));
+}
+
+pkv_status pkv_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                      const int32_t* block_tables, int32_t max_pages_per_seq,
+                      const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                      int32_t num_pages, int32_t max_seq_len, float scale, int32_t window,
+                      int32_t num_splits, void* workspace, size_t workspace_bytes,
+                      uint16_t* out, hipStream_t stream) {
+  pkv_status st = check_decode(q, k_pool, v_pool, block_tables, max_pages_per_seq, seq_lens,
+                               num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                               num_pages, max_seq_len);
+  if (st != PKV_OK) return st;
+  if (num_splits < 0) return PKV_ERR_BAD_SHAPE;
+  int32_t s = 0, pps = 0;
+  st = pkv_decode_plan(num_seqs, num_kv_heads, page_size, max_seq_len, window, num_splits, &s,
+                       &pps);
+  if (st != PKV_OK) return st;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out) return PKV_ERR_NULL_ARG;
+  DecodeArgs a = decode_args(q, k_pool, v_pool, block_tables, max_pages_per_seq, seq_lens,
+                             num_q_heads, num_kv_heads, head_dim, page_size, num_pages, scale,
+                             window, s, pps);
+  if (s <= 1) {
+    a.out = out;
+    return hip_status(launch_decode(a, num_seqs, head_dim, page_size, false, stream));
+  }
+  const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, num_kv_heads,
+                                                 page_size, max_seq_len, window, num_splits);
+  if (!workspace) return PKV_ERR_NULL_ARG;
+  if (workspace_bytes < need) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  const size_t cells = (size_t)num_seqs * num_q_heads * s;
+  float* ws = static_cast<float*>(workspace);
+  a.part_acc = ws;
+  a.part_m = ws + cells * head_dim;
+  a.part_l = a.part_m + cells;
+  pkv_status r = hip_status(launch_decode(a, num_seqs, head_dim, page_size, true, stream));
+  if (r != PKV_OK) return r;
+  return hip_status(launch_combine(a.part_m, a.part_l, a.part_acc, num_seqs, num_q_heads,
+                                   head_dim, s, out, stream));
+}
+
+pkv_status pkv_prefill_varlen(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                              const int32_t* block_tables, int32_t max_pages_per_seq,
+                              const int32_t* cu_seq_lens_q, const int32_t* cu_seq_lens_k,
+                              int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                              int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t page_size, int32_t num_pages,
+                              float scale, int32_t window, uint16_t* out, hipStream_t stream) {
+  if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 ||
+      max_pages_per_seq <= 0 || num_pages <= 0)
+    return PKV_ERR_BAD_SHAPE;
+  pkv_status st = check_heads(num_q_heads, num_kv_heads);
+  if (st != PKV_OK) return st;
+  if (!supported_dim(head_dim) || !supported_ps(page_size)) return PKV_ERR_UNSUPPORTED;
+  if ((int64_t)max_pages_per_seq * page_size > INT32_MAX) return PKV_ERR_BAD_SHAPE;
+  if (num_seqs > 65535) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PKV_OK;
+  if (!q || !k_pool || !v_pool || !block_tables || !cu_seq_lens_q || !cu_seq_lens_k || !out)
+    return PKV_ERR_NULL_ARG;
+  PrefillArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.cu_q = cu_seq_lens_q;
+  a.cu_k = cu_seq_lens_k;
+  a.out = out;
+  a.head_stride = (int64_t)num_pages * page_size * head_dim;
+  a.max_pages = max_pages_per_seq;
+  a.num_pages = num_pages;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_q_heads / num_kv_heads;
+  a.total_q = total_q;
+  a.window = window;
+  a.scale_log2 = scale * kLog2e;
+  return hip_status(launch_prefill(a, num_seqs, max_seqlen_q, head_dim, page_size, stream));
+}
+
+}  // extern "C"

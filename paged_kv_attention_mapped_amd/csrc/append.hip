@@ -1,0 +1,84 @@
+// Slot addressing and the slot-mapped K/V append.
+//
+// The engine writes each new token's K/V row straight into the shared page
+// pool at a physical row address (scripts/benchmarks commit log 1847125,
+// flex_attention paged-KV engine entry, "Files": k_cache[addr] = k_val).
+// The address comes from the sequence's block table (same entry, "Why this
+// works" item 1).
+#include "common.h"
+
+namespace pkv {
+namespace {
+
+// One workgroup per sequence; threads stride over its new tokens.
+__global__ __launch_bounds__(256) void slot_mapping_kernel(
+    const int32_t* __restrict__ bt, int max_pages, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_k, int total, int page_size, int num_pages,
+    int32_t* __restrict__ slots) {
+  const int j = blockIdx.x;
+  const int q0 = cu_q[j], q1 = cu_q[j + 1];
+  const int lk = cu_k[j + 1] - cu_k[j];
+  const int lq = q1 - q0;
+  for (int r = threadIdx.x; r < lq; r += blockDim.x) {
+    const int t = q0 + r;
+    if (t < 0 || t >= total) continue;
+    const int pos = lk - lq + r;
+    int slot = -1;
+    if (pos >= 0) {
+      const int lp = pos / page_size;
+      if (lp < max_pages) {
+        const int phys = bt[(int64_t)j * max_pages + lp];
+        if (phys >= 0 && phys < num_pages) slot = phys * page_size + pos % page_size;
+      }
+    }
+    slots[t] = slot;
+  }
+}
+
+// One thread per 16-byte chunk of a (token, head) row: consecutive lanes
+// read consecutive bytes of k_new and write consecutive bytes of the pool
+// row, so both sides are fully coalesced.
+__global__ __launch_bounds__(256) void append_kernel(
+    const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
+    const int32_t* __restrict__ slots, int64_t total_chunks, int hkv, int chunks_per_row,
+    uint4* __restrict__ k_pool, uint4* __restrict__ v_pool, int64_t num_slots) {
+  const int64_t per_token = (int64_t)hkv * chunks_per_row;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total_chunks;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / per_token;
+    const int64_t rem = i - t * per_token;
+    const int64_t h = rem / chunks_per_row;
+    const int64_t c = rem - h * chunks_per_row;
+    const int64_t slot = slots[t];
+    if (slot < 0 || slot >= num_slots) continue;
+    const int64_t dst = (h * num_slots + slot) * chunks_per_row + c;
+    k_pool[dst] = k_new[i];
+    v_pool[dst] = v_new[i];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_slot_mapping(const int32_t* bt, int max_pages, const int32_t* cu_q,
+                               const int32_t* cu_k, int num_seqs, int total, int page_size,
+                               int num_pages, int32_t* slots, hipStream_t st) {
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3(num_seqs), dim3(256), 0, st, bt, max_pages, cu_q,
+                     cu_k, total, page_size, num_pages, slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* slots,
+                         int num_tokens, int hkv, int d, uint16_t* k_pool, uint16_t* v_pool,
+                         int64_t num_slots, hipStream_t st) {
+  const int cpr = d / 8;
+  const int64_t total = (int64_t)num_tokens * hkv * cpr;
+  const int64_t want = (total + 255) / 256;
+  const int blocks = (int)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(append_kernel, dim3(blocks), dim3(256), 0, st,
+                     reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new),
+                     slots, total, hkv, cpr, reinterpret_cast<uint4*>(k_pool),
+                     reinterpret_cast<uint4*>(v_pool), num_slots);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

@@ -1,0 +1,120 @@
+// Shared device helpers for the gfx950 kernels (bf16 bit handling, MFMA
+// operand types, wave-level broadcasts) and the internal launcher interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace pkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// bf16 pattern in the low / high half of a 32-bit word -> float (exact).
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bf16 pattern, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value of lane SRC of this lane's 16-lane row (DPP row_newbcast).
+template <int SRC>
+__device__ __forceinline__ float row_bcast(float v) {
+  static_assert(SRC >= 0 && SRC < 16, "row lane");
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + SRC, 0xf, 0xf, false));
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(static_cast<F&&>(f));
+  }
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// launchers (host side; arguments already validated by the C ABI layer)
+// ---------------------------------------------------------------------------
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float* part_m;      // split mode
+  float* part_l;
+  float* part_acc;
+  uint16_t* out;      // direct mode
+  int64_t head_stride;  // elements per KV head in a pool = num_pages*page_size*D
+  int max_pages;
+  int num_pages;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;          // Hq / Hkv
+  int num_splits;
+  int pages_per_split;
+  int window;
+  float scale_log2;   // scale * log2(e)
+};
+
+hipError_t launch_slot_mapping(const int32_t* bt, int max_pages, const int32_t* cu_q,
+                               const int32_t* cu_k, int num_seqs, int total, int page_size,
+                               int num_pages, int32_t* slots, hipStream_t st);
+hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* slots,
+                         int num_tokens, int hkv, int d, uint16_t* k_pool, uint16_t* v_pool,
+                         int64_t num_slots, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, int num_seqs, int head_dim, int page_size,
+                         bool split, hipStream_t st);
+hipError_t launch_combine(const float* m, const float* l, const float* acc, int num_seqs,
+                          int hq, int d, int splits, uint16_t* out, hipStream_t st);
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* block_tables;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  uint16_t* out;
+  int64_t head_stride;
+  int max_pages;
+  int num_pages;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;
+  int total_q;
+  int window;
+  float scale_log2;
+};
+hipError_t launch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, int head_dim,
+                          int page_size, hipStream_t st);
+
+}  // namespace pkv

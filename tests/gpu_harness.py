@@ -1,0 +1,94 @@
+"""Shared set-up for the GPU tests: the same seeded workload is placed in GPU
+pools through the HIP path and in CPU pools through the oracle, and the two
+are compared.  The oracle never sees a value produced on the GPU."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_attention_mapped_amd as P
+import workloads as W
+
+# Tolerance for bf16 outputs with fp32 accumulation, against the float64 oracle.
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_i32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def dev_bits(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).cuda()
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def as_f64(bits) -> np.ndarray:
+    return W.bf16_to_f32(bits).astype(np.float64)
+
+
+def check_close(gpu_bits, ref, what="", max_abs=MAX_ABS, mean_abs=MEAN_ABS):
+    g = as_f64(gpu_bits)
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    err = np.abs(g - ref)
+    mx, mn = float(err.max()) if err.size else 0.0, float(err.mean()) if err.size else 0.0
+    rms = float(np.sqrt(np.mean((g - ref) ** 2)) / max(1e-30, np.sqrt(np.mean(ref ** 2)))) if err.size else 0.0
+    say(f"  {what}: max_abs={mx:.3e} mean_abs={mn:.3e} rms_rel={rms:.3e}")
+    assert mx <= max_abs and mn <= mean_abs, (what, mx, mn)
+
+
+class GpuPools:
+    """Poisoned GPU pools of a workload, filled through pkv_slot_mapping + pkv_append."""
+
+    def __init__(self, wl: W.Workload):
+        self.wl = wl
+        shape = (wl.num_kv_heads, wl.num_slots, wl.head_dim)
+        self.k = torch.full(shape, int(W.BF16_NAN), dtype=torch.int16, device="cuda")
+        self.v = torch.full(shape, int(W.BF16_NAN), dtype=torch.int16, device="cuda")
+        self.bt = dev_i32(wl.block_tables)
+
+    def write(self, part: str, seqs=None, chunk=64):
+        """Append the ``part`` tokens of ``seqs`` (default all), a few sequences at a time."""
+        wl = self.wl
+        seqs = np.arange(wl.num_seqs) if seqs is None else np.asarray(seqs)
+        for i in range(0, len(seqs), chunk):
+            sub = seqs[i:i + chunk]
+            wl.cache_all_kv(sub)
+            k, v, lq, lk = wl.packed_tokens(part, sub)
+            for s in sub:
+                wl._kv_cache.pop(int(s), None)
+            if k.shape[0] == 0:
+                continue
+            slots = P.slot_mapping(dev_i32(wl.block_tables[sub]), dev_i32(wl.cu_lens(lq)),
+                                   dev_i32(wl.cu_lens(lk)), page_size=wl.page_size,
+                                   num_pages=wl.num_pages, total_tokens=k.shape[0])
+            P.append(dev_bits(k), dev_bits(v), slots, self.k, self.v)
+        torch.cuda.synchronize()
+
+
+class OraclePools:
+    """CPU pools of the same workload, filled through the oracle (only ``seqs``)."""
+
+    def __init__(self, wl: W.Workload, seqs=None, parts=("prefix", "new")):
+        self.wl = wl
+        shape = (wl.num_kv_heads, wl.num_slots, wl.head_dim)
+        self.k = np.full(shape, W.BF16_NAN, np.uint16)
+        self.v = np.full(shape, W.BF16_NAN, np.uint16)
+        seqs = np.arange(wl.num_seqs) if seqs is None else np.asarray(seqs)
+        for part in parts:
+            k, v, lq, lk = wl.packed_tokens(part, seqs)
+            slots = oracle.slot_mapping(wl.block_tables[seqs], wl.cu_lens(lq), wl.cu_lens(lk),
+                                        wl.page_size)
+            self.k, self.v = oracle.append(self.k, self.v, k, v, slots)

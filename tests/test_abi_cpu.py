@@ -1,0 +1,116 @@
+"""The C ABI on the host: the library loads, exports every declared entry
+point, and rejects bad arguments before anything reaches the GPU.  No call
+here enqueues GPU work (every case returns during host validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+torch = pytest.importorskip("torch")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+
+@pytest.fixture(scope="module")
+def P():
+    import paged_kv_attention_mapped_amd as P
+    if not os.path.exists(P.lib_path()):
+        from paged_kv_attention_mapped_amd import build
+        build.build()
+    P.lib()
+    return P
+
+
+def declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:pkv_status|size_t|const char\*)\s+(pkv_\w+)\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared() == sorted([
+        "pkv_append", "pkv_decode", "pkv_decode_combine", "pkv_decode_plan", "pkv_decode_split",
+        "pkv_decode_workspace_bytes", "pkv_prefill_varlen", "pkv_slot_mapping",
+        "pkv_status_string"])
+
+
+def test_library_exports_every_declared_symbol(P):
+    lib = P.lib()
+    for name in declared():
+        assert hasattr(lib, name), name
+    assert sorted(P.exported_symbols()) == declared()
+
+
+def test_status_strings(P):
+    s = P.lib().pkv_status_string
+    assert s(0) == b"ok"
+    assert s(1) == b"null argument"
+    assert s(3) == b"unsupported configuration"
+    assert s(4) == b"workspace too small"
+    assert s(99) == b"unknown status"
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails validation first
+
+
+def _decode(P, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, maxp=4, lens=FAKE, B=2, hq=8, hkv=2, d=128, ps=32,
+             pages=10, maxlen=100, scale=1.0, window=0, splits=0, ws=None, wsb=0, out=FAKE)
+    a.update(kw)
+    return P.lib().pkv_decode(a["q"], a["k"], a["v"], a["bt"], a["maxp"], a["lens"], a["B"],
+                              a["hq"], a["hkv"], a["d"], a["ps"], a["pages"], a["maxlen"],
+                              a["scale"], a["window"], a["splits"], a["ws"], a["wsb"], a["out"],
+                              None)
+
+
+def test_decode_validation(P):
+    assert _decode(P, q=None) == 1
+    assert _decode(P, d=96) == 3
+    assert _decode(P, ps=8) == 3
+    assert _decode(P, hq=6, hkv=4) == 2
+    assert _decode(P, hq=32, hkv=2) == 3   # group 16 is not built
+    assert _decode(P, B=-1) == 2
+    assert _decode(P, maxp=0) == 2
+    # 2 splits requested: needs a workspace
+    assert _decode(P, splits=2, ws=None) == 1
+    assert _decode(P, splits=2, ws=FAKE, wsb=16) == 4
+    assert _decode(P, B=0) == 0            # empty batch: nothing to do
+
+
+def test_prefill_and_append_validation(P):
+    L = P.lib()
+    f = L.pkv_prefill_varlen
+    args = [FAKE, FAKE, FAKE, FAKE, 4, FAKE, FAKE, 2, 10, 8, 8, 8, 2, 128, 32, 10, 1.0, 0, FAKE, None]
+    a = list(args); a[0] = None
+    assert f(*a) == 1
+    a = list(args); a[13] = 80
+    assert f(*a) == 3
+    a = list(args); a[11] = 7
+    assert f(*a) == 2
+    a = list(args); a[8] = 0
+    assert f(*a) == 0
+    assert L.pkv_append(None, FAKE, FAKE, 4, 2, 128, FAKE, FAKE, 100, None) == 1
+    assert L.pkv_append(FAKE, FAKE, FAKE, 4, 2, 100, FAKE, FAKE, 100, None) == 3
+    assert L.pkv_append(FAKE, FAKE, FAKE, 0, 2, 128, FAKE, FAKE, 100, None) == 0
+    assert L.pkv_slot_mapping(None, 4, FAKE, FAKE, 2, 5, 32, 10, FAKE, None) == 1
+    assert L.pkv_slot_mapping(FAKE, 4, FAKE, FAKE, 2, 0, 32, 10, FAKE, None) == 0
+    assert L.pkv_decode_combine(FAKE, FAKE, FAKE, 2, 8, 128, 0, FAKE, None) == 2
+    assert L.pkv_decode_split(FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 8, 2, 128, 32, 10, 1000, 1.0,
+                              0, 2, 4, FAKE, FAKE, FAKE, None) == 2   # 2*4 pages < 32 needed
+
+
+def test_decode_plan(P):
+    # the workload shapes: (B, Hkv, ps, max_seq_len, window) -> splits cover every key page
+    for B, hkv, ps, L, w in [(256, 8, 32, 8193, 0), (32, 8, 32, 1025, 0), (4, 1, 16, 64, 0),
+                             (64, 1, 32, 4097, 512), (56, 8, 32, 2049, 0), (1, 1, 16, 1, 0)]:
+        s, pps = P.decode_plan(B, hkv, ps, L, w)
+        pages = -(-L // ps)
+        if w:
+            pages = min(pages, -(-(w - 1) // ps) + 1)
+        assert s * pps >= pages and (s - 1) * pps < pages
+        need = P.decode_workspace_bytes(B, hkv * 4, 128, hkv, ps, L, w)
+        assert need == (0 if s == 1 else B * hkv * 4 * s * 130 * 4)
+    assert P.decode_plan(256, 8, 32, 8193) == (9, 32)
+    assert P.decode_plan(4, 8, 32, 1000, 0, 7) == (7, 5)
+    assert P.decode_plan(4, 8, 32, 1000, 0, 1)[0] == 1

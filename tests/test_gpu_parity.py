@@ -1,0 +1,372 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI, on the
+seeded workloads.  Append and addressing must be bit-exact; attention must be
+within max-abs 2e-2 and mean-abs 2e-3 of the float64 oracle."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import workloads as W  # noqa: E402
+from gpu_harness import (GpuPools, OraclePools, check_close, dev_bits, dev_i32,  # noqa: E402
+                         host_bits, say)
+
+SMALL = ["tiny_decode", "qwen3_decode", "mixed_step", "window_shared"]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import paged_kv_attention_mapped_amd as P
+    P.lib()  # raises if the library was not built
+
+
+@pytest.fixture(scope="module")
+def P():
+    import paged_kv_attention_mapped_amd as P
+    return P
+
+
+_states = {}
+
+
+def state(name):
+    """GPU pools (prefix + this step's tokens appended through the HIP path)."""
+    if name not in _states:
+        wl = W.make(name)
+        say(f"[setup] {name}: seqs={wl.num_seqs} pages={wl.num_pages} tokens={int(wl.total_lens.sum())}")
+        g = GpuPools(wl)
+        g.write("prefix")
+        g.write("new")
+        _states[name] = g
+    return _states[name]
+
+
+def run_decode(P, g, q_bits, seqs=None, **kw):
+    wl = g.wl
+    seqs = wl.decode_ids() if seqs is None else seqs
+    lens = wl.total_lens[seqs].astype(np.int32)
+    out = P.decode(dev_bits(q_bits), g.k, g.v, dev_i32(wl.block_tables[seqs]), dev_i32(lens),
+                   int(lens.max()), page_size=wl.page_size, scale=wl.scale, window=wl.window, **kw)
+    torch.cuda.synchronize()
+    return host_bits(out)
+
+
+def run_prefill(P, g, q_bits, seqs=None):
+    wl = g.wl
+    seqs = wl.prefill_ids() if seqs is None else np.asarray(seqs)
+    lq = wl.new_lens[seqs]
+    lk = wl.total_lens[seqs]
+    out = P.prefill_varlen(dev_bits(q_bits), g.k, g.v, dev_i32(wl.block_tables[seqs]),
+                           dev_i32(wl.cu_lens(lq)), dev_i32(wl.cu_lens(lk)), int(lq.max()),
+                           int(lk.max()), page_size=wl.page_size, scale=wl.scale,
+                           window=wl.window)
+    torch.cuda.synchronize()
+    return host_bits(out)
+
+
+# ---------------------------------------------------------------------------
+# addressing and append: bit-exact
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", SMALL + ["large_decode", "long_prefill"])
+def test_slot_mapping_bit_exact(P, name):
+    wl = W.make(name)
+    say(f"[slot_mapping] {name}")
+    for part in ("prefix", "new"):
+        lq = wl.new_lens if part == "new" else wl.prefix_lens
+        lk = wl.total_lens if part == "new" else wl.prefix_lens
+        cq, ck = wl.cu_lens(lq), wl.cu_lens(lk)
+        got = P.slot_mapping(dev_i32(wl.block_tables), dev_i32(cq), dev_i32(ck),
+                             page_size=wl.page_size, num_pages=wl.num_pages,
+                             total_tokens=int(cq[-1]))
+        ref = oracle.slot_mapping(wl.block_tables, cq, ck, wl.page_size)
+        assert np.array_equal(got.cpu().numpy().astype(np.int64), ref)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_append_whole_pool_bit_exact(name):
+    g = state(name)
+    say(f"[append] {name}")
+    o = OraclePools(g.wl)
+    assert np.array_equal(host_bits(g.k), o.k)
+    assert np.array_equal(host_bits(g.v), o.v)
+
+
+def test_append_large_pool(P):
+    g = state("large_decode")
+    wl = g.wl
+    say("[append] large_decode: written-row mask + sampled sequences")
+    written = (g.k != int(W.BF16_NAN)).any(dim=-1).cpu().numpy()    # [Hkv, slots]
+    cq, ck = wl.cu_lens(wl.total_lens), wl.cu_lens(wl.total_lens)
+    used = np.zeros(wl.num_slots, bool)
+    used[oracle.slot_mapping(wl.block_tables, cq, ck, wl.page_size)] = True
+    assert np.array_equal(written, np.broadcast_to(used, written.shape))
+    samp = np.random.default_rng(0).choice(wl.num_seqs, 6, replace=False)
+    o = OraclePools(wl, samp)
+    rows = np.flatnonzero((o.k[0] != W.BF16_NAN).any(-1))
+    assert rows.size == int(wl.total_lens[samp].sum())
+    assert np.array_equal(host_bits(g.k[:, rows]), o.k[:, rows])
+    assert np.array_equal(host_bits(g.v[:, rows]), o.v[:, rows])
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny_decode", "qwen3_decode", "mixed_step", "window_shared"])
+def test_decode_parity(P, name):
+    g = state(name)
+    wl = g.wl
+    o = OraclePools(wl)
+    for layer in range(wl.num_layers):
+        qd, _ = wl.queries(layer)
+        say(f"[decode] {name} layer {layer}: B={wl.n_decode}")
+        got = run_decode(P, g, qd)
+        ref = oracle.decode(qd, o.k, o.v, wl.block_tables[:wl.n_decode], wl.decode_seq_lens(),
+                            wl.page_size, wl.scale, wl.window)
+        check_close(got, ref, f"{name} L{layer} decode")
+
+
+def test_decode_large_sampled(P):
+    g = state("large_decode")
+    wl = g.wl
+    qd, _ = wl.queries(0)
+    say("[decode] large_decode full batch, auto split")
+    got = run_decode(P, g, qd)
+    samp = np.sort(np.random.default_rng(1).choice(wl.n_decode, 8, replace=False))
+    o = OraclePools(wl, samp)
+    ref = oracle.decode(qd[samp], o.k, o.v, wl.block_tables[samp], wl.decode_seq_lens()[samp],
+                        wl.page_size, wl.scale)
+    check_close(got[samp], ref, "large_decode sampled rows")
+    # rows the oracle did not compute: finite, and every row of the output written
+    assert np.all(np.isfinite(W.bf16_to_f32(got)))
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 0])
+def test_split_count_invariance_and_determinism(P, splits):
+    g = state("qwen3_decode")
+    wl = g.wl
+    qd, _ = wl.queries(0)
+    say(f"[decode] qwen3_decode num_splits={splits}")
+    a = run_decode(P, g, qd, num_splits=splits)
+    b = run_decode(P, g, qd, num_splits=splits)
+    assert np.array_equal(a, b), "decode is not deterministic"
+    o = OraclePools(wl)
+    ref = oracle.decode(qd, o.k, o.v, wl.block_tables, wl.decode_seq_lens(), wl.page_size, wl.scale)
+    check_close(a, ref, f"splits={splits}")
+
+
+@pytest.mark.parametrize("name", ["qwen3_decode", "window_shared"])
+def test_decode_split_partials(P, name):
+    g = state(name)
+    wl = g.wl
+    qd, _ = wl.queries(0)
+    lens = wl.decode_seq_lens()
+    S, pps = P.decode_plan(wl.n_decode, wl.num_kv_heads, wl.page_size, int(lens.max()), wl.window)
+    if S == 1:
+        S, pps = P.decode_plan(wl.n_decode, wl.num_kv_heads, wl.page_size, int(lens.max()),
+                               wl.window, 3)
+    say(f"[decode_split] {name} S={S} pps={pps}")
+    m, l, acc = P.decode_split(dev_bits(qd), g.k, g.v, dev_i32(wl.block_tables[:wl.n_decode]),
+                               dev_i32(lens), int(lens.max()), page_size=wl.page_size,
+                               num_splits=S, pages_per_split=pps, scale=wl.scale,
+                               window=wl.window)
+    torch.cuda.synchronize()
+    m, l, acc = m.cpu().numpy(), l.cpu().numpy(), acc.cpu().numpy()
+    o = OraclePools(wl)
+    rm, rl, racc = oracle.decode_partials(qd, o.k, o.v, wl.block_tables, lens, wl.page_size,
+                                          wl.scale, wl.window, pps, S)
+    empty = ~np.isfinite(rm)
+    assert np.array_equal(~np.isfinite(m), empty)
+    assert np.all(l[empty] == 0) and np.all(acc[empty] == 0)
+    ne = ~empty
+    assert np.max(np.abs(m[ne] - rm[ne])) < 1e-3
+    np.testing.assert_allclose(l[ne], rl[ne], rtol=2e-2)
+    check_close_f = np.abs(acc[ne] / l[ne][:, None] - racc[ne] / rl[ne][:, None])
+    assert check_close_f.max() < 2e-2 and check_close_f.mean() < 2e-3
+
+
+def test_combine_from_oracle_partials(P):
+    # The combine kernel alone, fed with the oracle's partials.
+    wl = W.make("qwen3_decode")
+    o = OraclePools(wl)
+    qd, _ = wl.queries(0)
+    lens = wl.decode_seq_lens()
+    rm, rl, racc = oracle.decode_partials(qd, o.k, o.v, wl.block_tables, lens, wl.page_size,
+                                          wl.scale, 0, 4, 9)
+    say("[combine] qwen3_decode, 9 splits of 4 pages")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()  # noqa: E731
+    out = P.decode_combine(t(rm), t(rl), t(racc))
+    torch.cuda.synchronize()
+    check_close(host_bits(out), oracle.combine_partials(rm, rl, racc), "combine")
+
+
+def test_decode_page_permutation_bit_identical(P):
+    wl = W.make("qwen3_decode")
+    g1 = state("qwen3_decode")
+    perm = np.random.default_rng(5).permutation(wl.num_pages).astype(np.int32)
+    wl2 = W.make("qwen3_decode")
+    wl2.block_tables = perm[wl.block_tables]
+    say("[decode] page permutation")
+    g2 = GpuPools(wl2)
+    g2.write("prefix")
+    g2.write("new")
+    qd, _ = wl.queries(0)
+    assert np.array_equal(run_decode(P, g1, qd), run_decode(P, g2, qd))
+
+
+def test_decode_edge_lengths(P):
+    # L = 1 returns V exactly; L = 0 gives zeros; page-boundary lengths.
+    wl = W.make("qwen3_decode", decode_ctx=("fixed", (0, 31, 32, 63, 64, 1023)), name="edges")
+    g = GpuPools(wl)
+    g.write("prefix")
+    g.write("new")
+    qd, _ = wl.queries(0)
+    say("[decode] edge lengths 1,32,33,64,65,1024 and an empty row")
+    got = run_decode(P, g, qd)
+    o = OraclePools(wl)
+    ref = oracle.decode(qd, o.k, o.v, wl.block_tables, wl.decode_seq_lens(), wl.page_size, wl.scale)
+    check_close(got, ref, "edge lengths")
+    k, v = wl.kv_seq(0)
+    for h in range(wl.num_q_heads):
+        assert np.array_equal(got[0, h], v[0, h // 4])          # L = 1: exactly V
+    lens = wl.decode_seq_lens().copy()
+    lens[2] = 0
+    out = P.decode(dev_bits(qd), g.k, g.v, dev_i32(wl.block_tables), dev_i32(lens), 1024,
+                   page_size=wl.page_size)
+    torch.cuda.synchronize()
+    assert np.all(host_bits(out)[2] == 0)
+
+
+def test_decode_peaked_softmax(P):
+    # q = 30 x (the key of one token): that token's V must dominate.
+    wl = W.make("qwen3_decode")
+    g = state("qwen3_decode")
+    o = OraclePools(wl)
+    k, _ = wl.kv_seq(3)
+    qd, _ = wl.queries(0)
+    qd = qd.copy()
+    L = int(wl.total_lens[3])
+    qd[3] = W.bf16_bits((W.bf16_to_f32(k[L // 2]).repeat(4, axis=0) * 30).astype(np.float32))
+    got = run_decode(P, g, qd)
+    ref = oracle.decode(qd, o.k, o.v, wl.block_tables, wl.decode_seq_lens(), wl.page_size, wl.scale)
+    check_close(got, ref, "peaked")
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["mixed_step", "window_shared"])
+def test_prefill_parity(P, name):
+    g = state(name)
+    wl = g.wl
+    o = OraclePools(wl)
+    seqs = wl.prefill_ids()
+    for layer in range(wl.num_layers):
+        _, qp = wl.queries(layer)
+        say(f"[prefill] {name} layer {layer}: N={len(seqs)} Tq={qp.shape[0]}")
+        got = run_prefill(P, g, qp)
+        ref = oracle.prefill_varlen(qp, o.k, o.v, wl.block_tables[seqs],
+                                    wl.cu_lens(wl.new_lens[seqs]), wl.cu_lens(wl.total_lens[seqs]),
+                                    wl.page_size, wl.scale, wl.window)
+        check_close(got, ref, f"{name} L{layer} prefill")
+
+
+def test_prefill_long_sampled_rows(P):
+    g = state("long_prefill")
+    wl = g.wl
+    _, qp = wl.queries(0)
+    say(f"[prefill] long_prefill Tq={qp.shape[0]}")
+    got = run_prefill(P, g, qp)
+    assert np.all(np.isfinite(W.bf16_to_f32(got)))
+    rng = np.random.default_rng(2)
+    cq = wl.prefill_cu_q()
+    for j in rng.choice(wl.n_prefill, 3, replace=False):
+        s = wl.n_decode + j
+        Lk = int(wl.total_lens[s])
+        K, V = wl.kv_seq(s)
+        rows = np.unique(np.concatenate([rng.integers(0, Lk, 24), [0, Lk - 1, 63, 64, 127]]))
+        rows = rows[rows < Lk]
+        ref = oracle.attend_rows(oracle.bf16_to_f64(qp[cq[j] + rows]),
+                                 oracle.bf16_to_f64(K).transpose(1, 0, 2),
+                                 oracle.bf16_to_f64(V).transpose(1, 0, 2), rows, wl.scale, 0)
+        check_close(got[cq[j] + rows], ref, f"long_prefill seq {j} rows")
+
+
+def test_prefill_edge_cases(P):
+    # ragged lengths around tile sizes, an empty sequence, a chunk after a prefix
+    wl = W.make("mixed_step", decode_ctx=("fixed", ()), prefill_new=("fixed", (1, 31, 32, 0, 33, 127, 129)),
+                name="prefill_edges")
+    g = GpuPools(wl)
+    g.write("prefix")
+    g.write("new")
+    _, qp = wl.queries(0)
+    say("[prefill] ragged edges")
+    got = run_prefill(P, g, qp)
+    o = OraclePools(wl)
+    seqs = wl.prefill_ids()
+    ref = oracle.prefill_varlen(qp, o.k, o.v, wl.block_tables[seqs], wl.prefill_cu_q(),
+                                wl.prefill_cu_k(), wl.page_size, wl.scale)
+    check_close(got, ref, "prefill edges")
+    # first row of a fresh prompt attends only itself: exactly its V
+    cq = wl.prefill_cu_q()
+    for j, s in enumerate(seqs):
+        if wl.new_lens[s] == 0:
+            continue
+        _, v = wl.kv_seq(int(s))
+        assert np.array_equal(got[cq[j]][0], v[0, 0])
+
+
+def test_decode_equals_last_prefill_row_and_chunk_equals_full(P):
+    g = state("mixed_step")
+    wl = g.wl
+    seqs = wl.prefill_ids()
+    _, qp = wl.queries(0)
+    full = run_prefill(P, g, qp)
+    cq = wl.prefill_cu_q()
+    last = qp[cq[1:] - 1]
+    dec = run_decode(P, g, last, seqs=seqs)
+    a, b = W.bf16_to_f32(dec).astype(np.float64), W.bf16_to_f32(full[cq[1:] - 1]).astype(np.float64)
+    assert np.max(np.abs(a - b)) < 2e-2
+    # the last 40 rows of sequence 0 as a chunk over its first Lk-40 tokens
+    s0 = int(seqs[0])
+    Lk = int(wl.total_lens[s0])
+    out = P.prefill_varlen(dev_bits(qp[cq[1] - 40:cq[1]]), g.k, g.v, dev_i32(wl.block_tables[[s0]]),
+                           dev_i32([0, 40]), dev_i32([0, Lk]), 40, Lk, page_size=wl.page_size)
+    torch.cuda.synchronize()
+    c = W.bf16_to_f32(host_bits(out)).astype(np.float64)
+    f = W.bf16_to_f32(full[cq[1] - 40:cq[1]]).astype(np.float64)
+    assert np.max(np.abs(c - f)) < 2e-2
+
+
+def test_prefill_deterministic(P):
+    g = state("mixed_step")
+    _, qp = g.wl.queries(0)
+    assert np.array_equal(run_prefill(P, g, qp), run_prefill(P, g, qp))
+
+
+# ---------------------------------------------------------------------------
+# composed steps on one stream
+# ---------------------------------------------------------------------------
+def test_mixed_step_composed(P):
+    """One append of all new tokens, then prefill of the 8 prompts and decode
+    of the 56 decoders, on one stream, as the benchmark runs it."""
+    wl = W.make("mixed_step")
+    g = GpuPools(wl)
+    g.write("prefix")
+    k, v, lq, lk = wl.packed_tokens("new")
+    qd, qp = wl.queries(0)
+    say("[step] mixed_step composed")
+    slots = P.slot_mapping(g.bt, dev_i32(wl.cu_lens(lq)), dev_i32(wl.cu_lens(lk)),
+                           page_size=wl.page_size, num_pages=wl.num_pages, total_tokens=k.shape[0])
+    P.append(dev_bits(k), dev_bits(v), slots, g.k, g.v)
+    pre = run_prefill(P, g, qp)
+    dec = run_decode(P, g, qd)
+    o = OraclePools(wl)
+    seqs = wl.prefill_ids()
+    check_close(pre, oracle.prefill_varlen(qp, o.k, o.v, wl.block_tables[seqs], wl.prefill_cu_q(),
+                                           wl.prefill_cu_k(), wl.page_size, wl.scale), "step prefill")
+    check_close(dec, oracle.decode(qd, o.k, o.v, wl.block_tables, wl.decode_seq_lens(),
+                                   wl.page_size, wl.scale), "step decode")

@@ -293,5 +293,5 @@ def build(cfg: Config, *, seed: int | None = None, decode_ctx=None, prefill_new=
                     prefix, new, int(num_pages), bt, pad_page)
 
 
-def make(name: str, **kw) -> Workload:
-    return build(CONFIGS[name], **kw)
+def make(config: str, **kw) -> Workload:
+    return build(CONFIGS[config], **kw)
