@@ -12,6 +12,8 @@ namespace pkv {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -38,8 +40,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 template <int SRC>
 __device__ __forceinline__ float row_bcast(float v) {
   static_assert(SRC >= 0 && SRC < 16, "row lane");
-  return __int_as_float(
-      __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + SRC, 0xf, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + SRC, 0xf, 0xf, false));
 }
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
@@ -52,6 +53,33 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Buffer resource over [p, p + bytes): loads through it are bounds-checked by
+// the hardware (out-of-range lanes read 0) and take a uniform base in SGPRs.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+constexpr int kNonTemporal = 2;  // cache-policy bits: nt (streaming data)
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kNonTemporal);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, kNonTemporal);
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void buffer_load(uint4& d, __amdgpu_buffer_rsrc_t r, int off) { d = buffer_load16(r, off); }
+__device__ __forceinline__ void buffer_load(uint2& d, __amdgpu_buffer_rsrc_t r, int off) { d = buffer_load8(r, off); }
+
+// Streaming loads (read once, not kept in cache): 16 and 8 bytes.
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load_stream(const uint2* p) {
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

@@ -21,6 +21,7 @@
 //     its probabilities from lane h of its own row with a DPP broadcast.
 // K needs no transpose (the contraction runs over head_dim, its contiguous
 // axis); V would, so PV runs on the vector ALUs in fp32.
+#include <limits.h>
 #include <math.h>
 
 #include "common.h"
@@ -28,16 +29,37 @@
 namespace pkv {
 namespace {
 
+// Tuning knobs (fixed at build time): tokens processed per step of a wave
+// (a whole page or half of one), register buffers per wave (1, or 2 to keep
+// the next step's loads in flight while the current one is processed),
+// waves per workgroup and the occupancy the register budget is sized for.
+#ifndef PKV_DECODE_UNIT
+#define PKV_DECODE_UNIT 16
+#endif
+#ifndef PKV_DECODE_BUFFERS
+#define PKV_DECODE_BUFFERS 2
+#endif
+#ifndef PKV_DECODE_WAVES
+#define PKV_DECODE_WAVES 4
+#endif
+#ifndef PKV_DECODE_OCCUPANCY
+#define PKV_DECODE_OCCUPANCY 2
+#endif
+
 template <int D, int PS, int G>
 struct DecodeCfg {
-  static constexpr int NW = 4;                 // waves per workgroup
+  static constexpr int NW = PKV_DECODE_WAVES;  // waves per workgroup
+  static constexpr int UT = PKV_DECODE_UNIT < PS ? PKV_DECODE_UNIT : PS;  // tokens per step
+  static constexpr int UPP = PS / UT;          // steps per page
   static constexpr int EPL = D / 16;           // head-dim elements per lane (PV side)
   static constexpr int CH = EPL < 8 ? EPL : 8; // elements per V load (8 B or 16 B)
   static constexpr int NCH = EPL / CH;         // V loads per token per lane
-  static constexpr int KT = PS / 16;           // 16-token MFMA tiles per page
+  static constexpr int KT = UT / 16;           // 16-token MFMA tiles per step
   static constexpr int KB = D / 32;            // MFMA k-steps over head_dim
-  static constexpr int TPR = PS / 4;           // tokens per lane row per page
+  static constexpr int TPR = UT / 4;           // tokens per lane row per step
+  static constexpr int OCC = D == 256 ? 1 : PKV_DECODE_OCCUPANCY;
   static_assert(G <= 16, "group larger than one MFMA column tile");
+  static_assert(UT % 16 == 0 && PS % UT == 0, "step must be whole MFMA tiles of a page");
 };
 
 template <int CH>
@@ -56,7 +78,8 @@ __device__ __forceinline__ void unpack(const uint2& v, float* f) {
 }
 
 template <int D, int PS, int G, bool SPLIT>
-__global__ __launch_bounds__(256, (D == 256 ? 1 : 2)) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(PKV_DECODE_WAVES * 64, (DecodeCfg<D, PS, G>::OCC))
+void decode_kernel(DecodeArgs a) {
   using C = DecodeCfg<D, PS, G>;
   using VChunk = typename VChunkT<C::CH>::type;
   __shared__ float sm_m[C::NW][G];
@@ -103,43 +126,68 @@ __global__ __launch_bounds__(256, (D == 256 ? 1 : 2)) void decode_kernel(DecodeA
   // register r of lane row jj is token 4r + jj.
   const int tok_a = 4 * (n & 3) + (n >> 2);
 
-  for (int p = pa + w; p < pb; p += C::NW) {
-    const int phys = bt_row[p];
-    if (phys < 0 || phys >= a.num_pages) continue;
-    const uint16_t* kp = kh_base + (int64_t)phys * PS * D;
-    const uint16_t* vp = vh_base + (int64_t)phys * PS * D;
+  // This wave's pages are pa + w, pa + w + NW, ...; their table entries are
+  // fetched 64 at a time (one per lane) and read back with readlane, so no
+  // page load waits on a table load.
+  const int npw = pb - pa > w ? (pb - pa - w + C::NW - 1) / C::NW : 0;
+  const int nsteps = npw * C::UPP;
+  int phys_lane = 0;
 
-    uint4 kr[C::KT][C::KB];
+  struct Buf {
+    uint4 k[C::KT][C::KB];
+    VChunk v[C::TPR][C::NCH];
+    int tok0;
+    bool valid;
+  };
+  auto load = [&](Buf& bf, int j) {
+    const int i = j / C::UPP;            // page of this wave
+    const int half = j - i * C::UPP;     // step within the page
+    if ((i & 63) == 0 && half == 0) {
+      const int pl = pa + w + C::NW * (i + lane);
+      phys_lane = (i + lane < npw) ? bt_row[pl] : -1;
+    }
+    int phys = __builtin_amdgcn_readlane(phys_lane, i & 63);
+    bf.valid = phys >= 0 && phys < a.num_pages;
+    phys = bf.valid ? phys : 0;  // an unusable entry reads page 0 and is masked out
+    bf.tok0 = (pa + w + C::NW * i) * PS + half * C::UT;
+    const int64_t row0 = (int64_t)phys * PS + half * C::UT;
+    const auto kr = make_rsrc(kh_base + row0 * D, C::UT * D * 2);
+    const auto vr = make_rsrc(vh_base + row0 * D, C::UT * D * 2);
 #pragma unroll
     for (int ti = 0; ti < C::KT; ++ti)
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb)
-        kr[ti][kb] = *reinterpret_cast<const uint4*>(kp + (ti * 16 + tok_a) * D + 32 * kb + 8 * jj);
-    VChunk vr[C::TPR][C::NCH];
+        bf.k[ti][kb] = buffer_load16(kr, 2 * ((ti * 16 + tok_a) * D + 32 * kb + 8 * jj));
 #pragma unroll
-    for (int i = 0; i < C::TPR; ++i)
+    for (int i2 = 0; i2 < C::TPR; ++i2)
 #pragma unroll
       for (int ch = 0; ch < C::NCH; ++ch)
-        vr[i][ch] = *reinterpret_cast<const VChunk*>(vp + (4 * i + jj) * D + C::CH * n +
-                                                     16 * C::CH * ch);
-
-    // scores, in log2 units: x[i] belongs to token 4i + jj of the page
+        buffer_load(bf.v[i2][ch], vr, 2 * ((4 * i2 + jj) * D + C::CH * n + 16 * C::CH * ch));
+  };
+  auto process = [&](const Buf& bf) {
+    // scores, in log2 units: x[i] belongs to token 4i + jj of the step
     float x[C::TPR];
 #pragma unroll
     for (int ti = 0; ti < C::KT; ++ti) {
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) c = mfma16(as_bf16x8(kr[ti][kb]), qop[kb], c);
+      for (int kb = 0; kb < C::KB; ++kb) c = mfma16(as_bf16x8(bf.k[ti][kb]), qop[kb], c);
 #pragma unroll
       for (int r = 0; r < 4; ++r) x[4 * ti + r] = c[r] * a.scale_log2;
     }
-    const int tok0 = p * PS;
-    const bool partial = (tok0 < first_key) || (tok0 + PS > L);
+    // rows outside [first_key, L) (tail, window start, unusable page) are
+    // selected away: their scores become -inf and their V rows 0
+    const int lo = bf.valid ? first_key : INT_MAX;
+    const bool partial = (bf.tok0 < lo) || (bf.tok0 + C::UT > L);
+    uint32_t keep = 0xffffffffu;
     if (partial) {
+      keep = 0;
 #pragma unroll
       for (int i = 0; i < C::TPR; ++i) {
-        const int t = tok0 + 4 * i + jj;
-        x[i] = (t >= first_key && t < L) ? x[i] : -INFINITY;
+        const int t = bf.tok0 + 4 * i + jj;
+        const bool ok = t >= lo && t < L;
+        keep |= (ok ? 1u : 0u) << i;
+        x[i] = ok ? x[i] : -INFINITY;
       }
     }
     float pmax = x[0];
@@ -167,13 +215,11 @@ __global__ __launch_bounds__(256, (D == 256 ? 1 : 2)) void decode_kernel(DecodeA
     for (int i = 0; i < C::TPR; ++i) {
       float vf[C::EPL];
 #pragma unroll
-      for (int ch = 0; ch < C::NCH; ++ch) unpack(vr[i][ch], vf + ch * C::CH);
+      for (int ch = 0; ch < C::NCH; ++ch) unpack(bf.v[i][ch], vf + ch * C::CH);
       if (partial) {
-        const int t = tok0 + 4 * i + jj;
-        if (!(t >= first_key && t < L)) {
+        const bool ok = (keep >> i) & 1u;
 #pragma unroll
-          for (int e = 0; e < C::EPL; ++e) vf[e] = 0.f;
-        }
+        for (int e = 0; e < C::EPL; ++e) vf[e] = ok ? vf[e] : 0.f;
       }
       static_for<0, G>([&](auto hc) {
         constexpr int h = decltype(hc)::value;
@@ -181,6 +227,25 @@ __global__ __launch_bounds__(256, (D == 256 ? 1 : 2)) void decode_kernel(DecodeA
 #pragma unroll
         for (int e = 0; e < C::EPL; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
       });
+    }
+  };
+
+  if constexpr (PKV_DECODE_BUFFERS >= 2) {
+    // ping-pong: step j+1 is in flight while step j is processed
+    Buf b0, b1;
+    if (nsteps > 0) load(b0, 0);
+    for (int j = 0; j < nsteps; j += 2) {
+      if (j + 1 < nsteps) load(b1, j + 1);
+      process(b0);
+      if (j + 1 >= nsteps) break;
+      if (j + 2 < nsteps) load(b0, j + 2);
+      process(b1);
+    }
+  } else {
+    for (int j = 0; j < nsteps; ++j) {
+      Buf b0;
+      load(b0, j);
+      process(b0);
     }
   }
 
@@ -217,7 +282,7 @@ __global__ __launch_bounds__(256, (D == 256 ? 1 : 2)) void decode_kernel(DecodeA
   __syncthreads();
 
   // ---- merge the waves and write ----------------------------------------
-  for (int idx = tid; idx < g * D; idx += 256) {
+  for (int idx = tid; idx < g * D; idx += 64 * C::NW) {
     const int h = idx / D, d = idx - h * D;
     float Mx = -INFINITY;
 #pragma unroll
@@ -289,9 +354,9 @@ template <int D, int PS, int G>
 hipError_t launch_dpg(const DecodeArgs& a, int num_seqs, bool split, hipStream_t st) {
   dim3 grid(a.num_splits, a.num_kv_heads, num_seqs);
   if (split)
-    hipLaunchKernelGGL((decode_kernel<D, PS, G, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<D, PS, G, true>), grid, dim3(64 * PKV_DECODE_WAVES), 0, st, a);
   else
-    hipLaunchKernelGGL((decode_kernel<D, PS, G, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((decode_kernel<D, PS, G, false>), grid, dim3(64 * PKV_DECODE_WAVES), 0, st, a);
   return hipGetLastError();
 }
 
