@@ -38,7 +38,7 @@ DESCRIPTIONS = {
     "tiny_decode": "4 decode seqs, ctx {5,17,32,63}, Hq/Hkv/D 2/1/64, page 16, 32-page pool",
     "qwen3_decode": "32 decode seqs, ctx U[128,1024], Hq/Hkv/D 32/8/128, page 32",
     "mixed_step": "8 prompts U[64,256] + 56 decoders ctx U[256,2048], 32/8/128, page 32",
-    "large_decode": "256 decode seqs, ctx U[1024,8192], Hq/Hkv/D 32/8/128, page 32, split-K",
+    "large_decode": "256 decode seqs, ctx U[1024,8192], Hq/Hkv/D 32/8/128, page 32, random page order",
     "window_shared": "64 decoders ctx U[512,4096] + 4 chunks of 128 after U[512,4096], "
                      "8/1/256, page 32, window 512, 2 layers sharing the pool",
     "long_prefill": "16 prompts U[1024,4096], 32/8/128, page 32 (prefill only)",
@@ -110,7 +110,7 @@ def prefill_bytes(wl) -> int:
 # the step on the GPU
 # ---------------------------------------------------------------------------
 class Step:
-    def __init__(self, wl, torch, P):
+    def __init__(self, wl, torch, P, num_splits=0):
         self.wl, self.torch, self.P = wl, torch, P
         dev = torch.device("cuda")
         i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)  # noqa: E731
@@ -150,13 +150,21 @@ class Step:
             self.seq_lens = i32(lens)
             self.max_len = int(lens.max())
             self.bt_dec = i32(wl.block_tables[:self.B])
-            self.S, self.pps = P.decode_plan(self.B, wl.num_kv_heads, wl.page_size, self.max_len,
-                                             wl.window)
             hq, d = wl.num_q_heads, wl.head_dim
-            self.part = (torch.empty((self.B, hq, self.S), dtype=torch.float32, device=dev),
-                         torch.empty((self.B, hq, self.S), dtype=torch.float32, device=dev),
-                         torch.empty((self.B, hq, self.S, d), dtype=torch.float32, device=dev))
             self.out_dec = torch.empty((self.B, hq, d), dtype=torch.bfloat16, device=dev)
+            self.S, self.pps, self.nw = 0, 0, 0
+            if num_splits == 0 and self.B <= 2048:
+                # stream-K: persistent waves over the flattened page list + merge
+                self.nw = P.decode_stream_waves(self.B, wl.num_kv_heads, d, wl.page_size,
+                                                self.max_len, wl.window)
+                need = P.lib().pkv_decode_stream_workspace_bytes(self.nw, hq, wl.num_kv_heads, d)
+                self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            else:
+                self.S, self.pps = P.decode_plan(self.B, wl.num_kv_heads, wl.page_size,
+                                                 self.max_len, wl.window, num_splits)
+                self.part = (torch.empty((self.B, hq, self.S), dtype=torch.float32, device=dev),
+                             torch.empty((self.B, hq, self.S), dtype=torch.float32, device=dev),
+                             torch.empty((self.B, hq, self.S, d), dtype=torch.float32, device=dev))
         # prefill
         self.N = wl.n_prefill
         if self.N:
@@ -184,7 +192,15 @@ class Step:
             if self.B:
                 if ev is not None and layer == 0:
                     ev[0].record()
-                if self.S > 1:
+                if self.nw:
+                    P.decode_stream(qd, self.k_pool, self.v_pool, self.bt_dec, self.seq_lens,
+                                    page_size=wl.page_size, num_waves=self.nw, scale=wl.scale,
+                                    window=wl.window, workspace=self.ws, out=self.out_dec)
+                    if ev is not None and layer == 0:
+                        ev[1].record()
+                    P.decode_stream_merge(self.ws, self.out_dec, num_waves=self.nw,
+                                          num_kv_heads=wl.num_kv_heads)
+                elif self.S > 1:
                     P.decode_split(qd, self.k_pool, self.v_pool, self.bt_dec, self.seq_lens,
                                    self.max_len, page_size=wl.page_size, num_splits=self.S,
                                    pages_per_split=self.pps, scale=wl.scale, window=wl.window,
@@ -348,6 +364,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="large_decode", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--num-splits", type=int, default=0,
+                    help="0: automatic decomposition (stream-K); >= 1: split-K with that many splits")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the long-prefill MFMA measurement")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
@@ -390,7 +408,7 @@ def main():
     wl = W.make(args.config)
     _log(f"[bench] setting up {args.config}: {DESCRIPTIONS[args.config]}")
     t0 = time.perf_counter()
-    st = Step(wl, torch, P)
+    st = Step(wl, torch, P, args.num_splits)
     _log(f"[bench] set-up done in {time.perf_counter() - t0:.1f} s; warmup {args.warmup}, steps {args.steps}")
 
     for _ in range(args.warmup):
@@ -431,12 +449,15 @@ def main():
         kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
         kb = decode_kernel_bytes(wl)
         ach = kb / (kern_ms * 1e-3) / 1e9
-        src_hash = _src_hash("decode.hip", "common.h")
+        src_hash = _src_hash("decode.hip", "decode_core.h", "common.h")
         traffic = recorded_traffic(args.config, src_hash)
         out["decode_tokens_per_s"] = round(st.B / (ms_step * 1e-3), 1)
-        out["decode_plan"] = {"num_splits": st.S, "pages_per_split": st.pps}
+        out["decode_plan"] = ({"stream_k_waves": st.nw} if st.nw else
+                              {"num_splits": st.S, "pages_per_split": st.pps})
+        kname = ("decode_stream_kernel (stream-K)" if st.nw else
+                 "decode_kernel (split-K partials)" if st.S > 1 else "decode_kernel (direct)")
         out["roofline"] = {
-            "kernel": "decode_kernel (split-K partials)" if st.S > 1 else "decode_kernel (direct)",
+            "kernel": kname,
             "bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
             "avg_kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": kb,

@@ -109,7 +109,7 @@ pkv_status pkv_append(const uint16_t* k_new, const uint16_t* v_new,
                       hipStream_t stream);
 
 /*
- * Decode planning.  pkv_decode splits each row's keys into num_splits
+ * Split-K planning.  Split-K cuts each row's keys into num_splits
  * partitions of pages_per_split logical pages (flash-decoding); the plan
  * depends only on host scalars.  num_splits_requested = 0 picks a count from
  * the grid size; 1 disables splitting.  Writes the plan through the two
@@ -119,7 +119,7 @@ pkv_status pkv_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t page_
                            int32_t max_seq_len, int32_t window, int32_t num_splits_requested,
                            int32_t* num_splits, int32_t* pages_per_split);
 
-/* Bytes of split-K workspace pkv_decode needs for this plan (0 when it does not split). */
+/* Bytes of workspace pkv_decode needs for these arguments (0 when it needs none). */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t num_kv_heads, int32_t page_size, int32_t max_seq_len,
                                   int32_t window, int32_t num_splits_requested);
@@ -140,6 +140,11 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *   workspace      device scratch of pkv_decode_workspace_bytes(...) bytes;
  *                  may be NULL when that is 0
  *   out            bf16 [num_seqs, num_q_heads, head_dim]       (device, written)
+ *
+ * num_splits = 0 picks the decomposition: the stream-K partition
+ * (pkv_decode_stream + pkv_decode_stream_merge) for up to 2048 rows, else
+ * split-K with an automatic split count; num_splits >= 1 forces split-K with
+ * that many splits (1 = no split, no workspace).
  *
  * A row with no key (seq_lens[b] == 0) is written as zeros.  Results are
  * deterministic and independent of the physical page order.
@@ -185,6 +190,50 @@ pkv_status pkv_decode_split(const uint16_t* q, const uint16_t* k_pool, const uin
 pkv_status pkv_decode_combine(const float* part_m, const float* part_l, const float* part_acc,
                               int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                               int32_t num_splits, uint16_t* out, hipStream_t stream);
+
+/*
+ * Decode, stream-K half.  The units of the batch -- every logical page that
+ * holds an allowed key, for every KV head of every row, ordered by row,
+ * then KV head, then page -- are cut into num_waves contiguous ranges of
+ * equal size (unit counts differ by at most one), one per persistent wave,
+ * so the work per wave does not depend on the length mix.  A (row, KV head)
+ * whose pages all fall in one range is finished by that wave and written to
+ * out; one cut by range boundaries leaves a partial per piece in the
+ * workspace for pkv_decode_stream_merge.  Rows with seq_lens[b] == 0 are
+ * written as zeros.  The result depends on num_waves only through rounding
+ * order and is deterministic for a given num_waves.
+ *
+ *   num_waves   >= 1; pkv_decode_stream_waves gives the count pkv_decode
+ *               uses (a few waves per compute unit of the current device)
+ *   workspace   pkv_decode_stream_workspace_bytes(num_waves, ...) bytes;
+ *               holds partials and merge descriptors, and is fully rewritten
+ *               by every call (no initialisation needed)
+ *   num_seqs    <= 2048 (the row lengths are scanned in LDS)
+ * Other arguments as for pkv_decode.
+ */
+pkv_status pkv_decode_stream_waves(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t page_size, int32_t max_seq_len, int32_t window,
+                                   int32_t* num_waves);
+size_t pkv_decode_stream_workspace_bytes(int32_t num_waves, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim);
+pkv_status pkv_decode_stream(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                             const int32_t* block_tables, int32_t max_pages_per_seq,
+                             const int32_t* seq_lens, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t page_size, int32_t num_pages,
+                             float scale, int32_t window, int32_t num_waves,
+                             void* workspace, size_t workspace_bytes,
+                             uint16_t* out, hipStream_t stream);
+
+/*
+ * Decode, stream-K merge half: combines the pieces of every cut (row, KV
+ * head) left by pkv_decode_stream (same workspace, num_waves and shapes),
+ * in wave order, into out.  Rows pkv_decode_stream finished are untouched.
+ */
+pkv_status pkv_decode_stream_merge(const void* workspace, size_t workspace_bytes,
+                                   int32_t num_waves, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim,
+                                   uint16_t* out, hipStream_t stream);
 
 /*
  * Varlen causal prefill over the paged pool.  Query rows of num_seqs

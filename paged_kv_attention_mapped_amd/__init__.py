@@ -25,6 +25,9 @@ __all__ = [
     "decode_combine",
     "decode_plan",
     "decode_split",
+    "decode_stream",
+    "decode_stream_merge",
+    "decode_stream_waves",
     "decode_workspace_bytes",
     "exported_symbols",
     "lib",
@@ -45,6 +48,10 @@ EXPORTS = (
     "pkv_decode",
     "pkv_decode_split",
     "pkv_decode_combine",
+    "pkv_decode_stream_waves",
+    "pkv_decode_stream_workspace_bytes",
+    "pkv_decode_stream",
+    "pkv_decode_stream_merge",
     "pkv_prefill_varlen",
 )
 
@@ -73,6 +80,11 @@ _SIGS = {
     "pkv_decode_split": ([_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                           _F, _I32, _I32, _I32, _P, _P, _P, _P], _I32),
     "pkv_decode_combine": ([_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P], _I32),
+    "pkv_decode_stream_waves": ([_I32, _I32, _I32, _I32, _I32, _I32, _P], _I32),
+    "pkv_decode_stream_workspace_bytes": ([_I32, _I32, _I32, _I32], _SZ),
+    "pkv_decode_stream": ([_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _F,
+                           _I32, _I32, _P, _SZ, _P, _P], _I32),
+    "pkv_decode_stream_merge": ([_P, _SZ, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "pkv_prefill_varlen": ([_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                             _I32, _I32, _I32, _F, _I32, _P, _P], _I32),
 }
@@ -252,6 +264,50 @@ def decode_combine(m, l, acc, out=None, stream=None):
     _dev(m, l, acc, out)
     _check("pkv_decode_combine", lib().pkv_decode_combine(
         _ptr(m), _ptr(l), _ptr(acc), B, hq, d, S, _ptr(out), _stream(stream)))
+    return out
+
+
+def decode_stream_waves(num_seqs, num_kv_heads, head_dim, page_size, max_seq_len, window=0):
+    """Number of persistent waves ``decode`` uses for stream-K (``pkv_decode_stream_waves``)."""
+    n = ctypes.c_int32(0)
+    _check("pkv_decode_stream_waves", lib().pkv_decode_stream_waves(
+        num_seqs, num_kv_heads, head_dim, page_size, max_seq_len, window, ctypes.byref(n)))
+    return n.value
+
+
+def decode_stream(q, k_pool, v_pool, block_tables, seq_lens, *, page_size, num_waves,
+                  scale=None, window=0, workspace=None, out=None, stream=None):
+    """Stream-K half of decode (``pkv_decode_stream``); returns ``(out, workspace)``.
+
+    Rows whose (row, KV head) pieces were cut between waves are completed by
+    ``decode_stream_merge`` with the same workspace.
+    """
+    _bf16(q, "q"); _bf16(k_pool, "k_pool"); _bf16(v_pool, "v_pool")
+    _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
+    B, hq, d = q.shape
+    hkv, num_pages, _ = _pool_shape(k_pool, page_size)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    need = int(lib().pkv_decode_stream_workspace_bytes(num_waves, hq, hkv, d))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=q.device)
+    _dev(q, k_pool, v_pool, block_tables, seq_lens, out, workspace)
+    _check("pkv_decode_stream", lib().pkv_decode_stream(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
+        _ptr(seq_lens), B, hq, hkv, d, page_size, num_pages, float(scale), window, num_waves,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+        _stream(stream)))
+    return out, workspace
+
+
+def decode_stream_merge(workspace, out, *, num_waves, num_kv_heads, stream=None):
+    """Merge half of stream-K decode (``pkv_decode_stream_merge``), in place on ``out``."""
+    B, hq, d = out.shape
+    _dev(workspace, out)
+    _check("pkv_decode_stream_merge", lib().pkv_decode_stream_merge(
+        _ptr(workspace), workspace.numel() * workspace.element_size(), num_waves, hq,
+        num_kv_heads, d, _ptr(out), _stream(stream)))
     return out
 
 

@@ -3,6 +3,8 @@
 // touches device memory from the host or synchronises.
 #include <math.h>
 
+#include <atomic>
+
 #include "../../include/pkv.h"
 #include "common.h"
 
@@ -34,6 +36,32 @@ int64_t key_pages(int page_size, int max_seq_len, int window) {
     if (wp < pages) pages = wp;
   }
   return pages < 1 ? 1 : pages;
+}
+
+constexpr int kStreamMaxSeqs = 2048;     // row lengths are scanned in LDS
+constexpr int kStreamMinUnitsPerWave = 4;
+constexpr int kStreamWavesPerSimd = 2;   // matches the stream kernel's register budget
+
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+size_t stream_part_bytes(int num_waves, int group, int head_dim) {
+  const size_t b = (size_t)2 * num_waves * group * (head_dim + 2) * sizeof(float);
+  return (b + 255) & ~(size_t)255;
 }
 
 }  // namespace
@@ -108,6 +136,13 @@ pkv_status pkv_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t page_
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t num_kv_heads, int32_t page_size, int32_t max_seq_len,
                                   int32_t window, int32_t num_splits_requested) {
+  if (num_splits_requested == 0 && num_seqs > 0 && num_seqs <= kStreamMaxSeqs) {
+    int32_t nw = 0;
+    if (pkv_decode_stream_waves(num_seqs, num_kv_heads, head_dim, page_size, max_seq_len, window,
+                                &nw) != PKV_OK)
+      return 0;
+    return pkv_decode_stream_workspace_bytes(nw, num_q_heads, num_kv_heads, head_dim);
+  }
   int32_t s = 0, pps = 0;
   if (pkv_decode_plan(num_seqs, num_kv_heads, page_size, max_seq_len, window,
                       num_splits_requested, &s, &pps) != PKV_OK)
@@ -209,6 +244,23 @@ pkv_status pkv_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t*
                                num_pages, max_seq_len);
   if (st != PKV_OK) return st;
   if (num_splits < 0) return PKV_ERR_BAD_SHAPE;
+  if (num_splits == 0 && num_seqs > 0 && num_seqs <= kStreamMaxSeqs) {
+    int32_t nw = 0;
+    st = pkv_decode_stream_waves(num_seqs, num_kv_heads, head_dim, page_size, max_seq_len,
+                                 window, &nw);
+    if (st != PKV_OK) return st;
+    if (!out) return PKV_ERR_NULL_ARG;
+    if (!workspace) return PKV_ERR_NULL_ARG;
+    if (workspace_bytes <
+        pkv_decode_stream_workspace_bytes(nw, num_q_heads, num_kv_heads, head_dim))
+      return PKV_ERR_WORKSPACE_TOO_SMALL;
+    st = pkv_decode_stream(q, k_pool, v_pool, block_tables, max_pages_per_seq, seq_lens,
+                           num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
+                           scale, window, nw, workspace, workspace_bytes, out, stream);
+    if (st != PKV_OK) return st;
+    return pkv_decode_stream_merge(workspace, workspace_bytes, nw, num_q_heads, num_kv_heads,
+                                   head_dim, out, stream);
+  }
   int32_t s = 0, pps = 0;
   st = pkv_decode_plan(num_seqs, num_kv_heads, page_size, max_seq_len, window, num_splits, &s,
                        &pps);
@@ -235,6 +287,84 @@ pkv_status pkv_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t*
   if (r != PKV_OK) return r;
   return hip_status(launch_combine(a.part_m, a.part_l, a.part_acc, num_seqs, num_q_heads,
                                    head_dim, s, out, stream));
+}
+
+pkv_status pkv_decode_stream_waves(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t page_size, int32_t max_seq_len, int32_t window,
+                                   int32_t* num_waves) {
+  if (num_seqs < 0 || num_kv_heads <= 0 || max_seq_len < 0) return PKV_ERR_BAD_SHAPE;
+  if (!supported_dim(head_dim) || !supported_ps(page_size)) return PKV_ERR_UNSUPPORTED;
+  const int64_t units = (int64_t)num_seqs * num_kv_heads * key_pages(page_size, max_seq_len, window);
+  const int per_simd = head_dim == 256 ? 1 : kStreamWavesPerSimd;
+  int64_t nw = (int64_t)device_cus() * 4 * per_simd;
+  const int64_t want = (units + kStreamMinUnitsPerWave - 1) / kStreamMinUnitsPerWave;
+  if (want < nw) nw = want;
+  if (nw < 1) nw = 1;
+  if (num_waves) *num_waves = (int32_t)nw;
+  return PKV_OK;
+}
+
+size_t pkv_decode_stream_workspace_bytes(int32_t num_waves, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim) {
+  if (num_waves <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
+    return 0;
+  return stream_part_bytes(num_waves, num_q_heads / num_kv_heads, head_dim) +
+         (size_t)2 * num_waves * kDescInts * sizeof(int);
+}
+
+static void stream_layout(StreamArgs& sa, void* workspace, int num_waves, int group, int head_dim) {
+  sa.num_waves = num_waves;
+  sa.part = static_cast<float*>(workspace);
+  sa.desc = reinterpret_cast<int*>(static_cast<char*>(workspace) +
+                                   stream_part_bytes(num_waves, group, head_dim));
+}
+
+pkv_status pkv_decode_stream(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                             const int32_t* block_tables, int32_t max_pages_per_seq,
+                             const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                             int32_t num_pages, float scale, int32_t window, int32_t num_waves,
+                             void* workspace, size_t workspace_bytes, uint16_t* out,
+                             hipStream_t stream) {
+  pkv_status st = check_decode(q, k_pool, v_pool, block_tables, max_pages_per_seq, seq_lens,
+                               num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                               num_pages, 0);
+  if (st != PKV_OK) return st;
+  if (num_seqs > kStreamMaxSeqs) return PKV_ERR_UNSUPPORTED;
+  if (num_waves <= 0 || num_waves > (1 << 20)) return PKV_ERR_BAD_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !workspace) return PKV_ERR_NULL_ARG;
+  if (workspace_bytes <
+      pkv_decode_stream_workspace_bytes(num_waves, num_q_heads, num_kv_heads, head_dim))
+    return PKV_ERR_WORKSPACE_TOO_SMALL;
+  StreamArgs sa;
+  sa.base = decode_args(q, k_pool, v_pool, block_tables, max_pages_per_seq, seq_lens,
+                        num_q_heads, num_kv_heads, head_dim, page_size, num_pages, scale, window,
+                        1, 1);
+  sa.base.out = out;
+  sa.num_seqs = num_seqs;
+  stream_layout(sa, workspace, num_waves, num_q_heads / num_kv_heads, head_dim);
+  return hip_status(launch_decode_stream(sa, head_dim, page_size, stream));
+}
+
+pkv_status pkv_decode_stream_merge(const void* workspace, size_t workspace_bytes,
+                                   int32_t num_waves, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, uint16_t* out, hipStream_t stream) {
+  pkv_status st = check_heads(num_q_heads, num_kv_heads);
+  if (st != PKV_OK) return st;
+  if (!supported_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (num_waves <= 0 || num_waves > (1 << 20)) return PKV_ERR_BAD_SHAPE;
+  if (!workspace || !out) return PKV_ERR_NULL_ARG;
+  if (workspace_bytes <
+      pkv_decode_stream_workspace_bytes(num_waves, num_q_heads, num_kv_heads, head_dim))
+    return PKV_ERR_WORKSPACE_TOO_SMALL;
+  StreamArgs sa = {};
+  sa.base.out = out;
+  sa.base.num_q_heads = num_q_heads;
+  sa.base.num_kv_heads = num_kv_heads;
+  sa.base.group = num_q_heads / num_kv_heads;
+  stream_layout(sa, const_cast<void*>(workspace), num_waves, sa.base.group, head_dim);
+  return hip_status(launch_stream_merge(sa, head_dim, stream));
 }
 
 pkv_status pkv_prefill_varlen(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,

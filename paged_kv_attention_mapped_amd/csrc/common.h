@@ -124,6 +124,19 @@ hipError_t launch_decode(const DecodeArgs& a, int num_seqs, int head_dim, int pa
 hipError_t launch_combine(const float* m, const float* l, const float* acc, int num_seqs,
                           int hq, int d, int splits, uint16_t* out, hipStream_t st);
 
+// Stream-K decode: per persistent wave two partial slots of g*(D+2) floats
+// (accumulator, then max and sum per head) and two merge descriptors.
+constexpr int kDescInts = 8;  // valid, sequence, KV head, last wave, total units
+struct StreamArgs {
+  DecodeArgs base;
+  int num_seqs;
+  int num_waves;
+  float* part;  // [2*num_waves][g*(D+2)]
+  int* desc;    // [2*num_waves][kDescInts]
+};
+hipError_t launch_decode_stream(const StreamArgs& sa, int head_dim, int page_size, hipStream_t st);
+hipError_t launch_stream_merge(const StreamArgs& sa, int head_dim, hipStream_t st);
+
 struct PrefillArgs {
   const uint16_t* q;
   const uint16_t* k_pool;

@@ -1,96 +1,65 @@
-// GQA decode attention over the paged pool, with split-K partitions and a
-// combine kernel.
+// GQA decode attention over the paged pool: split-K partitions with a
+// combine kernel, and a persistent stream-K partition with a merge kernel.
 //
 // One query row per sequence attends its cached keys through the block
 // table (scripts/benchmarks commit log 1847125, flex_attention paged-KV
 // engine entry, "Why this works" items 1-2); the sliding regime adds
-// q_pos - kv_pos < window (same log, per-regime mask entry).
+// q_pos - kv_pos < window (same log, per-regime mask entry).  In both
+// decompositions the whole query-head group of a KV head shares every page
+// it streams, so each page crosses HBM once; the per-wave work is in
+// decode_core.h.
 //
-// Work decomposition.  A workgroup owns one (sequence, KV head, split): the
-// whole query-head group shares every K/V page it streams, so each page is
-// read from HBM once per group.  Its four waves take the split's pages
-// round-robin.  Per page a wave
-//   * loads K in the A-operand layout of v_mfma_f32_16x16x32_bf16 (rows =
-//     16 tokens, k = 32 head-dim elements) and computes the scores of all
-//     query heads of the group at once (columns = heads);
-//   * loads V row-major, 16 lanes per token (16 B per lane for D=128), so
-//     every load instruction reads whole contiguous token rows;
-//   * keeps an online softmax per (16-lane row, head): the A rows are
-//     permuted so that lane row j of the score tile holds exactly the tokens
-//     j, j+4, j+8, ... whose V rows lane row j loaded, and each lane gets
-//     its probabilities from lane h of its own row with a DPP broadcast.
-// K needs no transpose (the contraction runs over head_dim, its contiguous
-// axis); V would, so PV runs on the vector ALUs in fp32.
-#include <limits.h>
-#include <math.h>
-
-#include "common.h"
+// Split-K: a workgroup owns one (sequence, KV head, split of pages); its
+// waves take the split's pages round-robin and are merged through LDS.
+//
+// Stream-K: the (sequence, KV head, page) units of the whole batch are
+// flattened in that order and cut into one contiguous, equal range per
+// persistent wave, so every wave streams the same number of pages whatever
+// the length mix.  A (sequence, KV head) segment that lies inside one
+// wave's range is finished by that wave; a segment cut by range boundaries
+// leaves one partial per piece (at most two per wave), and a small merge
+// kernel combines the pieces in wave order.
+#include "decode_core.h"
 
 namespace pkv {
 namespace {
 
-// Tuning knobs (fixed at build time): tokens processed per step of a wave
-// (a whole page or half of one), register buffers per wave (1, or 2 to keep
-// the next step's loads in flight while the current one is processed),
-// waves per workgroup and the occupancy the register budget is sized for.
+// Tuning knobs (fixed at build time).
 #ifndef PKV_DECODE_UNIT
-#define PKV_DECODE_UNIT 16
-#endif
-#ifndef PKV_DECODE_BUFFERS
-#define PKV_DECODE_BUFFERS 2
+#define PKV_DECODE_UNIT 16          // tokens per step (half a 32-token page)
 #endif
 #ifndef PKV_DECODE_WAVES
-#define PKV_DECODE_WAVES 4
+#define PKV_DECODE_WAVES 4          // waves per split-K workgroup
 #endif
 #ifndef PKV_DECODE_OCCUPANCY
-#define PKV_DECODE_OCCUPANCY 2
+#define PKV_DECODE_OCCUPANCY 2      // waves per SIMD the split-K registers are sized for
+#endif
+#ifndef PKV_STREAM_OCCUPANCY
+#define PKV_STREAM_OCCUPANCY 2      // waves per SIMD for the stream-K kernel
 #endif
 
-template <int D, int PS, int G>
-struct DecodeCfg {
-  static constexpr int NW = PKV_DECODE_WAVES;  // waves per workgroup
-  static constexpr int UT = PKV_DECODE_UNIT < PS ? PKV_DECODE_UNIT : PS;  // tokens per step
-  static constexpr int UPP = PS / UT;          // steps per page
-  static constexpr int EPL = D / 16;           // head-dim elements per lane (PV side)
-  static constexpr int CH = EPL < 8 ? EPL : 8; // elements per V load (8 B or 16 B)
-  static constexpr int NCH = EPL / CH;         // V loads per token per lane
-  static constexpr int KT = UT / 16;           // 16-token MFMA tiles per step
-  static constexpr int KB = D / 32;            // MFMA k-steps over head_dim
-  static constexpr int TPR = UT / 4;           // tokens per lane row per step
-  static constexpr int OCC = D == 256 ? 1 : PKV_DECODE_OCCUPANCY;
-  static_assert(G <= 16, "group larger than one MFMA column tile");
-  static_assert(UT % 16 == 0 && PS % UT == 0, "step must be whole MFMA tiles of a page");
-};
+template <int D>
+constexpr int occ(int o) { return D == 256 ? 1 : o; }
 
-template <int CH>
-struct VChunkT;
-template <>
-struct VChunkT<8> { using type = uint4; };
-template <>
-struct VChunkT<4> { using type = uint2; };
-
-__device__ __forceinline__ void unpack(const uint4& v, float* f) {
-  f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
-  f[4] = bf_lo(v.z); f[5] = bf_hi(v.z); f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
-}
-__device__ __forceinline__ void unpack(const uint2& v, float* f) {
-  f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
-}
-
+// ---------------------------------------------------------------------------
+// split-K
+// ---------------------------------------------------------------------------
 template <int D, int PS, int G, bool SPLIT>
-__global__ __launch_bounds__(PKV_DECODE_WAVES * 64, (DecodeCfg<D, PS, G>::OCC))
+__global__ __launch_bounds__(PKV_DECODE_WAVES * 64, occ<D>(PKV_DECODE_OCCUPANCY))
 void decode_kernel(DecodeArgs a) {
-  using C = DecodeCfg<D, PS, G>;
-  using VChunk = typename VChunkT<C::CH>::type;
-  __shared__ float sm_m[C::NW][G];
-  __shared__ float sm_l[C::NW][G];
-  __shared__ float sm_acc[C::NW][G][D];
+  using W = WaveDecoder<D, PS, G, PKV_DECODE_UNIT>;
+  constexpr int NW = PKV_DECODE_WAVES;
+  __shared__ float sm_m[NW][G];
+  __shared__ float sm_l[NW][G];
+  __shared__ float sm_acc[NW][G][D];
 
   const int s = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int jj = lane >> 4;  // lane row
-  const int n = lane & 15;   // column within the row (= head slot on the score side)
   const int g = a.group;
+  W wd;
+  wd.init(lane);
+  wd.reset();
+  wd.load_q(a.q + ((int64_t)b * a.num_q_heads + hk * g) * D, g);
 
   int L = a.seq_lens[b];
   L = max(0, min(L, a.max_pages * PS));
@@ -100,197 +69,64 @@ void decode_kernel(DecodeArgs a) {
   const int pa = min(pend, p0 + s * a.pages_per_split);
   const int pb = min(pend, pa + a.pages_per_split);
 
-  // Q^T as the B operand: lane (jj, n) holds q[head n][32kb + 8jj .. +7].
-  bf16x8 qop[C::KB];
-  {
-    const uint16_t* qrow = a.q + ((int64_t)b * a.num_q_heads + hk * g + n) * D + 8 * jj;
-#pragma unroll
-    for (int kb = 0; kb < C::KB; ++kb) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (n < g) v = *reinterpret_cast<const uint4*>(qrow + 32 * kb);
-      qop[kb] = as_bf16x8(v);
-    }
-  }
-
-  float m_run = -INFINITY, l_run = 0.f;
-  float acc[G][C::EPL];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < C::EPL; ++e) acc[h][e] = 0.f;
-
-  const uint16_t* kh_base = a.k_pool + (int64_t)hk * a.head_stride;
-  const uint16_t* vh_base = a.v_pool + (int64_t)hk * a.head_stride;
+  const uint16_t* kh = a.k_pool + (int64_t)hk * a.head_stride;
+  const uint16_t* vh = a.v_pool + (int64_t)hk * a.head_stride;
   const int32_t* bt_row = a.block_tables + (int64_t)b * a.max_pages;
-  // A-operand row n holds token 4*(n%4) + n/4 of each 16-token tile, so score
-  // register r of lane row jj is token 4r + jj.
-  const int tok_a = 4 * (n & 3) + (n >> 2);
 
   // This wave's pages are pa + w, pa + w + NW, ...; their table entries are
-  // fetched 64 at a time (one per lane) and read back with readlane, so no
-  // page load waits on a table load.
-  const int npw = pb - pa > w ? (pb - pa - w + C::NW - 1) / C::NW : 0;
-  const int nsteps = npw * C::UPP;
+  // fetched 64 at a time (one per lane) and read back with readlane.
+  const int npw = pb - pa > w ? (pb - pa - w + NW - 1) / NW : 0;
+  const int nsteps = npw * W::UPP;
   int phys_lane = 0;
-
-  struct Buf {
-    uint4 k[C::KT][C::KB];
-    VChunk v[C::TPR][C::NCH];
-    int tok0;
-    bool valid;
-  };
-  auto load = [&](Buf& bf, int j) {
-    const int i = j / C::UPP;            // page of this wave
-    const int half = j - i * C::UPP;     // step within the page
-    if ((i & 63) == 0 && half == 0) {
-      const int pl = pa + w + C::NW * (i + lane);
-      phys_lane = (i + lane < npw) ? bt_row[pl] : -1;
-    }
+  int tok_of[2] = {0, 0};
+  bool ok_of[2] = {false, false};
+  auto load = [&](typename W::Buf& bf, int j, int slot) {
+    const int i = j / W::UPP, part = j - i * W::UPP;
+    if ((i & 63) == 0 && part == 0)
+      phys_lane = (i + lane < npw) ? bt_row[pa + w + NW * (i + lane)] : -1;
     int phys = __builtin_amdgcn_readlane(phys_lane, i & 63);
-    bf.valid = phys >= 0 && phys < a.num_pages;
-    phys = bf.valid ? phys : 0;  // an unusable entry reads page 0 and is masked out
-    bf.tok0 = (pa + w + C::NW * i) * PS + half * C::UT;
-    const int64_t row0 = (int64_t)phys * PS + half * C::UT;
-    const auto kr = make_rsrc(kh_base + row0 * D, C::UT * D * 2);
-    const auto vr = make_rsrc(vh_base + row0 * D, C::UT * D * 2);
-#pragma unroll
-    for (int ti = 0; ti < C::KT; ++ti)
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-        bf.k[ti][kb] = buffer_load16(kr, 2 * ((ti * 16 + tok_a) * D + 32 * kb + 8 * jj));
-#pragma unroll
-    for (int i2 = 0; i2 < C::TPR; ++i2)
-#pragma unroll
-      for (int ch = 0; ch < C::NCH; ++ch)
-        buffer_load(bf.v[i2][ch], vr, 2 * ((4 * i2 + jj) * D + C::CH * n + 16 * C::CH * ch));
+    ok_of[slot] = phys >= 0 && phys < a.num_pages;
+    phys = ok_of[slot] ? phys : 0;  // an unusable entry reads page 0 and is masked out
+    tok_of[slot] = (pa + w + NW * i) * PS + part * W::UT;
+    const int64_t row = (int64_t)phys * PS + part * W::UT;
+    wd.load(bf, kh + row * D, vh + row * D);
   };
-  auto process = [&](const Buf& bf) {
-    // scores, in log2 units: x[i] belongs to token 4i + jj of the step
-    float x[C::TPR];
-#pragma unroll
-    for (int ti = 0; ti < C::KT; ++ti) {
-      f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) c = mfma16(as_bf16x8(bf.k[ti][kb]), qop[kb], c);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x[4 * ti + r] = c[r] * a.scale_log2;
-    }
-    // rows outside [first_key, L) (tail, window start, unusable page) are
-    // selected away: their scores become -inf and their V rows 0
-    const int lo = bf.valid ? first_key : INT_MAX;
-    const bool partial = (bf.tok0 < lo) || (bf.tok0 + C::UT > L);
-    uint32_t keep = 0xffffffffu;
-    if (partial) {
-      keep = 0;
-#pragma unroll
-      for (int i = 0; i < C::TPR; ++i) {
-        const int t = bf.tok0 + 4 * i + jj;
-        const bool ok = t >= lo && t < L;
-        keep |= (ok ? 1u : 0u) << i;
-        x[i] = ok ? x[i] : -INFINITY;
-      }
-    }
-    float pmax = x[0];
-#pragma unroll
-    for (int i = 1; i < C::TPR; ++i) pmax = fmaxf(pmax, x[i]);
-    const float m_new = fmaxf(m_run, pmax);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < C::TPR; ++i) {
-      x[i] = fast_exp2(x[i] - m_use);
-      psum += x[i];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-
-    static_for<0, G>([&](auto hc) {
-      constexpr int h = decltype(hc)::value;
-      const float ah = row_bcast<h>(alpha);
-#pragma unroll
-      for (int e = 0; e < C::EPL; ++e) acc[h][e] *= ah;
-    });
-#pragma unroll
-    for (int i = 0; i < C::TPR; ++i) {
-      float vf[C::EPL];
-#pragma unroll
-      for (int ch = 0; ch < C::NCH; ++ch) unpack(bf.v[i][ch], vf + ch * C::CH);
-      if (partial) {
-        const bool ok = (keep >> i) & 1u;
-#pragma unroll
-        for (int e = 0; e < C::EPL; ++e) vf[e] = ok ? vf[e] : 0.f;
-      }
-      static_for<0, G>([&](auto hc) {
-        constexpr int h = decltype(hc)::value;
-        const float ph = row_bcast<h>(x[i]);
-#pragma unroll
-        for (int e = 0; e < C::EPL; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
-      });
-    }
+  auto process = [&](const typename W::Buf& bf, int slot) {
+    wd.process(bf, tok_of[slot], ok_of[slot] ? first_key : INT_MAX, L, a.scale_log2);
   };
-
-  if constexpr (PKV_DECODE_BUFFERS >= 2) {
-    // ping-pong: step j+1 is in flight while step j is processed
-    Buf b0, b1;
-    if (nsteps > 0) load(b0, 0);
-    for (int j = 0; j < nsteps; j += 2) {
-      if (j + 1 < nsteps) load(b1, j + 1);
-      process(b0);
-      if (j + 1 >= nsteps) break;
-      if (j + 2 < nsteps) load(b0, j + 2);
-      process(b1);
-    }
-  } else {
-    for (int j = 0; j < nsteps; ++j) {
-      Buf b0;
-      load(b0, j);
-      process(b0);
-    }
+  typename W::Buf b0, b1;
+  if (nsteps > 0) load(b0, 0, 0);
+  for (int j = 0; j < nsteps; j += 2) {
+    if (j + 1 < nsteps) load(b1, j + 1, 1);
+    process(b0, 0);
+    if (j + 1 >= nsteps) break;
+    if (j + 2 < nsteps) load(b0, j + 2, 0);
+    process(b1, 1);
   }
 
-  // ---- merge the four lane rows of this wave ----------------------------
-  float M = m_run;
-  M = fmaxf(M, __shfl_xor(M, 16));
-  M = fmaxf(M, __shfl_xor(M, 32));
-  const float f = (M == -INFINITY) ? 0.f : fast_exp2(m_run - M);
-  float lw = l_run * f;
-  lw += __shfl_xor(lw, 16);
-  lw += __shfl_xor(lw, 32);
-  static_for<0, G>([&](auto hc) {
-    constexpr int h = decltype(hc)::value;
-    const float fh = row_bcast<h>(f);
-#pragma unroll
-    for (int e = 0; e < C::EPL; ++e) {
-      float v = acc[h][e] * fh;
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      acc[h][e] = v;
-    }
-  });
-  if (jj == 0) {
-    if (n < G) {
-      sm_m[w][n] = M;
-      sm_l[w][n] = lw;
+  float M, lw;
+  wd.merge_rows(M, lw);
+  if (wd.jj == 0) {
+    if (wd.n < G) {
+      sm_m[w][wd.n] = M;
+      sm_l[w][wd.n] = lw;
     }
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < C::EPL; ++e)
-        sm_acc[w][h][C::CH * n + (e % C::CH) + 16 * C::CH * (e / C::CH)] = acc[h][e];
+      for (int e = 0; e < W::EPL; ++e) sm_acc[w][h][wd.dim_of(e)] = wd.acc[h][e];
   }
   __syncthreads();
 
-  // ---- merge the waves and write ----------------------------------------
-  for (int idx = tid; idx < g * D; idx += 64 * C::NW) {
+  for (int idx = tid; idx < g * D; idx += 64 * NW) {
     const int h = idx / D, d = idx - h * D;
     float Mx = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < C::NW; ++ww) Mx = fmaxf(Mx, sm_m[ww][h]);
+    for (int ww = 0; ww < NW; ++ww) Mx = fmaxf(Mx, sm_m[ww][h]);
     float o = 0.f, lsum = 0.f;
     if (Mx != -INFINITY) {
 #pragma unroll
-      for (int ww = 0; ww < C::NW; ++ww) {
+      for (int ww = 0; ww < NW; ++ww) {
         const float mw = sm_m[ww][h];
         if (mw == -INFINITY) continue;
         const float wt = fast_exp2(mw - Mx);
@@ -350,6 +186,246 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *reinterpret_cast<uint2*>(out + (int64_t)row * D + d0) = pk;
 }
 
+// ---------------------------------------------------------------------------
+// stream-K
+// ---------------------------------------------------------------------------
+// Wave whose range [w*U/nw, (w+1)*U/nw) contains unit u.
+__device__ __forceinline__ int wave_of(int64_t u, int64_t U, int nw) {
+  return (int)(((u + 1) * nw - 1) / U);
+}
+
+template <int D, int PS, int G>
+__global__ __launch_bounds__(64, occ<D>(PKV_STREAM_OCCUPANCY))
+void decode_stream_kernel(StreamArgs sa) {
+  using W = WaveDecoder<D, PS, G, PKV_DECODE_UNIT>;
+  extern __shared__ int smem[];
+  const DecodeArgs& a = sa.base;
+  const int B = sa.num_seqs, nw = sa.num_waves, w = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int Hkv = a.num_kv_heads, g = a.group;
+  int* pre = smem;           // pre[b] = first unit of sequence b; pre[B] = U
+  int* lens = smem + B + 1;  // clamped lengths
+
+  // ---- flattened unit counts: E_b pages per KV head, units = E_b * Hkv ----
+  int carry = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    int v = 0;
+    if (b < B) {
+      const int L = max(0, min(a.seq_lens[b], a.max_pages * PS));
+      const int fk = a.window > 0 ? max(0, L - a.window) : 0;
+      const int E = (L + PS - 1) / PS - fk / PS;
+      lens[b] = L;
+      v = E * Hkv;
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(v, off);
+      if (lane >= off) v += t;
+    }
+    if (b < B) pre[b + 1] = carry + v;
+    carry += __shfl(v, 63);
+  }
+  if (lane == 0) pre[0] = 0;
+  __syncthreads();
+  const int U = __builtin_amdgcn_readfirstlane(pre[B]);
+
+  // every wave clears its two merge descriptors for this launch
+  if (lane < 2) sa.desc[(2 * w + lane) * kDescInts] = 0;
+  // rows of empty sequences are zero
+  for (int b = w; b < B; b += nw) {
+    if (lens[b] != 0) continue;
+    uint16_t* o = a.out + (int64_t)b * a.num_q_heads * D;
+    for (int i = lane; i < a.num_q_heads * D; i += 64) o[i] = 0;
+  }
+  if (U == 0) return;
+  const int64_t u0 = (int64_t)w * U / nw, u1 = (int64_t)(w + 1) * U / nw;
+  if (u0 >= u1) return;
+
+  W wd;
+  wd.init(lane);
+
+  // ---- segments: (b, hk) with units [s0, s1) = its pages p0 .. ----------
+  struct Seg {
+    int b, hk, L, fk, p0, s0, s1;
+  };
+  // values read from LDS are per-lane registers; readfirstlane keeps the
+  // (wave-uniform) segment bookkeeping in scalar registers
+  auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  auto seg_at = [&](int b, int hk) -> Seg {
+    Seg sg;
+    sg.b = b;
+    sg.hk = hk;
+    sg.L = uni(lens[b]);
+    sg.fk = a.window > 0 ? max(0, sg.L - a.window) : 0;
+    sg.p0 = sg.fk / PS;
+    const int pb0 = uni(pre[b]);
+    const int E = (uni(pre[b + 1]) - pb0) / Hkv;
+    sg.s0 = pb0 + hk * E;
+    sg.s1 = sg.s0 + E;
+    return sg;
+  };
+  auto seg_next = [&](const Seg& sg) -> Seg {
+    int b = sg.b, hk = sg.hk + 1;
+    if (hk == Hkv) {
+      hk = 0;
+      ++b;
+      while (b < B - 1 && uni(pre[b + 1]) == uni(pre[b])) ++b;  // skip empty sequences
+    }
+    return seg_at(b, hk);
+  };
+  // first segment: the largest b with pre[b] <= u0 is non-empty (u0 < U)
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (uni(pre[mid]) <= u0) lo = mid; else hi = mid;
+  }
+  const int hk_first = (int)((u0 - uni(pre[lo])) / ((uni(pre[lo + 1]) - uni(pre[lo])) / Hkv));
+
+  // load cursor (runs one step ahead of the process cursor)
+  Seg ls = seg_at(lo, hk_first);
+  int tab_base = -1;  // unit of the first table entry held in phys_lane
+  int phys_lane = 0;
+  struct StepInfo {
+    Seg sg;
+    int u, part, tok0;
+    bool ok;
+  };
+  const int nsteps = (int)(u1 - u0) * W::UPP;
+  auto load = [&](typename W::Buf& bf, StepInfo& si, int j) {
+    const int u = (int)u0 + j / W::UPP, part = j % W::UPP;
+    while (u >= ls.s1) {
+      ls = seg_next(ls);
+      tab_base = -1;
+    }
+    if (tab_base < 0 || u - tab_base >= 64) {
+      tab_base = u;
+      const int page = ls.p0 + (u - ls.s0) + lane;
+      phys_lane = (u + lane < ls.s1) ? a.block_tables[(int64_t)ls.b * a.max_pages + page] : -1;
+    }
+    int phys = __builtin_amdgcn_readlane(phys_lane, u - tab_base);
+    si.ok = phys >= 0 && phys < a.num_pages;
+    phys = si.ok ? phys : 0;  // an unusable entry reads page 0 and is masked out
+    si.sg = ls;
+    si.u = u;
+    si.part = part;
+    si.tok0 = (ls.p0 + (u - ls.s0)) * PS + part * W::UT;
+    const int64_t hoff = (int64_t)ls.hk * a.head_stride + ((int64_t)phys * PS + part * W::UT) * D;
+    wd.load(bf, a.k_pool + hoff, a.v_pool + hoff);
+  };
+
+  auto finish = [&](const Seg& sg) {
+    float M, lsum;
+    wd.merge_rows(M, lsum);
+    if (sg.s0 >= u0 && sg.s1 <= u1) {  // the whole segment is here: final rows
+      if (wd.jj == 0) {
+        uint16_t* o = a.out + ((int64_t)sg.b * a.num_q_heads + sg.hk * g) * D;
+        static_for<0, G>([&](auto hc) {
+          constexpr int h = decltype(hc)::value;
+          const float ls_h = row_bcast<h>(lsum);
+          if (h < g) {
+            const float inv = ls_h > 0.f ? 1.f / ls_h : 0.f;
+#pragma unroll
+            for (int e = 0; e < W::EPL; ++e)
+              o[h * D + wd.dim_of(e)] = (uint16_t)f32_to_bf16(wd.acc[h][e] * inv);
+          }
+        });
+      }
+      return;
+    }
+    const int slot = 2 * w + (sg.s0 <= u0 ? 0 : 1);
+    float* p = sa.part + (int64_t)slot * g * (D + 2);
+    if (wd.jj == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        if (h < g)
+#pragma unroll
+          for (int e = 0; e < W::EPL; ++e) p[h * D + wd.dim_of(e)] = wd.acc[h][e];
+      if (wd.n < g) {
+        p[g * D + wd.n] = M;
+        p[g * D + g + wd.n] = lsum;
+      }
+    }
+    if (sg.s0 >= u0 && lane == 0) {  // first piece: describe the segment for the merge
+      int* dsc = sa.desc + slot * kDescInts;
+      dsc[1] = sg.b;
+      dsc[2] = sg.hk;
+      dsc[3] = wave_of(sg.s1 - 1, U, nw);
+      dsc[4] = U;
+      dsc[0] = 1;
+    }
+  };
+
+  auto process = [&](const typename W::Buf& bf, const StepInfo& si) {
+    const Seg& sg = si.sg;
+    if (si.part == 0 && (si.u == sg.s0 || si.u == u0)) {  // first step of the segment here
+      wd.reset();
+      wd.load_q(a.q + ((int64_t)sg.b * a.num_q_heads + sg.hk * g) * D, g);
+    }
+    wd.process(bf, si.tok0, si.ok ? sg.fk : INT_MAX, sg.L, a.scale_log2);
+    if (si.part == W::UPP - 1 && (si.u == sg.s1 - 1 || si.u == u1 - 1)) finish(sg);
+  };
+  StepInfo i0, i1;
+  typename W::Buf b0, b1;
+  load(b0, i0, 0);
+  for (int j = 0; j < nsteps; j += 2) {
+    if (j + 1 < nsteps) load(b1, i1, j + 1);
+    process(b0, i0);
+    if (j + 1 >= nsteps) break;
+    if (j + 2 < nsteps) load(b0, i0, j + 2);
+    process(b1, i1);
+  }
+}
+
+// Merge of cut segments: one wave per merge descriptor; pieces are merged
+// in wave order, so the result does not depend on timing.
+template <int D>
+__global__ __launch_bounds__(64) void stream_merge_kernel(StreamArgs sa) {
+  const int slot = blockIdx.x, lane = threadIdx.x;
+  const int* dsc = sa.desc + slot * kDescInts;
+  if (dsc[0] == 0) return;
+  const DecodeArgs& a = sa.base;
+  const int g = a.group, nw = sa.num_waves;
+  const int b = dsc[1], hk = dsc[2], w1 = dsc[3];
+  const int64_t U = dsc[4];
+  const int w0 = slot >> 1;
+  const int64_t stride = (int64_t)g * (D + 2);
+  auto piece = [&](int w) -> const float* {
+    return sa.part + (int64_t)(w == w0 ? slot : 2 * w) * stride;
+  };
+  // waves with an empty range (possible when there are fewer units than
+  // waves) hold no piece
+  auto holds = [&](int w) { return (int64_t)w * U / nw < (int64_t)(w + 1) * U / nw; };
+  for (int h = 0; h < g; ++h) {
+    float Mx = -INFINITY;
+    for (int w = w0; w <= w1; ++w)
+      if (holds(w)) Mx = fmaxf(Mx, piece(w)[g * D + h]);
+    float lsum = 0.f;
+    float o[D / 64];
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) o[i] = 0.f;
+    if (Mx != -INFINITY) {
+      for (int w = w0; w <= w1; ++w) {
+        if (!holds(w)) continue;
+        const float* p = piece(w);
+        const float mw = p[g * D + h];
+        if (mw == -INFINITY) continue;
+        const float wt = fast_exp2(mw - Mx);
+        lsum = fmaf(wt, p[g * D + g + h], lsum);
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) o[i] = fmaf(wt, p[h * D + lane + 64 * i], o[i]);
+      }
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    uint16_t* out = a.out + ((int64_t)b * a.num_q_heads + hk * g + h) * D;
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) out[lane + 64 * i] = (uint16_t)f32_to_bf16(o[i] * inv);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
 template <int D, int PS, int G>
 hipError_t launch_dpg(const DecodeArgs& a, int num_seqs, bool split, hipStream_t st) {
   dim3 grid(a.num_splits, a.num_kv_heads, num_seqs);
@@ -373,6 +449,25 @@ hipError_t launch_d(const DecodeArgs& a, int num_seqs, int ps, bool split, hipSt
                   : launch_dp<D, 32>(a, num_seqs, split, st);
 }
 
+template <int D, int PS, int G>
+hipError_t launch_sg(const StreamArgs& sa, hipStream_t st) {
+  const size_t smem = (size_t)(2 * sa.num_seqs + 1) * sizeof(int);
+  hipLaunchKernelGGL((decode_stream_kernel<D, PS, G>), dim3(sa.num_waves), dim3(64), smem, st, sa);
+  return hipGetLastError();
+}
+
+template <int D, int PS>
+hipError_t launch_sp(const StreamArgs& sa, hipStream_t st) {
+  if (sa.base.group <= 2) return launch_sg<D, PS, 2>(sa, st);
+  if (sa.base.group <= 4) return launch_sg<D, PS, 4>(sa, st);
+  return launch_sg<D, PS, 8>(sa, st);
+}
+
+template <int D>
+hipError_t launch_s(const StreamArgs& sa, int ps, hipStream_t st) {
+  return ps == 16 ? launch_sp<D, 16>(sa, st) : launch_sp<D, 32>(sa, st);
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int num_seqs, int head_dim, int page_size,
@@ -393,6 +488,24 @@ hipError_t launch_combine(const float* m, const float* l, const float* acc, int 
     case 64: hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(256), 0, st, m, l, acc, rows, splits, out); break;
     case 128: hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(256), 0, st, m, l, acc, rows, splits, out); break;
     default: hipLaunchKernelGGL(combine_kernel<256>, grid, dim3(256), 0, st, m, l, acc, rows, splits, out); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_stream(const StreamArgs& sa, int head_dim, int page_size, hipStream_t st) {
+  switch (head_dim) {
+    case 64: return launch_s<64>(sa, page_size, st);
+    case 128: return launch_s<128>(sa, page_size, st);
+    default: return launch_s<256>(sa, page_size, st);
+  }
+}
+
+hipError_t launch_stream_merge(const StreamArgs& sa, int head_dim, hipStream_t st) {
+  dim3 grid(2 * sa.num_waves);
+  switch (head_dim) {
+    case 64: hipLaunchKernelGGL(stream_merge_kernel<64>, grid, dim3(64), 0, st, sa); break;
+    case 128: hipLaunchKernelGGL(stream_merge_kernel<128>, grid, dim3(64), 0, st, sa); break;
+    default: hipLaunchKernelGGL(stream_merge_kernel<256>, grid, dim3(64), 0, st, sa); break;
   }
   return hipGetLastError();
 }

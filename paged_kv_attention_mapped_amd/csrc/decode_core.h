@@ -1,0 +1,209 @@
+// The per-wave decode machinery shared by the split-K and the stream-K
+// decode kernels: one wave attends the query-head group of one KV head over
+// a run of page steps and keeps an online softmax in registers.
+//
+// Layout of the work inside a wave.  A step is UT tokens of one page.
+//   * K is loaded in the A-operand layout of v_mfma_f32_16x16x32_bf16
+//     (rows = 16 tokens, k = 32 head-dim elements), and the scores of all
+//     query heads of the group come out of one MFMA per 32 head-dim
+//     elements (columns = heads).  K needs no transpose: the contraction
+//     runs over head_dim, its contiguous axis.
+//   * V is loaded row-major, 16 lanes per token row (16 B per lane for
+//     D=128), so every load instruction reads whole contiguous rows.
+//   * The A rows are permuted so that lane row j (lanes 16j..16j+15) of the
+//     score tile holds tokens j, j+4, j+8, ... of the step -- exactly the
+//     tokens whose V rows lane row j loaded.  Each lane row therefore runs
+//     its own online softmax per head, lane-locally, and a lane gets the
+//     probability of head h from lane h of its own row with a DPP
+//     row_newbcast.  PV accumulates in fp32 on the vector ALUs.
+//   * Rows outside [first_key, L) (sequence tail, window start, unusable
+//     page) are selected away -- score -inf, V row 0 -- so stale data in a
+//     page (NaN in tests) never reaches the result.
+#pragma once
+
+#include <limits.h>
+#include <math.h>
+
+#include "common.h"
+
+namespace pkv {
+
+template <int CH>
+struct VChunkT;
+template <>
+struct VChunkT<8> { using type = uint4; };
+template <>
+struct VChunkT<4> { using type = uint2; };
+
+__device__ __forceinline__ void unpack(const uint4& v, float* f) {
+  f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+  f[4] = bf_lo(v.z); f[5] = bf_hi(v.z); f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
+}
+__device__ __forceinline__ void unpack(const uint2& v, float* f) {
+  f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+}
+
+template <int D, int PS, int G, int UT_>
+struct WaveDecoder {
+  static constexpr int UT = UT_ < PS ? UT_ : PS;  // tokens per step
+  static constexpr int UPP = PS / UT;             // steps per page
+  static constexpr int EPL = D / 16;              // head-dim elements per lane (PV side)
+  static constexpr int CH = EPL < 8 ? EPL : 8;    // elements per V load (8 B or 16 B)
+  static constexpr int NCH = EPL / CH;            // V loads per token per lane
+  static constexpr int KT = UT / 16;              // 16-token MFMA tiles per step
+  static constexpr int KB = D / 32;               // MFMA k-steps over head_dim
+  static constexpr int TPR = UT / 4;              // tokens per lane row per step
+  static_assert(G <= 16, "group larger than one MFMA column tile");
+  static_assert(UT % 16 == 0 && PS % UT == 0, "a step is whole MFMA tiles of a page");
+  using VChunk = typename VChunkT<CH>::type;
+
+  struct Buf {
+    uint4 k[KT][KB];
+    VChunk v[TPR][NCH];
+  };
+
+  int jj, n, tok_a;
+  float m_run, l_run;
+  float acc[G][EPL];
+  bf16x8 qop[KB];
+
+  __device__ __forceinline__ void init(int lane) {
+    jj = lane >> 4;
+    n = lane & 15;
+    // A-operand row n holds token 4*(n%4) + n/4 of each 16-token tile, so
+    // score register r of lane row jj is token 4r + jj.
+    tok_a = 4 * (n & 3) + (n >> 2);
+  }
+
+  __device__ __forceinline__ void reset() {
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+
+  // Q^T as the B operand: lane (jj, n) holds q[head n][32kb + 8jj .. +7];
+  // qg points at the group's first query head, heads >= g read as zero.
+  __device__ __forceinline__ void load_q(const uint16_t* qg, int g) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (n < g) v = *reinterpret_cast<const uint4*>(qg + n * D + 32 * kb + 8 * jj);
+      qop[kb] = as_bf16x8(v);
+    }
+  }
+
+  // Issue the loads of one step; krow/vrow point at the step's first token row.
+  __device__ __forceinline__ void load(Buf& bf, const uint16_t* krow, const uint16_t* vrow) const {
+    const auto kr = make_rsrc(krow, UT * D * 2);
+    const auto vr = make_rsrc(vrow, UT * D * 2);
+#pragma unroll
+    for (int ti = 0; ti < KT; ++ti)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        bf.k[ti][kb] = buffer_load16(kr, 2 * ((ti * 16 + tok_a) * D + 32 * kb + 8 * jj));
+#pragma unroll
+    for (int i = 0; i < TPR; ++i)
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch)
+        buffer_load(bf.v[i][ch], vr, 2 * ((4 * i + jj) * D + CH * n + 16 * CH * ch));
+  }
+
+  // Fold one step into the running state.  Tokens tok0 .. tok0+UT-1 of the
+  // sequence; the ones outside [lo, hi) are masked.
+  __device__ __forceinline__ void process(const Buf& bf, int tok0, int lo, int hi,
+                                          float scale_log2) {
+    float x[TPR];
+#pragma unroll
+    for (int ti = 0; ti < KT; ++ti) {
+      f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) c = mfma16(as_bf16x8(bf.k[ti][kb]), qop[kb], c);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[4 * ti + r] = c[r] * scale_log2;
+    }
+    const bool partial = (tok0 < lo) || (tok0 + UT > hi);
+    uint32_t keep = 0xffffffffu;
+    if (partial) {
+      keep = 0;
+#pragma unroll
+      for (int i = 0; i < TPR; ++i) {
+        const int t = tok0 + 4 * i + jj;
+        const bool ok = t >= lo && t < hi;
+        keep |= (ok ? 1u : 0u) << i;
+        x[i] = ok ? x[i] : -INFINITY;
+      }
+    }
+    float pmax = x[0];
+#pragma unroll
+    for (int i = 1; i < TPR; ++i) pmax = fmaxf(pmax, x[i]);
+    const float m_new = fmaxf(m_run, pmax);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < TPR; ++i) {
+      x[i] = fast_exp2(x[i] - m_use);
+      psum += x[i];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+
+    static_for<0, G>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      const float ah = row_bcast<h>(alpha);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= ah;
+    });
+#pragma unroll
+    for (int i = 0; i < TPR; ++i) {
+      float vf[EPL];
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) unpack(bf.v[i][ch], vf + ch * CH);
+      if (partial) {
+        const bool ok = (keep >> i) & 1u;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) vf[e] = ok ? vf[e] : 0.f;
+      }
+      static_for<0, G>([&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        const float ph = row_bcast<h>(x[i]);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(ph, vf[e], acc[h][e]);
+      });
+    }
+  }
+
+  // Merge the four lane-row streams.  Afterwards every lane (jj, n) holds
+  // the wave maximum M (log2 units) and sum of head n, and every lane row
+  // holds the merged accumulator (relative to M).
+  __device__ __forceinline__ void merge_rows(float& M, float& lsum) {
+    M = m_run;
+    M = fmaxf(M, __shfl_xor(M, 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
+    const float f = (M == -INFINITY) ? 0.f : fast_exp2(m_run - M);
+    lsum = l_run * f;
+    lsum += __shfl_xor(lsum, 16);
+    lsum += __shfl_xor(lsum, 32);
+    static_for<0, G>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      const float fh = row_bcast<h>(f);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float v = acc[h][e] * fh;
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        acc[h][e] = v;
+      }
+    });
+  }
+
+  // Head-dim index of accumulator element e of this lane.
+  __device__ __forceinline__ int dim_of(int e) const {
+    return CH * n + (e % CH) + 16 * CH * (e / CH);
+  }
+};
+
+}  // namespace pkv

@@ -31,8 +31,9 @@ def declared():
 def test_header_declares_the_entry_points():
     assert declared() == sorted([
         "pkv_append", "pkv_decode", "pkv_decode_combine", "pkv_decode_plan", "pkv_decode_split",
-        "pkv_decode_workspace_bytes", "pkv_prefill_varlen", "pkv_slot_mapping",
-        "pkv_status_string"])
+        "pkv_decode_stream", "pkv_decode_stream_merge", "pkv_decode_stream_waves",
+        "pkv_decode_stream_workspace_bytes", "pkv_decode_workspace_bytes", "pkv_prefill_varlen",
+        "pkv_slot_mapping", "pkv_status_string"])
 
 
 def test_library_exports_every_declared_symbol(P):
@@ -109,8 +110,14 @@ def test_decode_plan(P):
         if w:
             pages = min(pages, -(-(w - 1) // ps) + 1)
         assert s * pps >= pages and (s - 1) * pps < pages
-        need = P.decode_workspace_bytes(B, hkv * 4, 128, hkv, ps, L, w)
+        need = P.decode_workspace_bytes(B, hkv * 4, 128, hkv, ps, L, w, s)
         assert need == (0 if s == 1 else B * hkv * 4 * s * 130 * 4)
     assert P.decode_plan(256, 8, 32, 8193) == (9, 32)
+    # stream-K: waves bounded by the work and by the device (256 CUs assumed without a GPU)
+    assert P.decode_stream_waves(4, 1, 64, 16, 64) == 4
+    assert P.decode_stream_waves(256, 8, 128, 32, 8193) == 256 * 4 * 2
+    nw = P.decode_stream_waves(256, 8, 128, 32, 8193)
+    assert P.decode_workspace_bytes(256, 32, 128, 8, 32, 8193) == \
+        P.lib().pkv_decode_stream_workspace_bytes(nw, 32, 8, 128)
     assert P.decode_plan(4, 8, 32, 1000, 0, 7) == (7, 5)
     assert P.decode_plan(4, 8, 32, 1000, 0, 1)[0] == 1

@@ -158,6 +158,46 @@ def test_split_count_invariance_and_determinism(P, splits):
     check_close(a, ref, f"splits={splits}")
 
 
+@pytest.mark.parametrize("name", ["tiny_decode", "qwen3_decode", "window_shared", "edges"])
+def test_stream_decode_any_partition(P, name):
+    """Stream-K with many wave counts: every cut of the flattened page list
+    must give the oracle's result, deterministically."""
+    if name == "edges":
+        wl = W.make("qwen3_decode", decode_ctx=("fixed", (0, 31, 32, 63, 64, 1023, 5)),
+                    name="edges")
+        g = GpuPools(wl)
+        g.write("prefix")
+        g.write("new")
+    else:
+        g = state(name)
+        wl = g.wl
+    o = OraclePools(wl)
+    lens = wl.decode_seq_lens().copy()
+    if name == "edges":
+        lens[0] = 0  # an empty row
+    auto = P.decode_stream_waves(wl.n_decode, wl.num_kv_heads, wl.head_dim, wl.page_size,
+                                 int(lens.max()), wl.window)
+    for layer in range(wl.num_layers):
+        qd, _ = wl.queries(layer)
+        ref = oracle.decode(qd, o.k, o.v, wl.block_tables[:wl.n_decode], lens, wl.page_size,
+                            wl.scale, wl.window)
+        for nw in sorted({1, 2, 3, 7, 64, 1000, auto}):
+            say(f"[decode_stream] {name} layer {layer} num_waves={nw}")
+            outs = []
+            for _ in range(2):
+                out, ws = P.decode_stream(dev_bits(qd), g.k, g.v,
+                                          dev_i32(wl.block_tables[:wl.n_decode]), dev_i32(lens),
+                                          page_size=wl.page_size, num_waves=nw, scale=wl.scale,
+                                          window=wl.window)
+                P.decode_stream_merge(ws, out, num_waves=nw, num_kv_heads=wl.num_kv_heads)
+                torch.cuda.synchronize()
+                outs.append(host_bits(out))
+            assert np.array_equal(outs[0], outs[1]), "stream-K decode is not deterministic"
+            check_close(outs[0], ref, f"{name} nw={nw}")
+            if name == "edges":
+                assert np.all(outs[0][0] == 0)  # the empty row
+
+
 @pytest.mark.parametrize("name", ["qwen3_decode", "window_shared"])
 def test_decode_split_partials(P, name):
     g = state(name)
