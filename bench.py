@@ -318,7 +318,7 @@ def _subset(wl, seqs):
 # measured traffic (rocprofv3 counters, recorded under profiles/)
 # ---------------------------------------------------------------------------
 def recorded_traffic(config: str, src_hash: str):
-    path = os.path.join(ROOT, "profiles", f"{config}_decode_split_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"{config}_decode_traffic.txt")
     if not os.path.exists(path):
         return None
     vals = {}
