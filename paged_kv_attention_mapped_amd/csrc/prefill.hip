@@ -9,17 +9,23 @@
 // no per-key document lookup is ever made (the same log reports that such
 // per-kv lookups were the slow path of the packed prefill mask).
 //
-// Work decomposition.  A workgroup owns up to 128 query rows of one
-// sequence for up to four query heads of one KV group; its waves each own
-// 32 rows of one head.  K/V tiles of 64 keys are gathered page by page
-// into LDS once per workgroup and shared by all its heads.
+// Work decomposition.  A workgroup of eight waves owns up to 32*QB query
+// rows of one sequence for HW query heads of one KV group (HW*QB = 8); each
+// wave owns 32 rows of one head.  K/V tiles of 64 keys are gathered page by
+// page into LDS once per workgroup, double-buffered, and shared by all its
+// heads and rows; the next tile's global loads are in flight while the
+// current tile is multiplied, and one barrier per tile separates them.
 //   S^T = K Q^T  on v_mfma_f32_32x32x16_bf16: A = K rows straight from LDS,
 //                B = Q rows held in registers; the result keeps one query
 //                row per lane column, so the softmax row statistics are
 //                lane-local plus one exchange with the lane 32 away.
 //   O^T += V^T P^T: the probabilities already sit in B-operand order in the
-//                score registers (only rounded to bf16); V is stored
-//                transposed in LDS while it is being staged.
+//                score registers (only rounded to bf16); V stays row-major
+//                in LDS and is read transposed with ds_read_b64_tr_b16.
+// Softmax: p = 2^(s*c - m*c) with c = scale*log2(e) in one FMA; the running
+// maximum is raised only when a tile's maximum exceeds it by more than
+// kRescaleSlack (in log2 units), which keeps p <= 2^kRescaleSlack and skips
+// most rescales of the accumulator.
 #include <math.h>
 
 #include "common.h"
@@ -27,27 +33,33 @@
 namespace pkv {
 namespace {
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr float kRescaleSlack = 8.0f;
+
 template <int D, int HW>
 struct PrefillCfg {
-  static constexpr int NW = 4;                 // waves per workgroup
+  static constexpr int NW = D == 256 ? 4 : 8;  // waves per workgroup (D=256: register budget)
+  static constexpr int NT = NW * 64;           // threads
   static constexpr int QB = NW / HW;           // 32-row query blocks per workgroup
   static constexpr int BM = 32 * QB;           // query rows per workgroup
   static constexpr int BN = 64;                // keys per tile
-  static constexpr int KPAD = D + 8;           // LDS row stride of K (elements)
-  static constexpr int VPAD = BN + 4;          // LDS row stride of V^T (elements)
+  static constexpr int KP = D + 8;             // LDS row pitch of K (elements)
+  static constexpr int VP = D + 16;            // LDS row pitch of V (elements)
   static constexpr int KS = D / 16;            // k-steps of S^T
   static constexpr int DT = D / 32;            // 32-row tiles of O^T
   static constexpr int CPR = D / 8;            // 16-byte chunks per token row
-  static constexpr int KCH = BN * CPR / 256;   // K chunks per thread per tile
-  static constexpr int VTASK = (BN / 4) * CPR; // (4 keys x 1 chunk) V tasks per tile
-  static constexpr int VPT = (VTASK + 255) / 256;
+  static constexpr int CH = BN * CPR / NT;     // K (and V) chunks per thread per tile
+  static constexpr int TILE = BN * KP + BN * VP;  // elements of one LDS buffer
+  static_assert(CH >= 1 && BN * CPR % NT == 0, "tile chunks must split evenly");
+  static_assert(QB >= 1, "more heads than waves");
 };
 
 template <int D, int PS, int HW>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a, int nqb) {
+__global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(PrefillArgs a, int nqb) {
   using C = PrefillCfg<D, HW>;
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[C::BN * C::KPAD];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * C::VPAD];
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];  // 2 x (K tile, V tile)
 
   const int HG = a.group / HW;  // workgroups per KV head along the heads
   const int j = blockIdx.z;
@@ -75,7 +87,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a, int nqb) {
   bf16x8 qop[C::KS];
   {
     const bool ok = qrow < Lq;
-    const uint16_t* qp = a.q + ((int64_t)(q_start + (ok ? qrow : 0)) * a.num_q_heads + head) * D + 8 * hh;
+    const uint16_t* qp =
+        a.q + ((int64_t)(q_start + (ok ? qrow : 0)) * a.num_q_heads + head) * D + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       uint4 v = make_uint4(0, 0, 0, 0);
@@ -93,91 +106,70 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a, int nqb) {
   const int w_last = min(r0 + 31, Lq - 1);
   const int wpmin = shift + r0, wpmax = shift + w_last;
   const int mypos = shift + qrow;
+  const float c = a.scale_log2;
 
   f32x16 acc[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY;  // running max of raw scores (this lane's query row)
+  float l_run = 0.f;        // this lane's partial sum of p
 
   const uint16_t* kh = a.k_pool + (int64_t)hk * a.head_stride;
   const uint16_t* vh = a.v_pool + (int64_t)hk * a.head_stride;
   const int32_t* bt_row = a.block_tables + (int64_t)j * a.max_pages;
 
-  uint4 kreg[C::KCH];
-  uint4 vreg[C::VPT][4];
-
-  auto row_addr = [&](int kpos, int64_t& off) -> bool {
-    if (kpos >= kend) return false;
-    const int phys = bt_row[kpos / PS];
-    if (phys < 0 || phys >= a.num_pages) return false;
-    off = ((int64_t)phys * PS + (kpos % PS)) * D;
-    return true;
-  };
+  uint4 kreg[C::CH], vreg[C::CH];
   auto load_tile = [&](int k0) {
 #pragma unroll
-    for (int it = 0; it < C::KCH; ++it) {
-      const int ci = tid + 256 * it;
-      const int key = ci / C::CPR, c = ci - key * C::CPR;
-      int64_t off;
-      kreg[it] = row_addr(k0 + key, off) ? *reinterpret_cast<const uint4*>(kh + off + 8 * c)
-                                         : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int it = 0; it < C::VPT; ++it) {
-      const int vt = tid + 256 * it;
-      const int kg = vt / C::CPR, c = vt - kg * C::CPR;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int64_t off;
-        vreg[it][i] = (vt < C::VTASK && row_addr(k0 + 4 * kg + i, off))
-                          ? *reinterpret_cast<const uint4*>(vh + off + 8 * c)
-                          : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int it = 0; it < C::KCH; ++it) {
-      const int ci = tid + 256 * it;
-      const int key = ci / C::CPR, c = ci - key * C::CPR;
-      *reinterpret_cast<uint4*>(&k_lds[key * C::KPAD + 8 * c]) = kreg[it];
-    }
-#pragma unroll
-    for (int it = 0; it < C::VPT; ++it) {
-      const int vt = tid + 256 * it;
-      if (vt >= C::VTASK) continue;
-      const int kg = vt / C::CPR, c = vt - kg * C::CPR;
-      const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vreg[it][0]);
-      const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vreg[it][1]);
-      const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&vreg[it][2]);
-      const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&vreg[it][3]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int wd = e >> 1;
-        uint2 t;
-        if (e & 1) {
-          t.x = (v0[wd] >> 16) | (v1[wd] & 0xffff0000u);
-          t.y = (v2[wd] >> 16) | (v3[wd] & 0xffff0000u);
-        } else {
-          t.x = (v0[wd] & 0xffffu) | (v1[wd] << 16);
-          t.y = (v2[wd] & 0xffffu) | (v3[wd] << 16);
+    for (int it = 0; it < C::CH; ++it) {
+      const int ci = tid + C::NT * it;
+      const int key = ci / C::CPR, cc = ci - key * C::CPR;
+      const int kpos = k0 + key;
+      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (kpos < kend) {
+        const int phys = bt_row[kpos / PS];
+        if (phys >= 0 && phys < a.num_pages) {
+          const int64_t off = ((int64_t)phys * PS + (kpos % PS)) * D + 8 * cc;
+          kv = *reinterpret_cast<const uint4*>(kh + off);
+          vv = *reinterpret_cast<const uint4*>(vh + off);
         }
-        *reinterpret_cast<uint2*>(&vt_lds[(8 * c + e) * C::VPAD + 4 * kg]) = t;
       }
+      kreg[it] = kv;
+      vreg[it] = vv;
     }
   };
+  auto store_tile = [&](int buf) {
+    uint16_t* kl = smem + buf * C::TILE;
+    uint16_t* vl = kl + C::BN * C::KP;
+#pragma unroll
+    for (int it = 0; it < C::CH; ++it) {
+      const int ci = tid + C::NT * it;
+      const int key = ci / C::CPR, cc = ci - key * C::CPR;
+      *reinterpret_cast<uint4*>(kl + key * C::KP + 8 * cc) = kreg[it];
+      *reinterpret_cast<uint4*>(vl + key * C::VP + 8 * cc) = vreg[it];
+    }
+  };
+
+  // transposed-read geometry (ds_read_b64_tr_b16, 16-lane groups): source
+  // lane 4r+a of a group reads V[key0 + r][d0 + 4a .. +3]; output lane i of
+  // the group then holds V[key0 .. key0+3][d0 + i].
+  const int grp = lane >> 4, gi = lane & 15;
+  const int tr_key = 4 * (grp >> 1) + (gi >> 2);       // + 16u (+8 for the second half)
+  const int tr_d = 16 * (grp & 1) + 4 * (gi & 3);      // + 32dt
 
   if (kend > kstart) {
     const int t_first = kstart / C::BN, t_last = (kend - 1) / C::BN;
     load_tile(t_first * C::BN);
+    store_tile(0);
+    __syncthreads();
     for (int t = t_first; t <= t_last; ++t) {
       const int k0 = t * C::BN;
-      __syncthreads();
-      store_tile();
-      __syncthreads();
+      const int cur = (t - t_first) & 1;
       if (t < t_last) load_tile(k0 + C::BN);
+      const uint16_t* kl = smem + cur * C::TILE;
+      const uint16_t* vl = kl + C::BN * C::KP;
 
       // ---- S^T = K Q^T for 64 keys x 32 rows ----
       f32x16 st[2];
@@ -185,7 +177,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a, int nqb) {
       for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) st[kt][r] = 0.f;
-        const uint16_t* krow = &k_lds[(32 * kt + col) * C::KPAD + 8 * hh];
+        const uint16_t* krow = kl + (32 * kt + col) * C::KP + 8 * hh;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
           const uint4 kv = *reinterpret_cast<const uint4*>(krow + 16 * ks);
@@ -193,64 +185,81 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a, int nqb) {
         }
       }
       // register r of tile kt is key k0 + 32kt + 8(r/4) + 4hh + r%4
-      float x[2][16];
       const bool need_mask = (k0 + C::BN - 1 > wpmin) ||
                              (a.window > 0 && wpmax - k0 >= a.window) || (k0 + C::BN > Lk);
+      if (need_mask) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = st[kt][r] * a.scale_log2;
-          if (need_mask) {
+          for (int r = 0; r < 16; ++r) {
             const int kp = k0 + 32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3);
             const bool ok = kp <= mypos && kp < Lk && (a.window <= 0 || mypos - kp < a.window);
-            v = ok ? v : -INFINITY;
+            st[kt][r] = ok ? st[kt][r] : -INFINITY;
           }
-          x[kt][r] = v;
-        }
+      }
       float tmax = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, x[kt][r]);
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[kt][r]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m_run, tmax);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
+      // raise the running max only when this tile exceeds it by the slack
+      const bool raise = (tmax - m_run) * c > kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        const float m_new = raise ? tmax : m_run;
+        const float alpha = raise ? fast_exp2((m_run - m_new) * c) : 1.f;  // 0 from -inf
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+        m_run = m_new;
+      }
+      const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
       float psum = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          x[kt][r] = fast_exp2(x[kt][r] - m_use);
-          psum += x[kt][r];
+          const float p = fast_exp2(fmaf(st[kt][r], c, -mc));
+          st[kt][r] = p;
+          psum += p;
         }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      l_run += psum;
 
       // ---- O^T += V^T P^T, 16 keys per step ----
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const float* pu = &x[u >> 1][8 * (u & 1)];
+        const f32x16& sv = st[u >> 1];
+        const int o8 = 8 * (u & 1);
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        bf16x2 p01 = {(__bf16)sv[o8 + 0], (__bf16)sv[o8 + 1]};
+        bf16x2 p23 = {(__bf16)sv[o8 + 2], (__bf16)sv[o8 + 3]};
+        bf16x2 p45 = {(__bf16)sv[o8 + 4], (__bf16)sv[o8 + 5]};
+        bf16x2 p67 = {(__bf16)sv[o8 + 6], (__bf16)sv[o8 + 7]};
         uint4 pp;
-        pp.x = pack_bf16x2(pu[0], pu[1]);
-        pp.y = pack_bf16x2(pu[2], pu[3]);
-        pp.z = pack_bf16x2(pu[4], pu[5]);
-        pp.w = pack_bf16x2(pu[6], pu[7]);
+        pp.x = __builtin_bit_cast(uint32_t, p01);
+        pp.y = __builtin_bit_cast(uint32_t, p23);
+        pp.z = __builtin_bit_cast(uint32_t, p45);
+        pp.w = __builtin_bit_cast(uint32_t, p67);
         const bf16x8 pop = as_bf16x8(pp);
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
-          const uint16_t* vrow = &vt_lds[(32 * dt + col) * C::VPAD + 16 * u + 4 * hh];
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-          const uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
+          const uint16_t* v0 = vl + (16 * u + tr_key) * C::VP + 32 * dt + tr_d;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)v0);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(v0 + 8 * C::VP));
+          uint4 vv;
+          vv.x = (uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+          vv.y = (uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+          vv.z = (uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+          vv.w = (uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
           acc[dt] = mfma32(as_bf16x8(vv), pop, acc[dt]);
         }
       }
+      if (t < t_last) store_tile(cur ^ 1);
+      __syncthreads();
     }
   }
 
@@ -276,12 +285,24 @@ hipError_t launch_p3(const PrefillArgs& a, int num_seqs, int max_q, hipStream_t 
   using C = PrefillCfg<D, HW>;
   const int nqb = (max_q + C::BM - 1) / C::BM;
   dim3 grid(nqb, a.num_kv_heads * (a.group / HW), num_seqs);
-  hipLaunchKernelGGL((prefill_kernel<D, PS, HW>), grid, dim3(256), 0, st, a, nqb);
+  const size_t smem = 2 * (size_t)C::TILE * sizeof(uint16_t);
+  static bool attr_set = false;  // raise the dynamic LDS limit once (above 64 KB)
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&prefill_kernel<D, PS, HW>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((prefill_kernel<D, PS, HW>), grid, dim3(C::NT), smem, st, a, nqb);
   return hipGetLastError();
 }
 
 template <int D, int PS>
 hipError_t launch_p2(const PrefillArgs& a, int num_seqs, int max_q, hipStream_t st) {
+  if constexpr (D != 256) {
+    if (a.group % 8 == 0) return launch_p3<D, PS, 8>(a, num_seqs, max_q, st);
+  }
   if (a.group % 4 == 0) return launch_p3<D, PS, 4>(a, num_seqs, max_q, st);
   if (a.group % 2 == 0) return launch_p3<D, PS, 2>(a, num_seqs, max_q, st);
   return launch_p3<D, PS, 1>(a, num_seqs, max_q, st);
