@@ -11,10 +11,12 @@
 //
 // Work decomposition.  A workgroup of eight waves owns up to 32*QB query
 // rows of one sequence for HW query heads of one KV group (HW*QB = 8); each
-// wave owns 32 rows of one head.  K/V tiles of 64 keys are gathered page by
-// page into LDS once per workgroup, double-buffered, and shared by all its
-// heads and rows; the next tile's global loads are in flight while the
-// current tile is multiplied, and one barrier per tile separates them.
+// wave owns 32 rows of one head.  K/V tiles of BN keys are gathered page by
+// page into LDS once per workgroup (three buffers) and shared by all its
+// heads and rows.  The key loop is software-pipelined: while the vector
+// ALUs turn tile t's scores into probabilities, the matrix cores already
+// compute tile t+1's scores, and tile t+3's global loads are in flight;
+// one barrier per tile.
 //   S^T = K Q^T  on v_mfma_f32_32x32x16_bf16: A = K rows straight from LDS,
 //                B = Q rows held in registers; the result keeps one query
 //                row per lane column, so the softmax row statistics are
@@ -38,15 +40,31 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kRescaleSlack = 8.0f;
 
+// Tuning knobs (fixed at build time): waves per workgroup for D <= 128 and
+// keys per tile.
+#ifndef PKV_PREFILL_WAVES
+#define PKV_PREFILL_WAVES 8
+#endif
+#ifndef PKV_PREFILL_KEYS
+#define PKV_PREFILL_KEYS 64
+#endif
+#ifndef PKV_PREFILL_KPAD
+#define PKV_PREFILL_KPAD 8      // K row pad (elements)
+#endif
+#ifndef PKV_PREFILL_VPAD
+#define PKV_PREFILL_VPAD 32     // V row pad (elements)
+#endif
+
 template <int D, int HW>
 struct PrefillCfg {
-  static constexpr int NW = D == 256 ? 4 : 8;  // waves per workgroup (D=256: register budget)
+  static constexpr int NW = D == 256 ? 4 : PKV_PREFILL_WAVES;  // waves per workgroup
   static constexpr int NT = NW * 64;           // threads
   static constexpr int QB = NW / HW;           // 32-row query blocks per workgroup
   static constexpr int BM = 32 * QB;           // query rows per workgroup
-  static constexpr int BN = 64;                // keys per tile
-  static constexpr int KP = D + 8;             // LDS row pitch of K (elements)
-  static constexpr int VP = D + 16;            // LDS row pitch of V (elements)
+  static constexpr int BN = D == 256 ? 32 : PKV_PREFILL_KEYS;  // keys per tile
+  static constexpr int KT = BN / 32;           // 32-key tiles of S^T
+  static constexpr int KP = D + PKV_PREFILL_KPAD;  // LDS row pitch of K (elements)
+  static constexpr int VP = D + PKV_PREFILL_VPAD;  // LDS row pitch of V (elements)
   static constexpr int KS = D / 16;            // k-steps of S^T
   static constexpr int DT = D / 32;            // 32-row tiles of O^T
   static constexpr int CPR = D / 8;            // 16-byte chunks per token row
@@ -59,13 +77,15 @@ struct PrefillCfg {
 template <int D, int PS, int HW>
 __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(PrefillArgs a, int nqb) {
   using C = PrefillCfg<D, HW>;
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];  // 2 x (K tile, V tile)
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];  // 3 x (K tile, V tile)
 
+  // grid: x = (KV head, head group), y = sequence, z = query block counted
+  // from the end, so the longest (latest) blocks of every sequence go first
   const int HG = a.group / HW;  // workgroups per KV head along the heads
-  const int j = blockIdx.z;
-  const int hk = blockIdx.y / HG;
-  const int hg = blockIdx.y - hk * HG;
-  const int qb = nqb - 1 - (int)blockIdx.x;  // late (long) query blocks first
+  const int j = blockIdx.y;
+  const int hk = blockIdx.x / HG;
+  const int hg = blockIdx.x - hk * HG;
+  const int qb = nqb - 1 - (int)blockIdx.z;
 
   const int q_start = a.cu_q[j];
   const int Lq = a.cu_q[j + 1] - q_start;
@@ -159,37 +179,51 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   const int tr_key = 4 * (grp >> 1) + (gi >> 2);       // + 16u (+8 for the second half)
   const int tr_d = 16 * (grp & 1) + 4 * (gi & 3);      // + 32dt
 
+  // S^T tile of keys k0.. from the LDS buffer of that tile
+  auto qk = [&](f32x16* st, int buf) {
+    const uint16_t* kl = smem + buf * C::TILE;
+#pragma unroll
+    for (int kt = 0; kt < C::KT; ++kt) {
+      const uint16_t* krow = kl + (32 * kt + col) * C::KP + 8 * hh;
+      f32x16 s = {};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(krow + 16 * ks);
+        s = mfma32(as_bf16x8(kv), qop[ks], s);
+      }
+      st[kt] = s;
+    }
+  };
+
   if (kend > kstart) {
+    // Pipeline over key tiles t (three LDS buffers, tile t in buffer t % 3):
+    //   iteration t: store tile t+2 (fetched during iteration t-1) into the
+    //   buffer tile t-1 used, issue the global loads of tile t+3; S(t+1) =
+    //   K(t+1) Q^T on the matrix cores while the vector ALUs turn S(t) into
+    //   probabilities; O += V(t) P(t); one barrier.
     const int t_first = kstart / C::BN, t_last = (kend - 1) / C::BN;
+    auto bufof = [&](int t) { return (t - t_first) % 3; };
     load_tile(t_first * C::BN);
     store_tile(0);
+    if (t_first + 1 <= t_last) {
+      load_tile((t_first + 1) * C::BN);
+      store_tile(1);
+    }
     __syncthreads();
+    if (t_first + 2 <= t_last) load_tile((t_first + 2) * C::BN);
+    f32x16 st[C::KT], sn[C::KT];
+    qk(st, 0);
     for (int t = t_first; t <= t_last; ++t) {
       const int k0 = t * C::BN;
-      const int cur = (t - t_first) & 1;
-      if (t < t_last) load_tile(k0 + C::BN);
-      const uint16_t* kl = smem + cur * C::TILE;
-      const uint16_t* vl = kl + C::BN * C::KP;
+      if (t + 2 <= t_last) store_tile(bufof(t + 2));  // loads issued one iteration ago
+      if (t + 3 <= t_last) load_tile((t + 3) * C::BN);  // in flight for a whole iteration
 
-      // ---- S^T = K Q^T for 64 keys x 32 rows ----
-      f32x16 st[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st[kt][r] = 0.f;
-        const uint16_t* krow = kl + (32 * kt + col) * C::KP + 8 * hh;
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          const uint4 kv = *reinterpret_cast<const uint4*>(krow + 16 * ks);
-          st[kt] = mfma32(as_bf16x8(kv), qop[ks], st[kt]);
-        }
-      }
       // register r of tile kt is key k0 + 32kt + 8(r/4) + 4hh + r%4
       const bool need_mask = (k0 + C::BN - 1 > wpmin) ||
                              (a.window > 0 && wpmax - k0 >= a.window) || (k0 + C::BN > Lk);
       if (need_mask) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < C::KT; ++kt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kp = k0 + 32 * kt + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -199,7 +233,7 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
       }
       float tmax = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < C::KT; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[kt][r]);
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
@@ -216,33 +250,39 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
         m_run = m_new;
       }
       const float mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-      float psum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(st[kt][r], c, -mc));
-          st[kt][r] = p;
-          psum += p;
-        }
-      l_run += psum;
 
-      // ---- O^T += V^T P^T, 16 keys per step ----
+      // next tile's scores on the matrix cores, this tile's probabilities on
+      // the VALU (unconditional, so both sit in one block the scheduler can
+      // interleave; after the last tile the result is simply unused)
+      qk(sn, bufof(t + 1));
+      float psum = 0.f;
+      bf16x8 pop[C::BN / 16];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const f32x16& sv = st[u >> 1];
-        const int o8 = 8 * (u & 1);
+      for (int u = 0; u < C::BN / 16; ++u) {
         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        bf16x2 p01 = {(__bf16)sv[o8 + 0], (__bf16)sv[o8 + 1]};
-        bf16x2 p23 = {(__bf16)sv[o8 + 2], (__bf16)sv[o8 + 3]};
-        bf16x2 p45 = {(__bf16)sv[o8 + 4], (__bf16)sv[o8 + 5]};
-        bf16x2 p67 = {(__bf16)sv[o8 + 6], (__bf16)sv[o8 + 7]};
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = fast_exp2(fmaf(st[u >> 1][8 * (u & 1) + e], c, -mc));
+          psum += p[e];
+        }
+        bf16x2 p01 = {(__bf16)p[0], (__bf16)p[1]};
+        bf16x2 p23 = {(__bf16)p[2], (__bf16)p[3]};
+        bf16x2 p45 = {(__bf16)p[4], (__bf16)p[5]};
+        bf16x2 p67 = {(__bf16)p[6], (__bf16)p[7]};
         uint4 pp;
         pp.x = __builtin_bit_cast(uint32_t, p01);
         pp.y = __builtin_bit_cast(uint32_t, p23);
         pp.z = __builtin_bit_cast(uint32_t, p45);
         pp.w = __builtin_bit_cast(uint32_t, p67);
-        const bf16x8 pop = as_bf16x8(pp);
+        pop[u] = as_bf16x8(pp);
+      }
+      l_run += psum;
+
+      // ---- O^T += V^T P^T, 16 keys per step ----
+      const uint16_t* vl = smem + bufof(t) * C::TILE + C::BN * C::KP;
+#pragma unroll
+      for (int u = 0; u < C::BN / 16; ++u) {
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
           const uint16_t* v0 = vl + (16 * u + tr_key) * C::VP + 32 * dt + tr_d;
@@ -250,16 +290,15 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
               (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)v0);
           const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(v0 + 8 * C::VP));
-          uint4 vv;
-          vv.x = (uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-          vv.y = (uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-          vv.z = (uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-          vv.w = (uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
-          acc[dt] = mfma32(as_bf16x8(vv), pop, acc[dt]);
+          const uint2 l2 = __builtin_bit_cast(uint2, lo);
+          const uint2 h2 = __builtin_bit_cast(uint2, hi);
+          const uint4 vv = make_uint4(l2.x, l2.y, h2.x, h2.y);
+          acc[dt] = mfma32(as_bf16x8(vv), pop[u], acc[dt]);
         }
       }
-      if (t < t_last) store_tile(cur ^ 1);
       __syncthreads();
+#pragma unroll
+      for (int kt = 0; kt < C::KT; ++kt) st[kt] = sn[kt];
     }
   }
 
@@ -284,8 +323,8 @@ template <int D, int PS, int HW>
 hipError_t launch_p3(const PrefillArgs& a, int num_seqs, int max_q, hipStream_t st) {
   using C = PrefillCfg<D, HW>;
   const int nqb = (max_q + C::BM - 1) / C::BM;
-  dim3 grid(nqb, a.num_kv_heads * (a.group / HW), num_seqs);
-  const size_t smem = 2 * (size_t)C::TILE * sizeof(uint16_t);
+  dim3 grid(a.num_kv_heads * (a.group / HW), num_seqs, nqb);
+  const size_t smem = 3 * (size_t)C::TILE * sizeof(uint16_t);
   static bool attr_set = false;  // raise the dynamic LDS limit once (above 64 KB)
   if (!attr_set) {
     const hipError_t e = hipFuncSetAttribute(
@@ -300,7 +339,7 @@ hipError_t launch_p3(const PrefillArgs& a, int num_seqs, int max_q, hipStream_t 
 
 template <int D, int PS>
 hipError_t launch_p2(const PrefillArgs& a, int num_seqs, int max_q, hipStream_t st) {
-  if constexpr (D != 256) {
+  if constexpr (D != 256 && PKV_PREFILL_WAVES >= 8) {
     if (a.group % 8 == 0) return launch_p3<D, PS, 8>(a, num_seqs, max_q, st);
   }
   if (a.group % 4 == 0) return launch_p3<D, PS, 4>(a, num_seqs, max_q, st);
