@@ -26,16 +26,22 @@
 // most rescales of the accumulator.
 //
 // Ping-pong schedule.  Every key tile t costs each wave two phases: a
-// vector phase V(t) (mask, max, exponentials, P packing, staging of the
-// next tile) and a matrix phase M(t) (O += V(t) P(t), then S(t+1) =
-// K(t+1) Q^T).  The waves form two groups, one wave of each on every SIMD;
-// group B runs one phase behind group A, and a workgroup barrier closes
-// every phase, so on each SIMD one wave's MFMAs overlap the other wave's
-// softmax.  Group A stages K tiles and group B stages V tiles: K(t+1) is
-// written during A's V(t) and V(t+1) during B's V(t), which is exactly when
-// the tile two back is no longer read, so two LDS buffers per tensor
-// suffice.  Global loads run two tiles ahead of those stores and
-// block-table entries two tiles ahead of the loads.
+// vector phase V(t) (mask, max, exponentials, P packing, staging) and a
+// matrix phase M(t) (O += V(t) P(t), then S(t+1) = K(t+1) Q^T).  The waves
+// form two groups, one wave of each on every SIMD; group B runs one phase
+// behind group A, and a workgroup barrier closes every phase, so on each
+// SIMD one wave's MFMAs overlap the other wave's softmax.
+//
+// Staging.  Group A fetches K tiles and group B V tiles, straight from the
+// pool into LDS (buffer loads with the LDS destination; no registers, no
+// LDS store instructions) into four-deep rings.  Tiles are laid out in LDS
+// in the order the MFMAs consume them: a K tile as 1 KB blocks that each
+// hold one 32x16 A operand with lane l's 16 bytes at 16*l, a V tile as
+// 512-byte blocks that each feed one transposed read with lane l's 8 bytes
+// at 8*l.  Every LDS read of the loop is therefore one contiguous,
+// conflict-free block with a compile-time offset.  Tile t+3 is requested
+// in V(t) and waited for at the end of V(t+2); block-table entries are
+// read through the scalar cache one tile before their tile.
 #include <math.h>
 
 #include "common.h"
@@ -59,54 +65,75 @@ __device__ __forceinline__ float half_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Tuning knobs (fixed at build time) for head_dim <= 128: waves per
-// workgroup, keys per tile, LDS row pads, wave priority in matrix phases.
+// Tuning knobs (fixed at build time): waves per workgroup for head_dim
+// <= 128 (a tile holds 8 keys per wave), wave priority in matrix phases.
 #ifndef PKV_PREFILL_WAVES
 #define PKV_PREFILL_WAVES 8
 #endif
-#ifndef PKV_PREFILL_KEYS
-#define PKV_PREFILL_KEYS 64
-#endif
-#ifndef PKV_PREFILL_KPAD
-#define PKV_PREFILL_KPAD 8      // K row pad (elements)
-#endif
-#ifndef PKV_PREFILL_VPAD
-#define PKV_PREFILL_VPAD 32     // V row pad (elements)
+#ifndef PKV_PREFILL_LOOKAHEAD
+#define PKV_PREFILL_LOOKAHEAD 6  // MFMA jobs between an operand request and its use
 #endif
 #ifndef PKV_PREFILL_SETPRIO
-#define PKV_PREFILL_SETPRIO 1   // raise the matrix-phase wave's issue priority
+#define PKV_PREFILL_SETPRIO 0   // raise the matrix-phase wave's issue priority
 #endif
 
 template <int D, int HW>
 struct PrefillCfg {
   static constexpr int NW = D == 256 ? 4 : PKV_PREFILL_WAVES;  // waves per workgroup
   static constexpr int NT = NW * 64;           // threads
-  static constexpr int GT = NT / 2;            // threads per group
+  static constexpr int G = NW / 2;             // waves per group
   static constexpr int QB = NW / HW;           // waves along the rows
   static constexpr int BM = 32 * QB;           // query rows per workgroup
-  static constexpr int BN = D == 256 ? 32 : PKV_PREFILL_KEYS;  // keys per tile
+  static constexpr int BN = 8 * NW;            // keys per tile: one 16-key V step per group-B wave
   static constexpr int KT = BN / 32;           // 32-key tiles of S^T
   static constexpr int NU = BN / 16;           // 16-key steps of O^T
-  static constexpr int KP = D + PKV_PREFILL_KPAD;  // LDS row pitch of K (elements)
-  static constexpr int VP = D + PKV_PREFILL_VPAD;  // LDS row pitch of V (elements)
   static constexpr int KS = D / 16;            // k-steps of S^T
   static constexpr int DT = D / 32;            // 32-row tiles of O^T
-  static constexpr int CPR = D / 8;            // 16-byte chunks per token row
-  static constexpr int WK = BN / (NW / 2);     // keys per wave per tile
-  static constexpr int KPW = 64 / CPR;         // keys per wave per 16-byte chunk
-  static constexpr int CH = WK / KPW;          // chunks per thread of its group's tensor
-  static constexpr int KBUF = BN * KP;         // elements of one K buffer
-  static constexpr int VBUF = BN * VP;         // elements of one V buffer
-  static constexpr int LDS_BYTES = 2 * (KBUF + VBUF) * 2;
-  static_assert(NW % 2 == 0 && NW >= 2, "two wave groups");
-  static_assert(CH >= 1 && WK % KPW == 0 && BN % (NW / 2) == 0, "tile chunks must split evenly");
+  static constexpr int NB = 4;                 // ring depth (tiles) per tensor
+  static constexpr int TILE = BN * D * 2;      // bytes of one K (or V) tile
+  static constexpr int LDS_BYTES = 2 * NB * TILE;
+  // each wave moves DT 1 KB blocks per tile: K blocks gw*DT .. +DT-1 (one
+  // 32-key row tile), or V step u = gw for all DT column tiles
+  static_assert(NW % 2 == 0 && NU == G && KS % DT == 0, "staging split");
   static_assert(QB >= 1, "more heads than waves");
 };
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource (SGPR quad) over [p, p + bytes): stride 0, raw offsets,
+// lanes whose offset falls past `bytes` read zeros.
+__device__ __forceinline__ i32x4 sgpr_rsrc(const void* p, int bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(p);
+  return i32x4{(int)(uint32_t)b, (int)((b >> 32) & 0xffffu), bytes, 0x00020000};
+}
+
+// 16 bytes per lane from rs + voff + soff into LDS at m0 + 16*lane.  Issued
+// as inline assembly so that the compiler neither counts it nor guards the
+// kernel's LDS reads against it: every wait for these loads is explicit.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16(i32x4 rs, uint32_t m0, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(m0), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// barrier that first waits for LDS reads and for all but VM of this wave's
+// memory loads (LDS-destination loads included); no cache maintenance
+template <int VM>
+__device__ __forceinline__ void phase_barrier() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | 0x70 | ((VM >> 4) << 14));  // vmcnt(VM) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int D, int PS, int HW>
 __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(PrefillArgs a, int nqb) {
   using C = PrefillCfg<D, HW>;
-  // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]
+  // [K ring: NB tiles][V ring: NB tiles]
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   // grid: x = (KV head, head group), y = sequence, z = query block counted
@@ -150,6 +177,10 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
     }
   }
 
+  // Q has landed before any tile request is issued (those are not counted
+  // by the compiler's own waits)
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+
   // keys any row of this workgroup may see
   const int wg_last = min(q0 + C::BM, Lq) - 1;
   const int pmin = shift + q0, pmax = shift + wg_last;
@@ -170,133 +201,170 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   float l_run = 0.f;        // this lane's partial sum of p
 
   // ---- staging: group A fetches K tiles, group B V tiles ----
-  // Wave gw of a group fetches the WK keys t*BN + WK*gw .. +WK-1 of tile t,
-  // which lie in one page: one table entry and one scalar buffer resource
-  // per wave and tile, bounded to the page's keys below kend (the hardware
-  // returns zeros past the bound, so keys past kend and unusable pages read
-  // zeros).  Lane chunk `it` is key WK*gw + KPW*it + lane/CPR, 16-byte
-  // column chunk lane%CPR; the chunks of one lane sit 1 KB apart in the page
-  // (immediate offsets).
+  // Wave gw's rows of tile s start at key s*BN + w0 (32 rows for K, 16 for
+  // V) and are fetched as NR page runs of RR rows (two 16-row runs for K
+  // when pages hold 16 keys).  Each run is one scalar buffer resource
+  // bounded to its keys below kend: the hardware writes zeros for lanes past
+  // the bound, so keys past kend and unusable pages read as zeros.
+  constexpr int NR = PS >= 32 ? 1 : 2;           // page runs per wave and tile
+  constexpr int NDMA = C::DT * NR;               // LDS-destination loads per wave and tile
+  constexpr int VM_AHEAD = 2 * NDMA;             // loads of the two tiles requested after
   const uint16_t* src = (grp_b ? a.v_pool : a.k_pool) + (int64_t)hk * a.head_stride;
-  uint16_t* const kbuf = smem;
-  uint16_t* const vbuf = smem + 2 * C::KBUF;
-  const int dbuf = grp_b ? C::VBUF : C::KBUF;   // elements per buffer of own tensor
-  const int dpitch = grp_b ? C::VP : C::KP;     // row pitch of own tensor
-  const auto bt_rsrc = make_rsrc(a.block_tables + (int64_t)j * a.max_pages, a.max_pages * 4);
-  const int lkey = lane / C::CPR;
-  const int lcol = (lane % C::CPR) * 16;  // byte offset within the row
-  static_assert(PS % C::WK == 0, "a wave's keys of a tile must share a page");
-  // this lane's first element in its tensor's LDS buffer 0
-  uint16_t* const dst = (grp_b ? vbuf : kbuf) + (C::WK * gw + lkey) * dpitch + lcol / 2;
-  // Two staging sets alternate: tile s uses set (s - t_first) & 1.  A set's
-  // loads are consumed two tiles after they are issued, and its table
-  // entry two tiles before its loads, so no wait ever covers the loads of
-  // the tile in between (memory loads complete in issue order).
-  int pg[2];              // block-table entry (same in every lane)
-  uint4 stage[2][C::CH];  // K or V rows on their way to LDS
-  auto bt_load = [&](int t, int& pgs) {
-    const int kb = t * C::BN + C::WK * gw;
-    pgs = __builtin_amdgcn_raw_buffer_load_b32(bt_rsrc, kb < kend ? (kb / PS) * 4 : -1, 0, 0);
-  };
-  auto load_tile = [&](int t, uint4 (&stg)[C::CH], int pgs) {
-    const int kb = t * C::BN + C::WK * gw;
-    const int phys = __builtin_amdgcn_readfirstlane(pgs);
-    const int page0 = kb - kb % PS;
-    const bool ok = kb < kend && phys >= 0 && phys < a.num_pages;
-    const int valid = ok ? min(kend - page0, PS) : 0;  // keys of the page below kend
-    const auto r = make_rsrc(src + (ok ? (int64_t)phys * PS * D : 0), valid * D * 2);
-    const int off = ((kb - page0) + lkey) * (D * 2) + lcol;
-#pragma unroll
-    for (int it = 0; it < C::CH; ++it) stg[it] = buffer_load16(r, off + it * C::KPW * D * 2);
-  };
-  auto store_tile = [&](int t, const uint4 (&stg)[C::CH]) {
-    uint16_t* d = dst + (t & 1) * dbuf;
-#pragma unroll
-    for (int it = 0; it < C::CH; ++it) *reinterpret_cast<uint4*>(d + it * C::KPW * dpitch) = stg[it];
-  };
+  const int w0 = grp_b ? 16 * gw : 32 * ((gw * C::DT) / C::KS);
+  const int rr_all = grp_b ? 16 : 32;            // rows of this wave
+  const int RR = NR == 2 ? 16 : rr_all;          // rows per run
+  const int roff = (NR == 2 && !grp_b) ? 16 : 0; // first row of run 1
+  const int sstride = grp_b ? 64 : 32;           // global bytes between the wave's blocks
+  // lane's row (relative to its run) and 16-byte chunk within the row
+  int lrow, lchunk;
+  if (!grp_b) {  // K block (kt, ks): lane l holds row l%32, d-chunk 2ks + l/32
+    lrow = lane & 31;
+    lchunk = 2 * ((gw * C::DT) % C::KS) + (lane >> 5);
+  } else {       // V: lane l covers transposed-read lanes 2(l%32), +1 of half l/32
+    const int s5 = lane & 31, g = s5 >> 3;
+    lrow = 8 * (lane >> 5) + 4 * (g >> 1) + ((s5 >> 1) & 3);
+    lchunk = 2 * (g & 1) + (s5 & 1);
+  }
+  // with two runs, lanes 16-31 and 48-63 take run 1 (K rows 16-31; for V
+  // both runs are the same page run, so both groups issue the same loads)
+  const bool run1 = NR == 2 && (lane & 16) != 0;
+  const int loff = ((run1 && !grp_b ? lrow - 16 : lrow) * D + 8 * lchunk) * 2;  // bytes from the run base
+  // block-table row, read through the scalar cache (it is never written here)
+  const __attribute__((address_space(4))) int32_t* bt_row =
+      (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)j * a.max_pages);
+  // LDS rings: K tiles at [0, NB*TILE), V tiles at [NB*TILE, 2*NB*TILE)
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)smem;
+  const uint32_t ring = lds0 + (grp_b ? C::NB * C::TILE : 0) + gw * C::DT * 1024;
 
-  // transposed-read geometry (ds_read_b64_tr_b16, 16-lane groups): source
-  // lane 4r+a of a group reads V[key0 + r][d0 + 4a .. +3]; output lane i of
-  // the group then holds V[key0 .. key0+3][d0 + i].
-  const int grp = lane >> 4, gi = lane & 15;
-  const int tr_key = 4 * (grp >> 1) + (gi >> 2);       // + 16u (+8 for the second half)
-  const int tr_d = 16 * (grp & 1) + 4 * (gi & 3);      // + 32dt
-
-  // S^T of key tile t: the K operands of a 32-key tile are all read before
-  // its MFMAs start
-  auto qk = [&](f32x16 (&st)[C::KT], int t) {
-    const uint16_t* kl = kbuf + (t & 1) * C::KBUF;
+  // block-table entries of tile s (scalar loads; a clamped index keeps the
+  // read inside the row, entries past kend are not used)
+  auto bt_load = [&](int s, int (&pgs)[NR]) {
 #pragma unroll
-    for (int kt = 0; kt < C::KT; ++kt) {
-      const uint16_t* krow = kl + (32 * kt + col) * C::KP + 8 * hh;
-      bf16x8 kop[C::KS];
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-        kop[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(krow + 16 * ks));
-      f32x16 s = {};
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) s = mfma32(kop[ks], qop[ks], s);
-      st[kt] = s;
+    for (int r = 0; r < NR; ++r) {
+      const int kb = s * C::BN + w0 + roff * r;
+      pgs[r] = bt_row[min(kb / PS, a.max_pages - 1)];
     }
   };
-  // O^T += V(t)^T P^T, 16 keys per step
-  auto pv = [&](const bf16x8 (&pop)[C::NU], int t) {
-    const uint16_t* vl = vbuf + (t & 1) * C::VBUF;
+  // request this wave's blocks of tile s into ring slot s % NB
+  auto dma_tile = [&](int s, const int (&pgs)[NR]) {
+    i32x4 rs[NR];
 #pragma unroll
-    for (int u = 0; u < C::NU; ++u) {
-      bf16x8 vop[C::DT];
+    for (int r = 0; r < NR; ++r) {
+      const int kb = s * C::BN + w0 + roff * r;
+      const int phys = pgs[r];
+      const bool ok = kb < kend && phys >= 0 && phys < a.num_pages;
+      const int valid = ok ? min(kend - kb, RR) : 0;
+      rs[r] = sgpr_rsrc(src + (ok ? ((int64_t)phys * PS + kb % PS) * D : 0), valid * D * 2);
+    }
+    const uint32_t m0 = ring + (s & (C::NB - 1)) * C::TILE;
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-        const uint16_t* v0 = vl + (16 * u + tr_key) * C::VP + 32 * dt + tr_d;
+    for (int i = 0; i < C::DT; ++i) {
+      if constexpr (NR == 1) {
+        load_lds16(rs[0], m0 + i * 1024, loff, sstride * i);
+      } else {
+        // both halves issue on every wave (exec-masked), so the load count
+        // is the same for all waves
+        if (run1) load_lds16(rs[1], m0 + i * 1024, loff, sstride * i);
+        else      load_lds16(rs[0], m0 + i * 1024, loff, sstride * i);
+      }
+    }
+  };
+
+  // Matrix phase M(t): O^T += V(t)^T P(t)^T, then S(t+1)^T = K(t+1) Q^T, as
+  // one stream of MFMA jobs whose LDS operands are requested LA jobs ahead
+  // (the scheduling barriers keep that order).  A V job (u, dt) takes the
+  // two transposed reads of blocks (u, dt, half): lane l's 8 bytes at 8*l,
+  // after which lane l of 16-lane group g holds
+  // V[16u + 8half + 4(g/2) .. +3][32dt + 16(g%2) + l%16].  A K job (kt, ks)
+  // takes block (kt, ks), lane l's 16 bytes at 16*l: the A operand
+  // K[32kt + l%32][16ks + 8(l/32) .. +7].  K jobs alternate between the two
+  // 32-key halves so that consecutive MFMAs do not depend on each other.
+  auto mphase = [&](const bf16x8 (&pop)[C::NU], int t, f32x16 (&st)[C::KT]) {
+    constexpr int NPV = C::NU * C::DT, NJ = NPV + C::KT * C::KS, LA = PKV_PREFILL_LOOKAHEAD;
+    const char* vl = (const char*)smem + (C::NB + (t & (C::NB - 1))) * C::TILE + 8 * lane;
+    const char* kl = (const char*)smem + ((t + 1) & (C::NB - 1)) * C::TILE + 16 * lane;
+    bf16x8 opnd[LA + 1];
+    f32x16 s[C::KT];
+    auto fetch = [&](auto J) {
+      constexpr int jj = decltype(J)::value;
+      if constexpr (jj < NPV) {
+        constexpr int u = jj / C::DT, dt = jj % C::DT;
+        const char* v0 = vl + (u * C::DT + dt) * 1024;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)v0);
+            (lds_s16x4*)(__attribute__((address_space(3))) char*)v0);
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4*)(__attribute__((address_space(3))) uint16_t*)(v0 + 8 * C::VP));
+            (lds_s16x4*)(__attribute__((address_space(3))) char*)(v0 + 512));
         const uint2 l2 = __builtin_bit_cast(uint2, lo);
         const uint2 h2 = __builtin_bit_cast(uint2, hi);
-        vop[dt] = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
+        opnd[jj % (LA + 1)] = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
+      } else {
+        constexpr int q = jj - NPV, kt = q % C::KT, ks = q / C::KT;
+        opnd[jj % (LA + 1)] = as_bf16x8(*reinterpret_cast<const uint4*>(kl + (kt * C::KS + ks) * 1024));
       }
+    };
+    static_for<0, LA>(fetch);
+    static_for<0, NJ>([&](auto J) {
+      constexpr int jj = decltype(J)::value;
+      if constexpr (jj + LA < NJ) fetch(std::integral_constant<int, jj + LA>{});
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (jj < NPV) {
+        constexpr int u = jj / C::DT, dt = jj % C::DT;
+        acc[dt] = mfma32(opnd[jj % (LA + 1)], pop[u], acc[dt]);
+      } else {
+        constexpr int q = jj - NPV, kt = q % C::KT, ks = q / C::KT;
+        s[kt] = mfma32(opnd[jj % (LA + 1)], qop[ks], ks == 0 ? f32x16{} : s[kt]);
+      }
+    });
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) acc[dt] = mfma32(vop[dt], pop[u], acc[dt]);
+    for (int kt = 0; kt < C::KT; ++kt) st[kt] = s[kt];
+  };
+  // S^T of key tile t_first (prologue), same block layout
+  auto qk_first = [&](f32x16 (&st)[C::KT], int t) {
+    const char* kl = (const char*)smem + (t & (C::NB - 1)) * C::TILE + 16 * lane;
+#pragma unroll
+    for (int kt = 0; kt < C::KT; ++kt) {
+      f32x16 sacc = {};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+        sacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(kl + (kt * C::KS + ks) * 1024)),
+                      qop[ks], sacc);
+      st[kt] = sacc;
     }
   };
 
   // Every wave executes the same number of barriers: group B one extra
-  // before its first phase, group A one extra after its last.
+  // before its first phase, group A one extra after its last.  Tile loads
+  // are issued unconditionally (tiles past the end read zeros), so every
+  // wave issues the same sequence and each wait count below is exact.
   if (kend > kstart) {
     const int t_first = kstart / C::BN, t_last = (kend - 1) / C::BN;
-    // prologue: tile t_first of both tensors in LDS; tiles t_first+1 and
-    // t_first+2 in flight; table entries of t_first+3 and t_first+4 too.
-    // Loads are issued unconditionally (tiles past the end read zeros from
-    // empty buffer ranges), so the number of loads in flight is the same on
-    // every path and each wait covers exactly the loads it needs.
-    bt_load(t_first, pg[0]);
-    load_tile(t_first, stage[0], pg[0]);
-    store_tile(t_first, stage[0]);
-    bt_load(t_first + 1, pg[1]);
-    bt_load(t_first + 2, pg[0]);
-    // same issue order as a pair of steady-state tile steps
-    load_tile(t_first + 1, stage[1], pg[1]);
-    bt_load(t_first + 3, pg[1]);
-    load_tile(t_first + 2, stage[0], pg[0]);
-    bt_load(t_first + 4, pg[0]);
-    __syncthreads();
-    if (grp_b) __syncthreads();
+    int pg[2][NR];  // table entries of tile t+3 (slot (t+3-t_first)&1) and t+4
+    {
+      int p0[NR], p1[NR], p2[NR];
+      bt_load(t_first, p0);
+      bt_load(t_first + 1, p1);
+      bt_load(t_first + 2, p2);
+      bt_load(t_first + 3, pg[1]);
+      dma_tile(t_first, p0);
+      dma_tile(t_first + 1, p1);
+      dma_tile(t_first + 2, p2);
+    }
+    phase_barrier<VM_AHEAD>();         // tile t_first of both tensors in LDS
+    if (grp_b) phase_barrier<63>();
 
     f32x16 st[C::KT];
-    qk(st, t_first);
-    __syncthreads();
+    qk_first(st, t_first);
+    phase_barrier<63>();
 
-    // one key tile: X is the staging set of tile t+1 (and t+3, t+5)
+    // one key tile; X is the table slot of tile t+3, the other slot takes t+4
     auto tile_step = [&](int t, auto X) {
       constexpr int x = decltype(X)::value;
       // ======== V(t): staging and softmax of S(t) ========
 #if PKV_PREFILL_SETPRIO
       __builtin_amdgcn_s_setprio(0);
 #endif
-      if (t + 1 <= t_last) store_tile(t + 1, stage[x]);  // fetched two tiles ago
-      load_tile(t + 3, stage[x], pg[x]);
-      bt_load(t + 5, pg[x]);
+      dma_tile(t + 3, pg[x]);
+      bt_load(t + 4, pg[x ^ 1]);
       const int k0 = t * C::BN;
       // register r of key tile kt is key k0 + 32kt + 8(r/4) + 4hh + r%4
       const bool need_mask = (k0 + C::BN - 1 > wpmin) ||
@@ -352,15 +420,16 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
         pop[u] = as_bf16x8(pp);
       }
       l_run += psum;
-      __syncthreads();
+      phase_barrier<VM_AHEAD>();       // this wave's part of tile t+1 has landed
 
       // ======== M(t): O += V(t) P(t), S(t+1) = K(t+1) Q^T ========
 #if PKV_PREFILL_SETPRIO
       __builtin_amdgcn_s_setprio(1);
 #endif
-      pv(pop, t);
-      if (t + 1 <= t_last) qk(st, t + 1);
-      __syncthreads();
+      // (after the last tile the S result is unused: its ring slot holds
+      // zeros or an older tile, both finite)
+      mphase(pop, t, st);
+      phase_barrier<63>();
     };
     // pairs of steps with no branch between them, so the loads in flight at
     // the loop head are the same on every path
@@ -373,7 +442,9 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
 #if PKV_PREFILL_SETPRIO
     __builtin_amdgcn_s_setprio(0);
 #endif
-    if (!grp_b) __syncthreads();
+    if (!grp_b) phase_barrier<63>();
+    // drain the loads of tiles past the end before the workgroup exits
+    __builtin_amdgcn_s_waitcnt(0x0070);
   }
 
   // ---- normalise and write: lane holds d = 32dt + 8(r/4) + 4hh + r%4 ----
