@@ -1,0 +1,66 @@
+// Device helpers shared by the prefill kernels: lane-pair reductions, scalar
+// buffer resources, loads that land directly in LDS, and barriers with
+// explicit wait counts.
+#pragma once
+
+#include "common.h"
+
+namespace pkv {
+namespace prefill_detail {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// The running max is raised only when a tile's max exceeds it by more than
+// this many log2 units, so p <= 2^kRescaleSlack and rescales are rare.
+constexpr float kRescaleSlack = 8.0f;
+
+// max / sum of a value over lanes l and l^32 (v_permlane32_swap: no LDS trip)
+__device__ __forceinline__ float half_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Buffer resource (SGPR quad) over [p, p + bytes): stride 0, raw offsets,
+// lanes whose offset falls past `bytes` read zeros.
+__device__ __forceinline__ i32x4 sgpr_rsrc(const void* p, int bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(p);
+  return i32x4{(int)(uint32_t)b, (int)((b >> 32) & 0xffffu), bytes, 0x00020000};
+}
+
+// 16 bytes per lane from rs + voff + soff into LDS at m0 + 16*lane.  Issued
+// as inline assembly so that the compiler neither counts it nor guards the
+// kernel's LDS reads against it: every wait for these loads is explicit.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16(i32x4 rs, uint32_t m0, int voff, int soff) {
+  // the operands are wave-uniform; readfirstlane only tells the compiler so
+  const i32x4 r = {__builtin_amdgcn_readfirstlane(rs[0]), __builtin_amdgcn_readfirstlane(rs[1]),
+                   __builtin_amdgcn_readfirstlane(rs[2]), __builtin_amdgcn_readfirstlane(rs[3])};
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(r),
+                  "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// barrier that first waits for LDS reads and for all but VM of this wave's
+// memory loads (LDS-destination loads included); no cache maintenance
+template <int VM>
+__device__ __forceinline__ void phase_barrier() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | 0x70 | ((VM >> 4) << 14));  // vmcnt(VM) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+}  // namespace prefill_detail
+}  // namespace pkv

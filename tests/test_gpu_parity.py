@@ -381,6 +381,41 @@ def test_decode_equals_last_prefill_row_and_chunk_equals_full(P):
     assert np.max(np.abs(c - f)) < 2e-2
 
 
+# head_dim, group size (Hq/Hkv, including one that is not a power of two),
+# page size and window: every prefill kernel instantiation family, with
+# ragged prompts around the 32/64-row and 64-key tile edges and chunks after
+# a cached prefix
+PREFILL_SHAPES = [  # name, Hq, Hkv, D, page, window
+    ("d64_g4_p16", 8, 2, 64, 16, 0),
+    ("d64_g1_p32", 4, 4, 64, 32, 0),
+    ("d64_g8_p32_win", 16, 2, 64, 32, 100),
+    ("d128_g3_p32", 6, 2, 128, 32, 0),
+    ("d128_g8_p16", 16, 2, 128, 16, 0),
+    ("d128_g2_p16_win", 4, 2, 128, 16, 77),
+    ("d256_g2_p16", 4, 2, 256, 16, 0),
+]
+
+
+@pytest.mark.parametrize("shape", PREFILL_SHAPES, ids=[s[0] for s in PREFILL_SHAPES])
+def test_prefill_shapes(P, shape):
+    name, hq, hkv, d, ps, win = shape
+    cfg = W.Config(name, 20261202, hq, hkv, d, ps, window=win, decode_ctx=("fixed", ()),
+                   prefill_new=("fixed", (1, 31, 63, 64, 65, 129, 0, 200)),
+                   chunk=("uniform", 2, 100, 700, 70))
+    wl = W.build(cfg)
+    g = GpuPools(wl)
+    g.write("prefix")
+    g.write("new")
+    _, qp = wl.queries(0)
+    say(f"[prefill] {name}: N={wl.n_prefill} Tq={qp.shape[0]}")
+    got = run_prefill(P, g, qp)
+    o = OraclePools(wl)
+    seqs = wl.prefill_ids()
+    ref = oracle.prefill_varlen(qp, o.k, o.v, wl.block_tables[seqs], wl.prefill_cu_q(),
+                                wl.prefill_cu_k(), wl.page_size, wl.scale, wl.window)
+    check_close(got, ref, f"{name} prefill")
+
+
 def test_prefill_deterministic(P):
     g = state("mixed_step")
     _, qp = g.wl.queries(0)
