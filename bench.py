@@ -3,17 +3,20 @@
 
 A step is one pass of the whole hot path over one batch:
 slot addressing -> append of the step's new K/V rows -> decode attention
-(split-K partials + combine) and/or varlen prefill, per layer.  The default
-workload is the bandwidth-bound decode: 256 sequences with context
-U[1024, 8192], 32 query / 8 KV heads, head_dim 128, page 32, random page
-order, split-K on.  Inputs (pools, tables, queries, new rows) are resident
+(stream-K partition of the batch's pages + merge of the cut segments, or
+split-K partials + combine with --num-splits) and/or varlen prefill, per
+layer.  The default workload is the bandwidth-bound decode: 256 sequences
+with context U[1024, 8192], 32 query / 8 KV heads, head_dim 128, page 32,
+random page order.  Inputs (pools, tables, queries, new rows) are resident
 in HBM before the timed region starts.
 
 Prints ONE JSON line.  ``value`` is the step's algorithmic HBM traffic
 divided by the measured step time (GB/s); ``roofline`` reports the
-dominant kernel (the split-K decode kernel) against the 8 TB/s HBM peak,
-timed with HIP events on the stream it runs on.  ``cpu_baseline`` times the
-CPU oracle on a bounded sample of the same workload.
+dominant kernel (the decode kernel; the prefill kernel for the prefill-only
+workload) against its peak, timed with HIP events on the stream it runs on.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload.  Steps whose K/V fit in the last-level caches are timed after a
+cache scrub (see --scrub).
 """
 from __future__ import annotations
 
@@ -155,7 +158,7 @@ class Step:
             self.S, self.pps, self.nw = 0, 0, 0
             if num_splits == 0 and self.B <= 2048:
                 # stream-K: persistent waves over the flattened page list + merge
-                self.nw = P.decode_stream_waves(self.B, wl.num_kv_heads, d, wl.page_size,
+                self.nw = P.decode_stream_waves(self.B, hq, wl.num_kv_heads, d, wl.page_size,
                                                 self.max_len, wl.window)
                 need = P.lib().pkv_decode_stream_workspace_bytes(self.nw, hq, wl.num_kv_heads, d)
                 self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
@@ -181,8 +184,9 @@ class Step:
             qd, qp = wl.queries(layer)
             self.q.append((bits(qd), bits(qp)))
 
-    def run(self, ev=None):
-        """One step.  ``ev`` = (before, after) events bracketing the layer-0 decode kernel."""
+    def run(self, ev=None, pev=None):
+        """One step.  ``ev`` / ``pev`` = (before, after) events bracketing the layer-0 decode
+        kernel / prefill kernel."""
         P, wl = self.P, self.wl
         P.slot_mapping(self.bt, self.cu_new_q, self.cu_new_k, page_size=wl.page_size,
                        num_pages=wl.num_pages, total_tokens=self.T, out=self.slots)
@@ -215,15 +219,42 @@ class Step:
                     if ev is not None and layer == 0:
                         ev[1].record()
             if self.N:
+                if pev is not None and layer == 0:
+                    pev[0].record()
                 P.prefill_varlen(qp, self.k_pool, self.v_pool, self.bt_pre, self.cu_q, self.cu_k,
                                  self.max_q, self.max_k, page_size=wl.page_size, scale=wl.scale,
                                  window=wl.window, out=self.out_pre)
+                if pev is not None and layer == 0:
+                    pev[1].record()
 
     def run_prefill(self):
         wl = self.wl
         self.P.prefill_varlen(self.q[0][1], self.k_pool, self.v_pool, self.bt_pre, self.cu_q,
                               self.cu_k, self.max_q, self.max_k, page_size=wl.page_size,
                               scale=wl.scale, window=wl.window, out=self.out_pre)
+
+
+SCRUB_BYTES = 1 << 30
+
+
+def copy_ceiling(torch, nbytes=1 << 31, reps=5):
+    """Read+write GB/s of a plain 2 GiB device copy: the box's practical HBM
+    ceiling, context for the roofline (whose peak stays at 8 TB/s)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 2 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(gbs, 1)
 
 
 def step_bytes(wl) -> int:
@@ -369,6 +400,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the long-prefill MFMA measurement")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--scrub", choices=["auto", "on", "off"], default="auto",
+                    help="1 GiB cache scrub before each timed step (auto: when the step's "
+                         "algorithmic bytes are under 1 GiB)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -415,16 +449,32 @@ def main():
         st.run()
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # A step whose K/V fit in the last-level caches (256 MB Infinity Cache +
+    # L2) is timed after a 1 GiB scratch write, outside its events, so that
+    # its K/V come from HBM as in a real model step; larger steps need none.
+    scrub = args.scrub == "on" or (args.scrub == "auto" and step_bytes(wl) < SCRUB_BYTES)
+    scratch = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda") if scrub else None
+
+    def evpair():
+        return (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    evs = [evpair() for _ in range(args.steps)]      # decode kernel
+    pevs = [evpair() for _ in range(args.steps)]     # prefill kernel
+    sevs = [evpair() for _ in range(args.steps)]     # whole step
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        st.run(evs[i] if st.B else None)
+        if scrub:
+            scratch.fill_(i & 0xff)
+        sevs[i][0].record()
+        st.run(evs[i] if st.B else None, pevs[i] if st.N else None)
+        sevs[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = wall / args.steps * 1e3
-    _log(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step")
+    step_ms = np.array([a.elapsed_time(b) for a, b in sevs])
+    # with scrubbing the scratch writes sit between the steps: time the steps by their events
+    ms_step = float(step_ms.mean()) if scrub else wall / args.steps * 1e3
+    _log(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step"
+         f"{' (cache scrubbed before each step)' if scrub else ''}")
 
     sb = step_bytes(wl)
     value = sb / (ms_step * 1e-3) / 1e9
@@ -444,6 +494,9 @@ def main():
         "config": {"workload": f"{args.config}: {DESCRIPTIONS[args.config]}",
                    "seed": wl.seed, "step_bytes": sb},
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+        "median_ms_per_step": round(float(np.median(step_ms)), 5),
+        "min_ms_per_step": round(float(step_ms.min()), 5),
+        "cache_scrub": bool(scrub),
     }
     if st.B:
         kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
@@ -463,22 +516,35 @@ def main():
             "avg_kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": kb,
             "kernel_source_sha256_16": src_hash,
         }
-    if st.N and not st.B:
-        fl = prefill_flops(wl) * wl.num_layers
-        tf = fl / (ms_step * 1e-3) / 1e12
-        out["roofline"] = {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tf, 3),
-                           "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    if st.N:
+        pk_ms = float(np.mean([a.elapsed_time(b) for a, b in pevs]))
+        fl = prefill_flops(wl)
+        tf = fl / (pk_ms * 1e-3) / 1e12
+        pre = {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tf, 3),
+               "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+               "traffic": None, "avg_kernel_ms": round(pk_ms, 5), "algorithmic_flops_per_launch": fl}
+        if st.B:
+            # the step's prefill is a few GFLOP: launch-bound, reported as it is
+            out["step_prefill"] = dict(pre, note="launch-bound at this size")
+        else:
+            out["roofline"] = pre
     del st
     torch.cuda.empty_cache()
 
     if not args.no_prefill and args.config != "long_prefill":
         _log("[bench] long-prefill MFMA measurement")
         out["prefill"] = prefill_measure(torch, P)
+    if scratch is not None:
+        del scratch
+        torch.cuda.empty_cache()
+    out["hbm_copy_ceiling_gbs"] = copy_ceiling(torch)
     if not args.no_cpu_baseline:
         _log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, 64)
+    cus, khz = P.device_info()
     out["gpu"] = torch.cuda.get_device_name(0)
+    out["device"] = {"compute_units": cus, "max_sclk_mhz": khz // 1000,
+                     "arch": torch.cuda.get_device_properties(0).gcnArchName}
     out["host"] = platform.node()
     print(json.dumps(out), flush=True)
 

@@ -66,6 +66,15 @@ enum {
 const char* pkv_status_string(pkv_status s);
 
 /*
+ * Compute units and peak shader clock (kHz) of the current HIP device, as
+ * the runtime reports them (what the MFMA and bandwidth peaks are quoted
+ * against).  Both pointers are host memory written on success.  Returns
+ * PKV_ERR_NULL_ARG for a NULL pointer, PKV_ERR_HIP if the runtime query
+ * fails.
+ */
+pkv_status pkv_device_info(int32_t* compute_units, int32_t* max_clock_khz);
+
+/*
  * Slot addressing: the physical pool row of every new token.
  *
  * Sequence j contributes Lq_j = cu_seq_lens_q[j+1]-cu_seq_lens_q[j] new
@@ -201,7 +210,10 @@ pkv_status pkv_decode_combine(const float* part_m, const float* part_l, const fl
  * out; one cut by range boundaries leaves a partial per piece in the
  * workspace for pkv_decode_stream_merge.  Rows with seq_lens[b] == 0 are
  * written as zeros.  The result depends on num_waves only through rounding
- * order and is deterministic for a given num_waves.
+ * order and is deterministic for a given num_waves.  With head_dim >= 128
+ * and an even query-head group larger than 4, each KV head counts as two
+ * units per page (each half of the group is a unit of its own, reading the
+ * page again from L2), which keeps one wave's accumulators in registers.
  *
  *   num_waves   >= 1; pkv_decode_stream_waves gives the count pkv_decode
  *               uses (a few waves per compute unit of the current device)
@@ -211,9 +223,9 @@ pkv_status pkv_decode_combine(const float* part_m, const float* part_l, const fl
  *   num_seqs    <= 2048 (the row lengths are scanned in LDS)
  * Other arguments as for pkv_decode.
  */
-pkv_status pkv_decode_stream_waves(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                                   int32_t page_size, int32_t max_seq_len, int32_t window,
-                                   int32_t* num_waves);
+pkv_status pkv_decode_stream_waves(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t page_size, int32_t max_seq_len,
+                                   int32_t window, int32_t* num_waves);
 size_t pkv_decode_stream_workspace_bytes(int32_t num_waves, int32_t num_q_heads,
                                          int32_t num_kv_heads, int32_t head_dim);
 pkv_status pkv_decode_stream(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,

@@ -41,6 +41,7 @@ _LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 EXPORTS = (
     "pkv_status_string",
+    "pkv_device_info",
     "pkv_slot_mapping",
     "pkv_append",
     "pkv_decode_plan",
@@ -71,6 +72,7 @@ _F = ctypes.c_float
 _SZ = ctypes.c_size_t
 _SIGS = {
     "pkv_status_string": ([_I32], ctypes.c_char_p),
+    "pkv_device_info": ([_P, _P], _I32),
     "pkv_slot_mapping": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "pkv_append": ([_P, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P], _I32),
     "pkv_decode_plan": ([_I32, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
@@ -80,7 +82,7 @@ _SIGS = {
     "pkv_decode_split": ([_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                           _F, _I32, _I32, _I32, _P, _P, _P, _P], _I32),
     "pkv_decode_combine": ([_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P], _I32),
-    "pkv_decode_stream_waves": ([_I32, _I32, _I32, _I32, _I32, _I32, _P], _I32),
+    "pkv_decode_stream_waves": ([_I32, _I32, _I32, _I32, _I32, _I32, _I32, _P], _I32),
     "pkv_decode_stream_workspace_bytes": ([_I32, _I32, _I32, _I32], _SZ),
     "pkv_decode_stream": ([_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _F,
                            _I32, _I32, _P, _SZ, _P, _P], _I32),
@@ -188,6 +190,13 @@ def append(k_new, v_new, slot_mapping, k_pool, v_pool, stream=None):
         k_pool.shape[1], _stream(stream)))
 
 
+def device_info():
+    """``(compute_units, max_clock_khz)`` of the current device (``pkv_device_info``)."""
+    cus, khz = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("pkv_device_info", lib().pkv_device_info(ctypes.byref(cus), ctypes.byref(khz)))
+    return cus.value, khz.value
+
+
 def decode_plan(num_seqs, num_kv_heads, page_size, max_seq_len, window=0, num_splits=0):
     """``(num_splits, pages_per_split)`` that ``decode`` uses (``pkv_decode_plan``)."""
     s, p = ctypes.c_int32(0), ctypes.c_int32(0)
@@ -267,11 +276,13 @@ def decode_combine(m, l, acc, out=None, stream=None):
     return out
 
 
-def decode_stream_waves(num_seqs, num_kv_heads, head_dim, page_size, max_seq_len, window=0):
+def decode_stream_waves(num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, max_seq_len,
+                        window=0):
     """Number of persistent waves ``decode`` uses for stream-K (``pkv_decode_stream_waves``)."""
     n = ctypes.c_int32(0)
     _check("pkv_decode_stream_waves", lib().pkv_decode_stream_waves(
-        num_seqs, num_kv_heads, head_dim, page_size, max_seq_len, window, ctypes.byref(n)))
+        num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, max_seq_len, window,
+        ctypes.byref(n)))
     return n.value
 
 

@@ -59,6 +59,16 @@ int device_cus() {
   return cus;
 }
 
+// Stream-K works on virtual KV heads: a group of more than four query heads
+// with head_dim >= 128 is split in two halves that each see every page of
+// their KV head (the second read of a page hits L2), so one wave's
+// accumulators and PV work stay within its register budget.  Query and
+// output addressing is unchanged (virtual head v, half-group g' covers query
+// heads v*g' ..); only the pool addressing maps v back to KV head v >> 1.
+int stream_kv_shift(int num_q_heads, int num_kv_heads, int head_dim) {
+  const int g = num_q_heads / num_kv_heads;
+  return (head_dim >= 128 && g > 4 && g % 2 == 0) ? 1 : 0;
+}
 size_t stream_part_bytes(int num_waves, int group, int head_dim) {
   const size_t b = (size_t)2 * num_waves * group * (head_dim + 2) * sizeof(float);
   return (b + 255) & ~(size_t)255;
@@ -78,6 +88,18 @@ const char* pkv_status_string(pkv_status s) {
     case PKV_ERR_HIP: return "HIP error";
     default: return "unknown status";
   }
+}
+
+pkv_status pkv_device_info(int32_t* compute_units, int32_t* max_clock_khz) {
+  if (compute_units == nullptr || max_clock_khz == nullptr) return PKV_ERR_NULL_ARG;
+  int dev = 0, cus = 0, khz = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeClockRate, dev);
+  if (e != hipSuccess) return PKV_ERR_HIP;
+  *compute_units = cus;
+  *max_clock_khz = khz;
+  return PKV_OK;
 }
 
 pkv_status pkv_slot_mapping(const int32_t* block_tables, int32_t max_pages_per_seq,
@@ -138,8 +160,8 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
                                   int32_t window, int32_t num_splits_requested) {
   if (num_splits_requested == 0 && num_seqs > 0 && num_seqs <= kStreamMaxSeqs) {
     int32_t nw = 0;
-    if (pkv_decode_stream_waves(num_seqs, num_kv_heads, head_dim, page_size, max_seq_len, window,
-                                &nw) != PKV_OK)
+    if (pkv_decode_stream_waves(num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                                max_seq_len, window, &nw) != PKV_OK)
       return 0;
     return pkv_decode_stream_workspace_bytes(nw, num_q_heads, num_kv_heads, head_dim);
   }
@@ -188,6 +210,7 @@ static DecodeArgs decode_args(const uint16_t* q, const uint16_t* k_pool, const u
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.group = num_q_heads / num_kv_heads;
+  a.kv_shift = 0;
   a.num_splits = splits;
   a.pages_per_split = pps;
   a.window = window;
@@ -246,8 +269,8 @@ pkv_status pkv_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t*
   if (num_splits < 0) return PKV_ERR_BAD_SHAPE;
   if (num_splits == 0 && num_seqs > 0 && num_seqs <= kStreamMaxSeqs) {
     int32_t nw = 0;
-    st = pkv_decode_stream_waves(num_seqs, num_kv_heads, head_dim, page_size, max_seq_len,
-                                 window, &nw);
+    st = pkv_decode_stream_waves(num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                                 max_seq_len, window, &nw);
     if (st != PKV_OK) return st;
     if (!out) return PKV_ERR_NULL_ARG;
     if (!workspace) return PKV_ERR_NULL_ARG;
@@ -289,12 +312,15 @@ pkv_status pkv_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t*
                                    head_dim, s, out, stream));
 }
 
-pkv_status pkv_decode_stream_waves(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                                   int32_t page_size, int32_t max_seq_len, int32_t window,
-                                   int32_t* num_waves) {
-  if (num_seqs < 0 || num_kv_heads <= 0 || max_seq_len < 0) return PKV_ERR_BAD_SHAPE;
+pkv_status pkv_decode_stream_waves(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t page_size, int32_t max_seq_len,
+                                   int32_t window, int32_t* num_waves) {
+  if (num_seqs < 0 || max_seq_len < 0) return PKV_ERR_BAD_SHAPE;
+  const pkv_status hs = check_heads(num_q_heads, num_kv_heads);
+  if (hs != PKV_OK) return hs;
   if (!supported_dim(head_dim) || !supported_ps(page_size)) return PKV_ERR_UNSUPPORTED;
-  const int64_t units = (int64_t)num_seqs * num_kv_heads * key_pages(page_size, max_seq_len, window);
+  const int64_t heads = (int64_t)num_kv_heads << stream_kv_shift(num_q_heads, num_kv_heads, head_dim);
+  const int64_t units = (int64_t)num_seqs * heads * key_pages(page_size, max_seq_len, window);
   const int per_simd = head_dim == 256 ? 1 : kStreamWavesPerSimd;
   int64_t nw = (int64_t)device_cus() * 4 * per_simd;
   const int64_t want = (units + kStreamMinUnitsPerWave - 1) / kStreamMinUnitsPerWave;
@@ -310,6 +336,13 @@ size_t pkv_decode_stream_workspace_bytes(int32_t num_waves, int32_t num_q_heads,
     return 0;
   return stream_part_bytes(num_waves, num_q_heads / num_kv_heads, head_dim) +
          (size_t)2 * num_waves * kDescInts * sizeof(int);
+}
+
+// the virtual KV heads of stream-K (see stream_kv_shift)
+static void stream_heads(DecodeArgs& a, int head_dim) {
+  a.kv_shift = stream_kv_shift(a.num_q_heads, a.num_kv_heads, head_dim);
+  a.num_kv_heads <<= a.kv_shift;
+  a.group >>= a.kv_shift;
 }
 
 static void stream_layout(StreamArgs& sa, void* workspace, int num_waves, int group, int head_dim) {
@@ -343,7 +376,8 @@ pkv_status pkv_decode_stream(const uint16_t* q, const uint16_t* k_pool, const ui
                         1, 1);
   sa.base.out = out;
   sa.num_seqs = num_seqs;
-  stream_layout(sa, workspace, num_waves, num_q_heads / num_kv_heads, head_dim);
+  stream_heads(sa.base, head_dim);
+  stream_layout(sa, workspace, num_waves, sa.base.group, head_dim);
   return hip_status(launch_decode_stream(sa, head_dim, page_size, stream));
 }
 
@@ -363,6 +397,7 @@ pkv_status pkv_decode_stream_merge(const void* workspace, size_t workspace_bytes
   sa.base.num_q_heads = num_q_heads;
   sa.base.num_kv_heads = num_kv_heads;
   sa.base.group = num_q_heads / num_kv_heads;
+  stream_heads(sa.base, head_dim);
   stream_layout(sa, const_cast<void*>(workspace), num_waves, sa.base.group, head_dim);
   return hip_status(launch_stream_merge(sa, head_dim, stream));
 }

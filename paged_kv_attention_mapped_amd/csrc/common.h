@@ -106,7 +106,8 @@ struct DecodeArgs {
   int num_pages;
   int num_q_heads;
   int num_kv_heads;
-  int group;          // Hq / Hkv
+  int group;          // Hq / Hkv (per virtual KV head, see kv_shift)
+  int kv_shift;       // stream-K: KV head = virtual KV head >> kv_shift
   int num_splits;
   int pages_per_split;
   int window;

@@ -310,7 +310,8 @@ void decode_stream_kernel(StreamArgs sa) {
     si.u = u;
     si.part = part;
     si.tok0 = (ls.p0 + (u - ls.s0)) * PS + part * W::UT;
-    const int64_t hoff = (int64_t)ls.hk * a.head_stride + ((int64_t)phys * PS + part * W::UT) * D;
+    const int64_t hoff =
+        (int64_t)(ls.hk >> a.kv_shift) * a.head_stride + ((int64_t)phys * PS + part * W::UT) * D;
     wd.load(bf, a.k_pool + hoff, a.v_pool + hoff);
   };
 

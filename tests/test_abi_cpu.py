@@ -31,6 +31,7 @@ def declared():
 def test_header_declares_the_entry_points():
     assert declared() == sorted([
         "pkv_append", "pkv_decode", "pkv_decode_combine", "pkv_decode_plan", "pkv_decode_split",
+        "pkv_device_info",
         "pkv_decode_stream", "pkv_decode_stream_merge", "pkv_decode_stream_waves",
         "pkv_decode_stream_workspace_bytes", "pkv_decode_workspace_bytes", "pkv_prefill_varlen",
         "pkv_slot_mapping", "pkv_status_string"])
@@ -114,10 +115,19 @@ def test_decode_plan(P):
         assert need == (0 if s == 1 else B * hkv * 4 * s * 130 * 4)
     assert P.decode_plan(256, 8, 32, 8193) == (9, 32)
     # stream-K: waves bounded by the work and by the device (256 CUs assumed without a GPU)
-    assert P.decode_stream_waves(4, 1, 64, 16, 64) == 4
-    assert P.decode_stream_waves(256, 8, 128, 32, 8193) == 256 * 4 * 2
-    nw = P.decode_stream_waves(256, 8, 128, 32, 8193)
+    assert P.decode_stream_waves(4, 2, 1, 64, 16, 64) == 4
+    assert P.decode_stream_waves(256, 32, 8, 128, 32, 8193) == 256 * 4 * 2
+    nw = P.decode_stream_waves(256, 32, 8, 128, 32, 8193)
+    # a window of 512 keys touches at most 17 pages of 32: 64 rows x 1 KV head x 17 = 1088
+    # units; a group of 8 with head_dim >= 128 counts each KV head twice; >= 4 units per wave
+    assert P.decode_stream_waves(64, 8, 1, 256, 32, 4096, 512) == 2 * 1088 // 4
+    assert P.decode_stream_waves(64, 8, 1, 64, 32, 4096, 512) == 1088 // 4
     assert P.decode_workspace_bytes(256, 32, 128, 8, 32, 8193) == \
         P.lib().pkv_decode_stream_workspace_bytes(nw, 32, 8, 128)
     assert P.decode_plan(4, 8, 32, 1000, 0, 7) == (7, 5)
     assert P.decode_plan(4, 8, 32, 1000, 0, 1)[0] == 1
+
+
+def test_device_info_rejects_null(P):
+    # validation happens before any runtime query, so this needs no GPU
+    assert P.lib().pkv_device_info(None, None) == 1

@@ -175,7 +175,7 @@ def test_stream_decode_any_partition(P, name):
     lens = wl.decode_seq_lens().copy()
     if name == "edges":
         lens[0] = 0  # an empty row
-    auto = P.decode_stream_waves(wl.n_decode, wl.num_kv_heads, wl.head_dim, wl.page_size,
+    auto = P.decode_stream_waves(wl.n_decode, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.page_size,
                                  int(lens.max()), wl.window)
     for layer in range(wl.num_layers):
         qd, _ = wl.queries(layer)
@@ -196,6 +196,42 @@ def test_stream_decode_any_partition(P, name):
             check_close(outs[0], ref, f"{name} nw={nw}")
             if name == "edges":
                 assert np.all(outs[0][0] == 0)  # the empty row
+
+
+# group sizes around the stream-K split of wide groups (6 and 8 split into
+# halves at head_dim >= 128; 7 and head_dim 64 do not), pages 16/32, a window
+DECODE_SHAPES = [  # name, Hq, Hkv, D, page, window
+    ("d128_g6_p16", 12, 2, 128, 16, 0),
+    ("d128_g8_p32", 16, 2, 128, 32, 0),
+    ("d128_g7_p32", 7, 1, 128, 32, 0),
+    ("d64_g8_p16", 8, 1, 64, 16, 0),
+    ("d256_g6_p32_win", 6, 1, 256, 32, 200),
+]
+
+
+@pytest.mark.parametrize("shape", DECODE_SHAPES, ids=[s[0] for s in DECODE_SHAPES])
+def test_decode_shapes(P, shape):
+    name, hq, hkv, d, ps, win = shape
+    cfg = W.Config(name, 20261203, hq, hkv, d, ps, window=win,
+                   decode_ctx=("fixed", (1, 15, 16, 17, 33, 64, 300, 777, 1500)))
+    wl = W.build(cfg)
+    g = GpuPools(wl)
+    g.write("prefix")
+    g.write("new")
+    o = OraclePools(wl)
+    qd, _ = wl.queries(0)
+    lens = wl.decode_seq_lens()
+    ref = oracle.decode(qd, o.k, o.v, wl.block_tables[:wl.n_decode], lens, wl.page_size,
+                        wl.scale, wl.window)
+    say(f"[decode] {name}: automatic decomposition and 5 waves")
+    got = run_decode(P, g, qd)
+    check_close(got, ref, f"{name} decode")
+    out, ws = P.decode_stream(dev_bits(qd), g.k, g.v, dev_i32(wl.block_tables[:wl.n_decode]),
+                              dev_i32(lens), page_size=wl.page_size, num_waves=5, scale=wl.scale,
+                              window=wl.window)
+    P.decode_stream_merge(ws, out, num_waves=5, num_kv_heads=wl.num_kv_heads)
+    torch.cuda.synchronize()
+    check_close(host_bits(out), ref, f"{name} decode, 5 waves")
 
 
 @pytest.mark.parametrize("name", ["qwen3_decode", "window_shared"])
