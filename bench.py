@@ -2,7 +2,7 @@
 """Benchmark of the paged KV-cache attention step on one MI355X.
 
 A step is one pass of the whole hot path over one batch:
-slot addressing -> append of the step's new K/V rows -> decode attention
+fused slot addressing + append of the step's new K/V rows -> decode attention
 (stream-K partition of the batch's pages + merge of the cut segments, or
 split-K partials + combine with --num-splits) and/or varlen prefill, per
 layer.  The default workload is the bandwidth-bound decode: 256 sequences
@@ -16,7 +16,12 @@ dominant kernel (the decode kernel; the prefill kernel for the prefill-only
 workload) against its peak, timed with HIP events on the stream it runs on.
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
 workload.  Steps whose K/V fit in the last-level caches are timed after a
-cache scrub (see --scrub).
+cache scrub (see --scrub).  The step is also captured once as a step graph
+and replayed (see --graph), as the rollout engine replays its decode step;
+the JSON then reports the replay time, with the eager time beside it.
+Every launch of the step takes lengths and tables from device memory and
+sizes its grid from host bounds only, so prefill launches are captured too
+(one graph per set of host bounds).
 """
 from __future__ import annotations
 
@@ -86,7 +91,7 @@ def decode_bytes(wl) -> int:
 
 def append_bytes(wl) -> int:
     T = int(wl.new_lens.sum())
-    return 2 * 2 * T * wl.num_kv_heads * wl.head_dim * 2 + 4 * T + 4 * T  # rows r+w, slots w+r
+    return 2 * 2 * T * wl.num_kv_heads * wl.head_dim * 2 + 4 * T  # rows r+w, table entries
 
 
 def prefill_flops(wl) -> int:
@@ -145,7 +150,6 @@ class Step:
         self.T = nk.shape[0]
         self.cu_new_q = i32(wl.cu_lens(wl.new_lens))
         self.cu_new_k = i32(wl.cu_lens(wl.total_lens))
-        self.slots = torch.empty(self.T, dtype=torch.int32, device=dev)
         # decode
         self.B = wl.n_decode
         if self.B:
@@ -156,12 +160,16 @@ class Step:
             hq, d = wl.num_q_heads, wl.head_dim
             self.out_dec = torch.empty((self.B, hq, d), dtype=torch.bfloat16, device=dev)
             self.S, self.pps, self.nw = 0, 0, 0
-            if num_splits == 0 and self.B <= 2048:
+            # the decomposition the library picks for these arguments
+            self.method, cnt = P.decode_method(self.B, hq, wl.num_kv_heads, d, wl.page_size,
+                                               self.max_len, wl.window, num_splits)
+            if self.method == "stream":
                 # stream-K: persistent waves over the flattened page list + merge
-                self.nw = P.decode_stream_waves(self.B, hq, wl.num_kv_heads, d, wl.page_size,
-                                                self.max_len, wl.window)
+                self.nw = cnt
                 need = P.lib().pkv_decode_stream_workspace_bytes(self.nw, hq, wl.num_kv_heads, d)
                 self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            elif self.method == "direct":
+                self.S, self.pps = 1, 0
             else:
                 self.S, self.pps = P.decode_plan(self.B, wl.num_kv_heads, wl.page_size,
                                                  self.max_len, wl.window, num_splits)
@@ -188,9 +196,8 @@ class Step:
         """One step.  ``ev`` / ``pev`` = (before, after) events bracketing the layer-0 decode
         kernel / prefill kernel."""
         P, wl = self.P, self.wl
-        P.slot_mapping(self.bt, self.cu_new_q, self.cu_new_k, page_size=wl.page_size,
-                       num_pages=wl.num_pages, total_tokens=self.T, out=self.slots)
-        P.append(self.k_new, self.v_new, self.slots, self.k_pool, self.v_pool)
+        P.append_mapped(self.k_new, self.v_new, self.bt, self.cu_new_q, self.cu_new_k,
+                        self.k_pool, self.v_pool, page_size=wl.page_size)
         for layer in range(wl.num_layers):
             qd, qp = self.q[layer]
             if self.B:
@@ -403,6 +410,8 @@ def main():
     ap.add_argument("--scrub", choices=["auto", "on", "off"], default="auto",
                     help="1 GiB cache scrub before each timed step (auto: when the step's "
                          "algorithmic bytes are under 1 GiB)")
+    ap.add_argument("--graph", choices=["on", "off"], default="on",
+                    help="also time the step as a replayed step graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -475,6 +484,49 @@ def main():
     ms_step = float(step_ms.mean()) if scrub else wall / args.steps * 1e3
     _log(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step"
          f"{' (cache scrubbed before each step)' if scrub else ''}")
+    eager = {"ms_per_step": round(ms_step, 5),
+             "median_ms_per_step": round(float(np.median(step_ms)), 5),
+             "min_ms_per_step": round(float(step_ms.min()), 5)}
+
+    graph_info = None
+    if args.graph == "on":
+        # the same step captured once on a side stream and replayed; the new
+        # rows go to the same slots every step, so every replay's output must
+        # equal the eager step's bit for bit
+        ref_out = st.out_dec.clone() if st.B else None
+        ref_pre = st.out_pre.clone() if st.N else None
+        gs = torch.cuda.Stream()
+        gs.wait_stream(torch.cuda.current_stream())
+        graph = P.capture_graph(st.run, gs)
+        gsevs = [evpair() for _ in range(args.steps)]
+        with torch.cuda.stream(gs):
+            for _ in range(max(1, args.warmup)):
+                graph.launch(gs)
+            gs.synchronize()
+            t0 = time.perf_counter()
+            for i in range(args.steps):
+                if scrub:
+                    scratch.fill_(i & 0xff)
+                gsevs[i][0].record()
+                graph.launch(gs)
+                gsevs[i][1].record()
+            gs.synchronize()
+        gwall = time.perf_counter() - t0
+        g_ms = np.array([a.elapsed_time(b) for a, b in gsevs])
+        g_step = float(g_ms.mean()) if scrub else gwall / args.steps * 1e3
+        same = ((not st.B or bool(torch.equal(st.out_dec, ref_out))) and
+                (not st.N or bool(torch.equal(st.out_pre, ref_pre))))
+        kn, on = graph.nodes()
+        graph.destroy()
+        _log(f"[bench] graph replay: {g_step:.4f} ms/step (eager {ms_step:.4f}); "
+             f"matches eager: {same}")
+        graph_info = {"used": True, "kernel_nodes": kn, "other_nodes": on,
+                      "matches_eager": same, "ms_per_step": round(g_step, 5),
+                      "median_ms_per_step": round(float(np.median(g_ms)), 5),
+                      "min_ms_per_step": round(float(g_ms.min()), 5)}
+        if same is False:
+            raise SystemExit("graph replay differs from the eager step")
+        ms_step, step_ms = g_step, g_ms
 
     sb = step_bytes(wl)
     value = sb / (ms_step * 1e-3) / 1e9
@@ -497,6 +549,8 @@ def main():
         "median_ms_per_step": round(float(np.median(step_ms)), 5),
         "min_ms_per_step": round(float(step_ms.min()), 5),
         "cache_scrub": bool(scrub),
+        "step_graph": graph_info or {"used": False},
+        "eager": eager,
     }
     if st.B:
         kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
@@ -505,8 +559,10 @@ def main():
         src_hash = _src_hash("decode.hip", "decode_core.h", "common.h")
         traffic = recorded_traffic(args.config, src_hash)
         out["decode_tokens_per_s"] = round(st.B / (ms_step * 1e-3), 1)
-        out["decode_plan"] = ({"stream_k_waves": st.nw} if st.nw else
-                              {"num_splits": st.S, "pages_per_split": st.pps})
+        out["decode_plan"] = ({"method": "stream", "stream_k_waves": st.nw} if st.nw else
+                              {"method": "direct"} if st.S == 1 else
+                              {"method": "split", "num_splits": st.S,
+                               "pages_per_split": st.pps})
         kname = ("decode_stream_kernel (stream-K)" if st.nw else
                  "decode_kernel (split-K partials)" if st.S > 1 else "decode_kernel (direct)")
         out["roofline"] = {

@@ -2,8 +2,10 @@
  * pkv.h -- paged KV-cache attention for AMD Instinct MI355X (gfx950).
  *
  * A stateless C ABI.  Every buffer is caller-owned device memory on the
- * current HIP device; the library allocates nothing, never synchronises and
- * never reads device memory from the host.  All work is enqueued on the
+ * current HIP device; the library allocates no device memory (the only
+ * objects it creates are the step graphs of pkv_graph_end, which the caller
+ * frees with pkv_graph_destroy), never synchronises and never reads device
+ * memory from the host.  All work is enqueued on the
  * caller's stream and is asynchronous.  Calls are thread-safe.
  *
  * Data types.  bf16 values travel as their 16-bit patterns (uint16_t).
@@ -118,6 +120,32 @@ pkv_status pkv_append(const uint16_t* k_new, const uint16_t* v_new,
                       hipStream_t stream);
 
 /*
+ * Slot addressing and append fused in one launch: the slot of each new
+ * token is resolved from the block table exactly as pkv_slot_mapping does
+ * and its K/V rows are copied exactly as pkv_append does, without the
+ * slot array making a round trip through HBM (the engine writes the cache
+ * from inside its step, commit log 1847125, flex_attention paged-KV engine
+ * entry, "Files").  The pool holds num_pages*page_size slots.
+ *
+ *   k_new, v_new   bf16 [total_tokens, num_kv_heads, head_dim] (device, read)
+ *   block_tables, cu_seq_lens_q, cu_seq_lens_k: as pkv_slot_mapping
+ *   k_pool, v_pool bf16 [num_kv_heads, num_pages*page_size, head_dim]
+ *                  (device, written)
+ *   slot_mapping   int32 [total_tokens] (device, written) or NULL; when given
+ *                  it receives the same values pkv_slot_mapping writes
+ *
+ * Tokens with slot -1 are skipped.  Two tokens with the same slot give an
+ * unspecified row.  num_seqs or total_tokens may be 0 (nothing is enqueued).
+ */
+pkv_status pkv_append_mapped(const uint16_t* k_new, const uint16_t* v_new,
+                             const int32_t* block_tables, int32_t max_pages_per_seq,
+                             const int32_t* cu_seq_lens_q, const int32_t* cu_seq_lens_k,
+                             int32_t num_seqs, int32_t total_tokens, int32_t page_size,
+                             int32_t num_pages, int32_t num_kv_heads, int32_t head_dim,
+                             uint16_t* k_pool, uint16_t* v_pool, int32_t* slot_mapping,
+                             hipStream_t stream);
+
+/*
  * Split-K planning.  Split-K cuts each row's keys into num_splits
  * partitions of pages_per_split logical pages (flash-decoding); the plan
  * depends only on host scalars.  num_splits_requested = 0 picks a count from
@@ -127,6 +155,23 @@ pkv_status pkv_append(const uint16_t* k_new, const uint16_t* v_new,
 pkv_status pkv_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t page_size,
                            int32_t max_seq_len, int32_t window, int32_t num_splits_requested,
                            int32_t* num_splits, int32_t* pages_per_split);
+
+/*
+ * The decomposition pkv_decode uses for these host arguments:
+ *   *method = PKV_DECODE_DIRECT  one workgroup per (sequence, KV head), one
+ *                                kernel, no workspace (*count = 1);
+ *             PKV_DECODE_SPLIT   split-K partials + combine (*count = splits);
+ *             PKV_DECODE_STREAM  stream-K + merge (*count = persistent waves).
+ * With num_splits_requested = 0 a batch of at most 256 (sequence, KV head)
+ * rows whose query-head group is not split in two by stream-K goes direct,
+ * up to 2048 sequences go stream-K, larger batches split-K.  Either output
+ * pointer may be NULL.
+ */
+enum { PKV_DECODE_DIRECT = 0, PKV_DECODE_SPLIT = 1, PKV_DECODE_STREAM = 2 };
+pkv_status pkv_decode_method(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t page_size, int32_t max_seq_len,
+                             int32_t window, int32_t num_splits_requested, int32_t* method,
+                             int32_t* count);
 
 /* Bytes of workspace pkv_decode needs for these arguments (0 when it needs none). */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
@@ -150,10 +195,12 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
  *                  may be NULL when that is 0
  *   out            bf16 [num_seqs, num_q_heads, head_dim]       (device, written)
  *
- * num_splits = 0 picks the decomposition: the stream-K partition
- * (pkv_decode_stream + pkv_decode_stream_merge) for up to 2048 rows, else
- * split-K with an automatic split count; num_splits >= 1 forces split-K with
- * that many splits (1 = no split, no workspace).
+ * num_splits = 0 picks the decomposition with pkv_decode_method: one
+ * kernel with one workgroup per (sequence, KV head) row for small batches,
+ * the stream-K partition (pkv_decode_stream + pkv_decode_stream_merge) up
+ * to 2048 sequences, else split-K with an automatic split count;
+ * num_splits >= 1 forces split-K with that many splits (1 = no split, no
+ * workspace).
  *
  * A row with no key (seq_lens[b] == 0) is written as zeros.  Results are
  * deterministic and independent of the physical page order.
@@ -276,6 +323,37 @@ pkv_status pkv_prefill_varlen(const uint16_t* q, const uint16_t* k_pool, const u
                               int32_t page_size, int32_t num_pages,
                               float scale, int32_t window,
                               uint16_t* out, hipStream_t stream);
+
+/*
+ * Step graphs.  The rollout engine captures one decode step per batch-size
+ * bucket (1, 2, 4, 8, ...) during warm-up, dispatches each step to the
+ * nearest bucket at or above the live batch, pads it with no-op rows and
+ * replays the graph; graph replay is its main lever against launch cost
+ * (commit log 1847125, flex_attention paged-KV engine entry, "Why this
+ * works" item 3).  Every pkv_* launch above is replay-safe: lengths, tables
+ * and slot positions are read from device arrays when the kernels run, and
+ * grids depend on host arguments only, which a graph freezes.  A padded
+ * decode row is a row with seq_len 0 (its output is zero) and, for
+ * pkv_append_mapped, no new tokens (cu_seq_lens_q repeats its last value).
+ *
+ * pkv_graph_begin starts capturing `stream` (not the legacy null stream;
+ * thread-local capture mode): pkv_* calls on it are then recorded, not
+ * run.  pkv_graph_end stops the capture and instantiates the graph into
+ * *graph (set to NULL on failure; a call that failed during the capture
+ * makes pkv_graph_end fail too, and the capture is ended either way).
+ * pkv_graph_launch enqueues one replay on any stream of the same device;
+ * the buffers it was captured with must stay allocated and must not be
+ * resized.  pkv_graph_nodes counts the graph's kernel nodes and its other
+ * nodes (memset, copy, ...).  pkv_graph_destroy frees the graph (NULL is
+ * accepted); replays already enqueued still complete.
+ */
+typedef struct pkv_graph_s* pkv_graph;
+
+pkv_status pkv_graph_begin(hipStream_t stream);
+pkv_status pkv_graph_end(hipStream_t stream, pkv_graph* graph);
+pkv_status pkv_graph_launch(pkv_graph graph, hipStream_t stream);
+pkv_status pkv_graph_nodes(pkv_graph graph, int32_t* kernel_nodes, int32_t* other_nodes);
+pkv_status pkv_graph_destroy(pkv_graph graph);
 
 #ifdef __cplusplus
 }

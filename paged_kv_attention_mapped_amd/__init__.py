@@ -20,9 +20,13 @@ import torch
 
 __all__ = [
     "PkvError",
+    "StepGraph",
     "append",
+    "append_mapped",
+    "capture_graph",
     "decode",
     "decode_combine",
+    "decode_method",
     "decode_plan",
     "decode_split",
     "decode_stream",
@@ -44,7 +48,9 @@ EXPORTS = (
     "pkv_device_info",
     "pkv_slot_mapping",
     "pkv_append",
+    "pkv_append_mapped",
     "pkv_decode_plan",
+    "pkv_decode_method",
     "pkv_decode_workspace_bytes",
     "pkv_decode",
     "pkv_decode_split",
@@ -54,6 +60,11 @@ EXPORTS = (
     "pkv_decode_stream",
     "pkv_decode_stream_merge",
     "pkv_prefill_varlen",
+    "pkv_graph_begin",
+    "pkv_graph_end",
+    "pkv_graph_launch",
+    "pkv_graph_nodes",
+    "pkv_graph_destroy",
 )
 
 
@@ -75,7 +86,9 @@ _SIGS = {
     "pkv_device_info": ([_P, _P], _I32),
     "pkv_slot_mapping": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "pkv_append": ([_P, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P], _I32),
+    "pkv_append_mapped": ([_P, _P, _P, _I32, _P, _P] + [_I32] * 6 + [_P, _P, _P, _P], _I32),
     "pkv_decode_plan": ([_I32, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
+    "pkv_decode_method": ([_I32] * 8 + [_P, _P], _I32),
     "pkv_decode_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
     "pkv_decode": ([_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                     _F, _I32, _I32, _P, _SZ, _P, _P], _I32),
@@ -89,6 +102,11 @@ _SIGS = {
     "pkv_decode_stream_merge": ([_P, _SZ, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "pkv_prefill_varlen": ([_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                             _I32, _I32, _I32, _F, _I32, _P, _P], _I32),
+    "pkv_graph_begin": ([_P], _I32),
+    "pkv_graph_end": ([_P, _P], _I32),
+    "pkv_graph_launch": ([_P, _P], _I32),
+    "pkv_graph_nodes": ([_P, _P, _P], _I32),
+    "pkv_graph_destroy": ([_P], _I32),
 }
 
 
@@ -190,11 +208,52 @@ def append(k_new, v_new, slot_mapping, k_pool, v_pool, stream=None):
         k_pool.shape[1], _stream(stream)))
 
 
+def append_mapped(k_new, v_new, block_tables, cu_seq_lens_q, cu_seq_lens_k, k_pool, v_pool, *,
+                  page_size, slot_mapping_out=None, stream=None):
+    """Slot addressing and append in one launch (``pkv_append_mapped``).
+
+    ``k_pool``/``v_pool`` are ``[Hkv, num_pages * page_size, D]``; when
+    ``slot_mapping_out`` (int32 ``[T]``) is given it receives every token's slot.
+    """
+    _bf16(k_new, "k_new"); _bf16(v_new, "v_new"); _bf16(k_pool, "k_pool"); _bf16(v_pool, "v_pool")
+    _i32(block_tables, "block_tables"); _i32(cu_seq_lens_q, "cu_q"); _i32(cu_seq_lens_k, "cu_k")
+    if slot_mapping_out is not None:
+        _i32(slot_mapping_out, "slot_mapping_out")
+    _dev(k_new, v_new, block_tables, cu_seq_lens_q, cu_seq_lens_k, k_pool, v_pool,
+         slot_mapping_out)
+    T, hkv, d = k_new.shape
+    if v_new.shape != k_new.shape or k_pool.shape != v_pool.shape:
+        raise ValueError("shape mismatch")
+    if k_pool.shape[0] != hkv or k_pool.shape[2] != d or k_pool.shape[1] % page_size:
+        raise ValueError("pool shape must be [Hkv, num_pages * page_size, D]")
+    if slot_mapping_out is not None and slot_mapping_out.numel() < T:
+        raise ValueError("slot_mapping_out is shorter than the token count")
+    _check("pkv_append_mapped", lib().pkv_append_mapped(
+        _ptr(k_new), _ptr(v_new), _ptr(block_tables), block_tables.shape[1],
+        _ptr(cu_seq_lens_q), _ptr(cu_seq_lens_k), cu_seq_lens_q.numel() - 1, T, page_size,
+        k_pool.shape[1] // page_size, hkv, d, _ptr(k_pool), _ptr(v_pool),
+        _ptr(slot_mapping_out), _stream(stream)))
+
+
 def device_info():
     """``(compute_units, max_clock_khz)`` of the current device (``pkv_device_info``)."""
     cus, khz = ctypes.c_int32(0), ctypes.c_int32(0)
     _check("pkv_device_info", lib().pkv_device_info(ctypes.byref(cus), ctypes.byref(khz)))
     return cus.value, khz.value
+
+
+DECODE_METHODS = {0: "direct", 1: "split", 2: "stream"}
+
+
+def decode_method(num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, max_seq_len,
+                  window=0, num_splits=0):
+    """``(method, count)`` that ``pkv_decode`` uses: ``("direct", 1)``,
+    ``("split", splits)`` or ``("stream", waves)`` (``pkv_decode_method``)."""
+    m, c = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("pkv_decode_method", lib().pkv_decode_method(
+        num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, max_seq_len, window,
+        num_splits, ctypes.byref(m), ctypes.byref(c)))
+    return DECODE_METHODS[m.value], c.value
 
 
 def decode_plan(num_seqs, num_kv_heads, page_size, max_seq_len, window=0, num_splits=0):
@@ -340,3 +399,64 @@ def prefill_varlen(q, k_pool, v_pool, block_tables, cu_seq_lens_q, cu_seq_lens_k
         _ptr(cu_seq_lens_q), _ptr(cu_seq_lens_k), n, Tq, max_seqlen_q, max_seqlen_k, hq, hkv, d,
         page_size, num_pages, float(scale), window, _ptr(out), _stream(stream)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# step graphs
+# ---------------------------------------------------------------------------
+class StepGraph:
+    """A captured sequence of pkv launches (``pkv_graph_end``), replayed by ``launch``.
+
+    The tensors the launches were captured with must stay alive and keep
+    their storage for as long as the graph is replayed.
+    """
+
+    def __init__(self, handle: ctypes.c_void_p, keep=()):
+        self._h = handle
+        self._keep = tuple(keep)
+
+    def launch(self, stream=None):
+        if not self._h:
+            raise ValueError("graph was destroyed")
+        _check("pkv_graph_launch", lib().pkv_graph_launch(self._h, _stream(stream)))
+
+    def nodes(self):
+        """``(kernel_nodes, other_nodes)`` of the captured graph (``pkv_graph_nodes``)."""
+        k, o = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check("pkv_graph_nodes", lib().pkv_graph_nodes(self._h, ctypes.byref(k), ctypes.byref(o)))
+        return k.value, o.value
+
+    def destroy(self):
+        if self._h:
+            h, self._h = self._h, None
+            _check("pkv_graph_destroy", lib().pkv_graph_destroy(h))
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def capture_graph(fn, stream, keep=()):
+    """Capture the pkv calls ``fn()`` enqueues into a ``StepGraph`` (``pkv_graph_begin/end``).
+
+    ``fn`` runs once with ``stream`` (a non-default ``torch.cuda.Stream``)
+    current; it must only enqueue pkv calls on preallocated tensors (no
+    allocation, copy or host read).  ``keep`` holds tensors the graph uses.
+    """
+    if stream is None or stream.cuda_stream == 0:
+        raise ValueError("capture needs a non-default stream")
+    hs = _stream(stream)
+    with torch.cuda.stream(stream):
+        _check("pkv_graph_begin", lib().pkv_graph_begin(hs))
+        h = ctypes.c_void_p(None)
+        try:
+            fn()
+        except BaseException:
+            lib().pkv_graph_end(hs, ctypes.byref(h))
+            if h:
+                lib().pkv_graph_destroy(h)
+            raise
+        _check("pkv_graph_end", lib().pkv_graph_end(hs, ctypes.byref(h)))
+    return StepGraph(h, keep)

@@ -39,6 +39,10 @@ int64_t key_pages(int page_size, int max_seq_len, int window) {
 }
 
 constexpr int kStreamMaxSeqs = 2048;     // row lengths are scanned in LDS
+// A batch of at most this many (sequence, KV head) rows is decoded by one
+// workgroup per row with no second kernel: at that size a stream-K launch
+// is no faster and its merge launch costs more than the balance it buys.
+constexpr int kDirectMaxRows = 256;
 constexpr int kStreamMinUnitsPerWave = 4;
 constexpr int kStreamWavesPerSimd = 2;   // matches the stream kernel's register budget
 
@@ -129,6 +133,29 @@ pkv_status pkv_append(const uint16_t* k_new, const uint16_t* v_new, const int32_
                                   k_pool, v_pool, num_slots, stream));
 }
 
+pkv_status pkv_append_mapped(const uint16_t* k_new, const uint16_t* v_new,
+                             const int32_t* block_tables, int32_t max_pages_per_seq,
+                             const int32_t* cu_seq_lens_q, const int32_t* cu_seq_lens_k,
+                             int32_t num_seqs, int32_t total_tokens, int32_t page_size,
+                             int32_t num_pages, int32_t num_kv_heads, int32_t head_dim,
+                             uint16_t* k_pool, uint16_t* v_pool, int32_t* slot_mapping,
+                             hipStream_t stream) {
+  if (num_seqs < 0 || total_tokens < 0 || max_pages_per_seq <= 0 || num_pages <= 0 ||
+      num_kv_heads <= 0 || page_size <= 0)
+    return PKV_ERR_BAD_SHAPE;
+  if ((int64_t)num_pages * page_size > INT32_MAX) return PKV_ERR_BAD_SHAPE;
+  if (!supported_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || total_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !block_tables || !cu_seq_lens_q || !cu_seq_lens_k || !k_pool ||
+      !v_pool)
+    return PKV_ERR_NULL_ARG;
+  return hip_status(launch_append_mapped(k_new, v_new, block_tables, max_pages_per_seq,
+                                         cu_seq_lens_q, cu_seq_lens_k, num_seqs, total_tokens,
+                                         page_size, num_pages, num_kv_heads, head_dim, k_pool,
+                                         v_pool, (int64_t)num_pages * page_size, slot_mapping,
+                                         stream));
+}
+
 pkv_status pkv_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t page_size,
                            int32_t max_seq_len, int32_t window, int32_t num_splits_requested,
                            int32_t* num_splits, int32_t* pages_per_split) {
@@ -155,16 +182,48 @@ pkv_status pkv_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t page_
   return PKV_OK;
 }
 
+pkv_status pkv_decode_method(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t page_size, int32_t max_seq_len,
+                             int32_t window, int32_t num_splits_requested, int32_t* method,
+                             int32_t* count) {
+  if (num_seqs < 0 || max_seq_len < 0 || num_splits_requested < 0) return PKV_ERR_BAD_SHAPE;
+  const pkv_status hs = check_heads(num_q_heads, num_kv_heads);
+  if (hs != PKV_OK) return hs;
+  if (!supported_dim(head_dim) || !supported_ps(page_size)) return PKV_ERR_UNSUPPORTED;
+  int32_t m = PKV_DECODE_SPLIT, c = 0;
+  if (num_splits_requested == 0 && num_seqs > 0 && num_seqs <= kStreamMaxSeqs) {
+    const int shift = stream_kv_shift(num_q_heads, num_kv_heads, head_dim);
+    if (shift == 0 && (int64_t)num_seqs * num_kv_heads <= kDirectMaxRows) {
+      m = PKV_DECODE_DIRECT;
+      c = 1;
+    } else {
+      m = PKV_DECODE_STREAM;
+      const pkv_status st = pkv_decode_stream_waves(num_seqs, num_q_heads, num_kv_heads,
+                                                    head_dim, page_size, max_seq_len, window, &c);
+      if (st != PKV_OK) return st;
+    }
+  } else {
+    int32_t pps = 0;
+    const pkv_status st = pkv_decode_plan(num_seqs, num_kv_heads, page_size, max_seq_len, window,
+                                          num_splits_requested, &c, &pps);
+    if (st != PKV_OK) return st;
+    if (c <= 1) m = PKV_DECODE_DIRECT;
+  }
+  if (method) *method = m;
+  if (count) *count = c;
+  return PKV_OK;
+}
+
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t num_kv_heads, int32_t page_size, int32_t max_seq_len,
                                   int32_t window, int32_t num_splits_requested) {
-  if (num_splits_requested == 0 && num_seqs > 0 && num_seqs <= kStreamMaxSeqs) {
-    int32_t nw = 0;
-    if (pkv_decode_stream_waves(num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
-                                max_seq_len, window, &nw) != PKV_OK)
-      return 0;
+  int32_t method = 0, nw = 0;
+  if (pkv_decode_method(num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, max_seq_len,
+                        window, num_splits_requested, &method, &nw) != PKV_OK)
+    return 0;
+  if (method == PKV_DECODE_STREAM)
     return pkv_decode_stream_workspace_bytes(nw, num_q_heads, num_kv_heads, head_dim);
-  }
+  if (method == PKV_DECODE_DIRECT) return 0;
   int32_t s = 0, pps = 0;
   if (pkv_decode_plan(num_seqs, num_kv_heads, page_size, max_seq_len, window,
                       num_splits_requested, &s, &pps) != PKV_OK)
@@ -267,11 +326,11 @@ pkv_status pkv_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t*
                                num_pages, max_seq_len);
   if (st != PKV_OK) return st;
   if (num_splits < 0) return PKV_ERR_BAD_SHAPE;
-  if (num_splits == 0 && num_seqs > 0 && num_seqs <= kStreamMaxSeqs) {
-    int32_t nw = 0;
-    st = pkv_decode_stream_waves(num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
-                                 max_seq_len, window, &nw);
-    if (st != PKV_OK) return st;
+  int32_t method = 0, nw = 0;
+  st = pkv_decode_method(num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, max_seq_len,
+                         window, num_splits, &method, &nw);
+  if (st != PKV_OK) return st;
+  if (method == PKV_DECODE_STREAM) {
     if (!out) return PKV_ERR_NULL_ARG;
     if (!workspace) return PKV_ERR_NULL_ARG;
     if (workspace_bytes <
@@ -284,9 +343,9 @@ pkv_status pkv_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t*
     return pkv_decode_stream_merge(workspace, workspace_bytes, nw, num_q_heads, num_kv_heads,
                                    head_dim, out, stream);
   }
-  int32_t s = 0, pps = 0;
-  st = pkv_decode_plan(num_seqs, num_kv_heads, page_size, max_seq_len, window, num_splits, &s,
-                       &pps);
+  int32_t s = 1, pps = 0;
+  st = pkv_decode_plan(num_seqs, num_kv_heads, page_size, max_seq_len, window,
+                       method == PKV_DECODE_DIRECT ? 1 : num_splits, &s, &pps);
   if (st != PKV_OK) return st;
   if (num_seqs == 0) return PKV_OK;
   if (!out) return PKV_ERR_NULL_ARG;

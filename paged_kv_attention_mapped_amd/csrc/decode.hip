@@ -378,49 +378,81 @@ void decode_stream_kernel(StreamArgs sa) {
   }
 }
 
-// Merge of cut segments: one wave per merge descriptor; pieces are merged
-// in wave order, so the result does not depend on timing.
-template <int D>
+// Merge of cut segments: one wave per merge descriptor.  The pieces are
+// taken in wave order, kMergeBatch at a time with all their loads issued
+// together, and folded into a running (max, sum, accumulator) per query
+// head, so the result does not depend on timing and a segment cut into n
+// pieces costs about n / kMergeBatch memory round trips.
+constexpr int kMergeBatch = 4;
+
+template <int D, int G>
 __global__ __launch_bounds__(64) void stream_merge_kernel(StreamArgs sa) {
+  constexpr int EPL = D / 64;
   const int slot = blockIdx.x, lane = threadIdx.x;
-  const int* dsc = sa.desc + slot * kDescInts;
-  if (dsc[0] == 0) return;
+  // descriptor: [valid, sequence, KV head, last wave, total units]
+  const int dv = lane < 5 ? sa.desc[slot * kDescInts + lane] : 0;
+  if (__builtin_amdgcn_readfirstlane(dv) == 0) return;
+  const int b = __builtin_amdgcn_readlane(dv, 1);
+  const int hk = __builtin_amdgcn_readlane(dv, 2);
+  const int w1 = __builtin_amdgcn_readlane(dv, 3);
+  const int64_t U = __builtin_amdgcn_readlane(dv, 4);
   const DecodeArgs& a = sa.base;
   const int g = a.group, nw = sa.num_waves;
-  const int b = dsc[1], hk = dsc[2], w1 = dsc[3];
-  const int64_t U = dsc[4];
   const int w0 = slot >> 1;
   const int64_t stride = (int64_t)g * (D + 2);
-  auto piece = [&](int w) -> const float* {
-    return sa.part + (int64_t)(w == w0 ? slot : 2 * w) * stride;
-  };
   // waves with an empty range (possible when there are fewer units than
   // waves) hold no piece
   auto holds = [&](int w) { return (int64_t)w * U / nw < (int64_t)(w + 1) * U / nw; };
-  for (int h = 0; h < g; ++h) {
-    float Mx = -INFINITY;
-    for (int w = w0; w <= w1; ++w)
-      if (holds(w)) Mx = fmaxf(Mx, piece(w)[g * D + h]);
-    float lsum = 0.f;
-    float o[D / 64];
+
+  float Mr[G], Lr[G], o[G][EPL];
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) o[i] = 0.f;
-    if (Mx != -INFINITY) {
-      for (int w = w0; w <= w1; ++w) {
-        if (!holds(w)) continue;
-        const float* p = piece(w);
-        const float mw = p[g * D + h];
-        if (mw == -INFINITY) continue;
-        const float wt = fast_exp2(mw - Mx);
-        lsum = fmaf(wt, p[g * D + g + h], lsum);
+  for (int h = 0; h < G; ++h) {
+    Mr[h] = -INFINITY;
+    Lr[h] = 0.f;
 #pragma unroll
-        for (int i = 0; i < D / 64; ++i) o[i] = fmaf(wt, p[h * D + lane + 64 * i], o[i]);
+    for (int i = 0; i < EPL; ++i) o[h][i] = 0.f;
+  }
+  for (int wb = w0; wb <= w1; wb += kMergeBatch) {
+    float ml[kMergeBatch], pv[kMergeBatch][G][EPL];
+    // loads are unconditional (a wave past w1 re-reads w1's piece) so that
+    // they all leave before the first one is used
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const int w = min(wb + k, w1);
+      const float* p = sa.part + (int64_t)(w == w0 ? slot : 2 * w) * stride;
+      ml[k] = p[g * D + min(lane, 2 * g - 1)];  // lanes h: max of head h; lanes g+h: its sum
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) pv[k][h][i] = p[min(h, g - 1) * D + lane + 64 * i];
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const int w = wb + k;
+      if (w > w1 || !holds(w)) continue;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        if (h >= g) continue;
+        const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml[k]), h));
+        const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml[k]), g + h));
+        if (m == -INFINITY) continue;
+        const float Mn = fmaxf(Mr[h], m);
+        const float al = fast_exp2(Mr[h] - Mn);
+        const float be = fast_exp2(m - Mn);
+        Lr[h] = fmaf(Lr[h], al, l * be);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) o[h][i] = fmaf(o[h][i], al, pv[k][h][i] * be);
+        Mr[h] = Mn;
       }
     }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if (h >= g) continue;
+    const float inv = Lr[h] > 0.f ? 1.f / Lr[h] : 0.f;
     uint16_t* out = a.out + ((int64_t)b * a.num_q_heads + hk * g + h) * D;
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) out[lane + 64 * i] = (uint16_t)f32_to_bf16(o[i] * inv);
+    for (int i = 0; i < EPL; ++i) out[lane + 64 * i] = (uint16_t)f32_to_bf16(o[h][i] * inv);
   }
 }
 
@@ -501,12 +533,22 @@ hipError_t launch_decode_stream(const StreamArgs& sa, int head_dim, int page_siz
   }
 }
 
+template <int D>
+void launch_merge_d(const StreamArgs& sa, hipStream_t st) {
+  const dim3 grid(2 * sa.num_waves);
+  if (sa.base.group <= 2)
+    hipLaunchKernelGGL((stream_merge_kernel<D, 2>), grid, dim3(64), 0, st, sa);
+  else if (sa.base.group <= 4)
+    hipLaunchKernelGGL((stream_merge_kernel<D, 4>), grid, dim3(64), 0, st, sa);
+  else
+    hipLaunchKernelGGL((stream_merge_kernel<D, 8>), grid, dim3(64), 0, st, sa);
+}
+
 hipError_t launch_stream_merge(const StreamArgs& sa, int head_dim, hipStream_t st) {
-  dim3 grid(2 * sa.num_waves);
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL(stream_merge_kernel<64>, grid, dim3(64), 0, st, sa); break;
-    case 128: hipLaunchKernelGGL(stream_merge_kernel<128>, grid, dim3(64), 0, st, sa); break;
-    default: hipLaunchKernelGGL(stream_merge_kernel<256>, grid, dim3(64), 0, st, sa); break;
+    case 64: launch_merge_d<64>(sa, st); break;
+    case 128: launch_merge_d<128>(sa, st); break;
+    default: launch_merge_d<256>(sa, st); break;
   }
   return hipGetLastError();
 }

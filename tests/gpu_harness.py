@@ -50,7 +50,8 @@ def check_close(gpu_bits, ref, what="", max_abs=MAX_ABS, mean_abs=MEAN_ABS):
 
 
 class GpuPools:
-    """Poisoned GPU pools of a workload, filled through pkv_slot_mapping + pkv_append."""
+    """Poisoned GPU pools of a workload, filled through pkv_slot_mapping + pkv_append
+    (or through pkv_append_mapped when ``fused``)."""
 
     def __init__(self, wl: W.Workload):
         self.wl = wl
@@ -59,8 +60,11 @@ class GpuPools:
         self.v = torch.full(shape, int(W.BF16_NAN), dtype=torch.int16, device="cuda")
         self.bt = dev_i32(wl.block_tables)
 
-    def write(self, part: str, seqs=None, chunk=64):
-        """Append the ``part`` tokens of ``seqs`` (default all), a few sequences at a time."""
+    def write(self, part: str, seqs=None, chunk=64, fused=False, slots_log=None):
+        """Append the ``part`` tokens of ``seqs`` (default all), a few sequences at a time.
+
+        With ``slots_log`` (a list) the fused path also returns every chunk's
+        slot array, as ``(seqs, cu_q, cu_k, slots)`` tuples."""
         wl = self.wl
         seqs = np.arange(wl.num_seqs) if seqs is None else np.asarray(seqs)
         for i in range(0, len(seqs), chunk):
@@ -70,6 +74,15 @@ class GpuPools:
             for s in sub:
                 wl._kv_cache.pop(int(s), None)
             if k.shape[0] == 0:
+                continue
+            if fused:
+                out = None if slots_log is None else torch.full(
+                    (k.shape[0],), -7, dtype=torch.int32, device="cuda")
+                P.append_mapped(dev_bits(k), dev_bits(v), dev_i32(wl.block_tables[sub]),
+                                dev_i32(wl.cu_lens(lq)), dev_i32(wl.cu_lens(lk)), self.k, self.v,
+                                page_size=wl.page_size, slot_mapping_out=out)
+                if slots_log is not None:
+                    slots_log.append((sub, wl.cu_lens(lq), wl.cu_lens(lk), out))
                 continue
             slots = P.slot_mapping(dev_i32(wl.block_tables[sub]), dev_i32(wl.cu_lens(lq)),
                                    dev_i32(wl.cu_lens(lk)), page_size=wl.page_size,

@@ -30,8 +30,10 @@ def declared():
 
 def test_header_declares_the_entry_points():
     assert declared() == sorted([
-        "pkv_append", "pkv_decode", "pkv_decode_combine", "pkv_decode_plan", "pkv_decode_split",
-        "pkv_device_info",
+        "pkv_append", "pkv_append_mapped", "pkv_decode", "pkv_decode_combine",
+        "pkv_decode_method", "pkv_decode_plan", "pkv_decode_split",
+        "pkv_device_info", "pkv_graph_begin", "pkv_graph_destroy", "pkv_graph_end",
+        "pkv_graph_launch", "pkv_graph_nodes",
         "pkv_decode_stream", "pkv_decode_stream_merge", "pkv_decode_stream_waves",
         "pkv_decode_stream_workspace_bytes", "pkv_decode_workspace_bytes", "pkv_prefill_varlen",
         "pkv_slot_mapping", "pkv_status_string"])
@@ -131,3 +133,57 @@ def test_decode_plan(P):
 def test_device_info_rejects_null(P):
     # validation happens before any runtime query, so this needs no GPU
     assert P.lib().pkv_device_info(None, None) == 1
+
+
+def test_append_mapped_validation(P):
+    f = P.lib().pkv_append_mapped
+    args = [FAKE, FAKE, FAKE, 4, FAKE, FAKE, 2, 5, 32, 10, 2, 128, FAKE, FAKE, None, None]
+    a = list(args); a[0] = None
+    assert f(*a) == 1
+    a = list(args); a[2] = None
+    assert f(*a) == 1
+    a = list(args); a[11] = 96
+    assert f(*a) == 3
+    a = list(args); a[3] = 0
+    assert f(*a) == 2
+    a = list(args); a[9] = 0
+    assert f(*a) == 2
+    a = list(args); a[8] = 1 << 20; a[9] = 1 << 12   # pool of 2^32 slots does not fit int32
+    assert f(*a) == 2
+    a = list(args); a[7] = 0; a[0] = None            # no tokens: nothing to check or enqueue
+    assert f(*a) == 0
+    a = list(args); a[6] = 0
+    assert f(*a) == 0
+
+
+def test_graph_validation(P):
+    L = P.lib()
+    h = ctypes.c_void_p(None)
+    assert L.pkv_graph_begin(None) == 1              # the null stream cannot be captured
+    assert L.pkv_graph_end(None, ctypes.byref(h)) == 1
+    assert L.pkv_graph_end(FAKE, None) == 1
+    assert L.pkv_graph_launch(None, None) == 1
+    k, o = ctypes.c_int32(0), ctypes.c_int32(0)
+    assert L.pkv_graph_nodes(None, ctypes.byref(k), ctypes.byref(o)) == 1
+    assert L.pkv_graph_destroy(None) == 0
+    with pytest.raises(ValueError):
+        P.capture_graph(lambda: None, None)
+
+
+def test_decode_method(P):
+    # small batches: one kernel, one workgroup per (sequence, KV head) row
+    assert P.decode_method(4, 2, 1, 64, 16, 64) == ("direct", 1)
+    assert P.decode_method(32, 32, 8, 128, 32, 1025) == ("direct", 1)      # 256 rows
+    assert P.lib().pkv_decode_workspace_bytes(32, 32, 128, 8, 32, 1025, 0, 0) == 0
+    # larger batches, or a group that stream-K splits in two: stream-K
+    assert P.decode_method(56, 32, 8, 128, 32, 2049) == \
+        ("stream", P.decode_stream_waves(56, 32, 8, 128, 32, 2049))
+    assert P.decode_method(64, 8, 1, 256, 32, 4097, 512)[0] == "stream"
+    assert P.decode_method(256, 32, 8, 128, 32, 8193) == ("stream", 2048)
+    # past the stream-K row limit, or when splits are asked for: split-K
+    assert P.decode_method(4096, 32, 8, 128, 32, 8192) == ("split", 8)   # 32-page splits
+    assert P.decode_method(4096, 32, 8, 128, 32, 1024) == ("direct", 1)  # one split suffices
+    assert P.decode_method(4, 8, 2, 128, 32, 1000, 0, 3) == ("split", 3)
+    assert P.decode_method(4, 8, 2, 128, 32, 1000, 0, 1) == ("direct", 1)
+    assert P.lib().pkv_decode_method(4, 8, 2, 96, 32, 100, 0, 0, None, None) == 3
+    assert P.lib().pkv_decode_method(4, 8, 3, 128, 32, 100, 0, 0, None, None) == 2

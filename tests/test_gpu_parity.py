@@ -95,6 +95,61 @@ def test_append_whole_pool_bit_exact(name):
     assert np.array_equal(host_bits(g.v), o.v)
 
 
+@pytest.mark.parametrize("name", SMALL)
+def test_append_mapped_bit_exact(P, name):
+    """The fused addressing + append writes the oracle's pools and slots."""
+    wl = W.make(name)
+    say(f"[append_mapped] {name}")
+    g = GpuPools(wl)
+    log = []
+    g.write("prefix", fused=True, slots_log=log)
+    g.write("new", fused=True, slots_log=log, chunk=3)
+    o = OraclePools(wl)
+    assert np.array_equal(host_bits(g.k), o.k)
+    assert np.array_equal(host_bits(g.v), o.v)
+    for sub, cq, ck, got in log:
+        ref = oracle.slot_mapping(wl.block_tables[sub], cq, ck, wl.page_size)
+        assert np.array_equal(got.cpu().numpy().astype(np.int64), ref)
+
+
+def test_append_mapped_edge_cases(P):
+    """Sequences with no new tokens, unmapped table entries (-1, past the pool)
+    and positions past the table: those tokens get slot -1 and leave the pool
+    untouched; empty steps enqueue nothing."""
+    hkv, d, ps, npg = 2, 64, 16, 6
+    rng = np.random.default_rng(5)
+    bt = np.array([[3, -1, 0], [5, 1, 9], [2, 4, 0], [0, 0, 0]], np.int32)
+    lq = np.array([20, 20, 5, 0], np.int32)    # seq 3: no new tokens
+    lk = np.array([20, 40, 60, 5], np.int32)   # seq 2 runs past its 3-page table
+    cq = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    ck = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    T = int(cq[-1])
+    kn = rng.integers(0, 1 << 16, (T, hkv, d), dtype=np.uint16)
+    vn = rng.integers(0, 1 << 16, (T, hkv, d), dtype=np.uint16)
+    # expected slots: the oracle's address over a table padded with -1, and
+    # -1 wherever the physical page is not in [0, npg)
+    bt_pad = np.concatenate([bt, np.full((4, 1), -1, np.int32)], axis=1)
+    slots = oracle.slot_mapping(bt_pad, cq, ck, ps)
+    slots = np.where((slots >= 0) & (slots < npg * ps), slots, -1)
+    assert (slots >= 0).sum() == 16 + 12      # seq 0 page 0, seq 1 page 1
+    pool0 = np.full((hkv, npg * ps, d), W.BF16_NAN, np.uint16)
+    ok, ov = oracle.append(pool0, pool0, kn, vn, slots)
+    gk, gv = dev_bits(pool0), dev_bits(pool0)
+    out = torch.full((T,), -7, dtype=torch.int32, device="cuda")
+    P.append_mapped(dev_bits(kn), dev_bits(vn), dev_i32(bt), dev_i32(cq), dev_i32(ck), gk, gv,
+                    page_size=ps, slot_mapping_out=out)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().astype(np.int64), slots)
+    assert np.array_equal(host_bits(gk), ok) and np.array_equal(host_bits(gv), ov)
+    # zero new tokens, and zero sequences: nothing is enqueued
+    P.append_mapped(dev_bits(kn[:0]), dev_bits(vn[:0]), dev_i32(bt), dev_i32(cq * 0),
+                    dev_i32(ck), gk, gv, page_size=ps)
+    P.append_mapped(dev_bits(kn[:0]), dev_bits(vn[:0]), dev_i32(bt[:0]), dev_i32(cq[:1]),
+                    dev_i32(ck[:1]), gk, gv, page_size=ps)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(gk), ok) and np.array_equal(host_bits(gv), ov)
+
+
 def test_append_large_pool(P):
     g = state("large_decode")
     wl = g.wl
