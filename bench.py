@@ -148,6 +148,7 @@ class Step:
         # this step's new rows and their addressing inputs
         self.k_new, self.v_new = bits(nk), bits(nv)
         self.T = nk.shape[0]
+        self.max_new = int(wl.new_lens.max())
         self.cu_new_q = i32(wl.cu_lens(wl.new_lens))
         self.cu_new_k = i32(wl.cu_lens(wl.total_lens))
         # decode
@@ -197,7 +198,8 @@ class Step:
         kernel / prefill kernel."""
         P, wl = self.P, self.wl
         P.append_mapped(self.k_new, self.v_new, self.bt, self.cu_new_q, self.cu_new_k,
-                        self.k_pool, self.v_pool, page_size=wl.page_size)
+                        self.k_pool, self.v_pool, page_size=wl.page_size,
+                        max_seqlen_q=self.max_new)
         for layer in range(wl.num_layers):
             qd, qp = self.q[layer]
             if self.B:

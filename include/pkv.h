@@ -129,21 +129,27 @@ pkv_status pkv_append(const uint16_t* k_new, const uint16_t* v_new,
  *
  *   k_new, v_new   bf16 [total_tokens, num_kv_heads, head_dim] (device, read)
  *   block_tables, cu_seq_lens_q, cu_seq_lens_k: as pkv_slot_mapping
+ *   max_seqlen_q   host bound on the new rows of any one sequence
+ *                  (Lq_j <= max_seqlen_q; 1 for a decode step); it sizes the
+ *                  grid, and rows of a sequence past it are not written
  *   k_pool, v_pool bf16 [num_kv_heads, num_pages*page_size, head_dim]
  *                  (device, written)
  *   slot_mapping   int32 [total_tokens] (device, written) or NULL; when given
- *                  it receives the same values pkv_slot_mapping writes
+ *                  it receives, for every written row, the value
+ *                  pkv_slot_mapping writes
  *
  * Tokens with slot -1 are skipped.  Two tokens with the same slot give an
- * unspecified row.  num_seqs or total_tokens may be 0 (nothing is enqueued).
+ * unspecified row.  num_seqs, total_tokens or max_seqlen_q may be 0
+ * (nothing is enqueued).  max_seqlen_q*num_kv_heads*head_dim/8 must stay
+ * below 2^31.
  */
 pkv_status pkv_append_mapped(const uint16_t* k_new, const uint16_t* v_new,
                              const int32_t* block_tables, int32_t max_pages_per_seq,
                              const int32_t* cu_seq_lens_q, const int32_t* cu_seq_lens_k,
-                             int32_t num_seqs, int32_t total_tokens, int32_t page_size,
-                             int32_t num_pages, int32_t num_kv_heads, int32_t head_dim,
-                             uint16_t* k_pool, uint16_t* v_pool, int32_t* slot_mapping,
-                             hipStream_t stream);
+                             int32_t num_seqs, int32_t total_tokens, int32_t max_seqlen_q,
+                             int32_t page_size, int32_t num_pages, int32_t num_kv_heads,
+                             int32_t head_dim, uint16_t* k_pool, uint16_t* v_pool,
+                             int32_t* slot_mapping, hipStream_t stream);
 
 /*
  * Split-K planning.  Split-K cuts each row's keys into num_splits

@@ -86,7 +86,7 @@ _SIGS = {
     "pkv_device_info": ([_P, _P], _I32),
     "pkv_slot_mapping": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "pkv_append": ([_P, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P], _I32),
-    "pkv_append_mapped": ([_P, _P, _P, _I32, _P, _P] + [_I32] * 6 + [_P, _P, _P, _P], _I32),
+    "pkv_append_mapped": ([_P, _P, _P, _I32, _P, _P] + [_I32] * 7 + [_P, _P, _P, _P], _I32),
     "pkv_decode_plan": ([_I32, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "pkv_decode_method": ([_I32] * 8 + [_P, _P], _I32),
     "pkv_decode_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
@@ -209,11 +209,13 @@ def append(k_new, v_new, slot_mapping, k_pool, v_pool, stream=None):
 
 
 def append_mapped(k_new, v_new, block_tables, cu_seq_lens_q, cu_seq_lens_k, k_pool, v_pool, *,
-                  page_size, slot_mapping_out=None, stream=None):
+                  page_size, max_seqlen_q=None, slot_mapping_out=None, stream=None):
     """Slot addressing and append in one launch (``pkv_append_mapped``).
 
-    ``k_pool``/``v_pool`` are ``[Hkv, num_pages * page_size, D]``; when
-    ``slot_mapping_out`` (int32 ``[T]``) is given it receives every token's slot.
+    ``k_pool``/``v_pool`` are ``[Hkv, num_pages * page_size, D]``;
+    ``max_seqlen_q`` bounds the new rows of any one sequence (default: the
+    token count, always a bound); when ``slot_mapping_out`` (int32 ``[T]``)
+    is given it receives every token's slot.
     """
     _bf16(k_new, "k_new"); _bf16(v_new, "v_new"); _bf16(k_pool, "k_pool"); _bf16(v_pool, "v_pool")
     _i32(block_tables, "block_tables"); _i32(cu_seq_lens_q, "cu_q"); _i32(cu_seq_lens_k, "cu_k")
@@ -230,7 +232,8 @@ def append_mapped(k_new, v_new, block_tables, cu_seq_lens_q, cu_seq_lens_k, k_po
         raise ValueError("slot_mapping_out is shorter than the token count")
     _check("pkv_append_mapped", lib().pkv_append_mapped(
         _ptr(k_new), _ptr(v_new), _ptr(block_tables), block_tables.shape[1],
-        _ptr(cu_seq_lens_q), _ptr(cu_seq_lens_k), cu_seq_lens_q.numel() - 1, T, page_size,
+        _ptr(cu_seq_lens_q), _ptr(cu_seq_lens_k), cu_seq_lens_q.numel() - 1, T,
+        T if max_seqlen_q is None else max_seqlen_q, page_size,
         k_pool.shape[1] // page_size, hkv, d, _ptr(k_pool), _ptr(v_pool),
         _ptr(slot_mapping_out), _stream(stream)))
 

@@ -136,24 +136,26 @@ pkv_status pkv_append(const uint16_t* k_new, const uint16_t* v_new, const int32_
 pkv_status pkv_append_mapped(const uint16_t* k_new, const uint16_t* v_new,
                              const int32_t* block_tables, int32_t max_pages_per_seq,
                              const int32_t* cu_seq_lens_q, const int32_t* cu_seq_lens_k,
-                             int32_t num_seqs, int32_t total_tokens, int32_t page_size,
-                             int32_t num_pages, int32_t num_kv_heads, int32_t head_dim,
-                             uint16_t* k_pool, uint16_t* v_pool, int32_t* slot_mapping,
-                             hipStream_t stream) {
-  if (num_seqs < 0 || total_tokens < 0 || max_pages_per_seq <= 0 || num_pages <= 0 ||
-      num_kv_heads <= 0 || page_size <= 0)
+                             int32_t num_seqs, int32_t total_tokens, int32_t max_seqlen_q,
+                             int32_t page_size, int32_t num_pages, int32_t num_kv_heads,
+                             int32_t head_dim, uint16_t* k_pool, uint16_t* v_pool,
+                             int32_t* slot_mapping, hipStream_t stream) {
+  if (num_seqs < 0 || total_tokens < 0 || max_seqlen_q < 0 || max_pages_per_seq <= 0 ||
+      num_pages <= 0 || num_kv_heads <= 0 || page_size <= 0)
     return PKV_ERR_BAD_SHAPE;
   if ((int64_t)num_pages * page_size > INT32_MAX) return PKV_ERR_BAD_SHAPE;
   if (!supported_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
-  if (num_seqs == 0 || total_tokens == 0) return PKV_OK;
+  // chunk indices of one sequence's rows stay below 2^31
+  if ((int64_t)max_seqlen_q * num_kv_heads * (head_dim / 8) > INT32_MAX) return PKV_ERR_BAD_SHAPE;
+  if (num_seqs == 0 || total_tokens == 0 || max_seqlen_q == 0) return PKV_OK;
+  if (num_seqs > INT32_MAX / 2) return PKV_ERR_BAD_SHAPE;
   if (!k_new || !v_new || !block_tables || !cu_seq_lens_q || !cu_seq_lens_k || !k_pool ||
       !v_pool)
     return PKV_ERR_NULL_ARG;
-  return hip_status(launch_append_mapped(k_new, v_new, block_tables, max_pages_per_seq,
-                                         cu_seq_lens_q, cu_seq_lens_k, num_seqs, total_tokens,
-                                         page_size, num_pages, num_kv_heads, head_dim, k_pool,
-                                         v_pool, (int64_t)num_pages * page_size, slot_mapping,
-                                         stream));
+  return hip_status(launch_append_mapped(
+      k_new, v_new, block_tables, max_pages_per_seq, cu_seq_lens_q, cu_seq_lens_k, num_seqs,
+      total_tokens, max_seqlen_q, page_size, num_pages, num_kv_heads, head_dim, k_pool, v_pool,
+      (int64_t)num_pages * page_size, slot_mapping, stream));
 }
 
 pkv_status pkv_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t page_size,

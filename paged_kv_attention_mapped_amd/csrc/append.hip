@@ -57,45 +57,69 @@ __global__ __launch_bounds__(256) void append_kernel(
   }
 }
 
-// Slot addressing and append in one launch: workgroup (j, y) walks the
-// (token, KV head, 16-byte chunk) triples of sequence j with stride
-// gridDim.y * blockDim.x, resolves each token's slot from the block table
-// (as slot_mapping_kernel) and copies the chunk (as append_kernel).
+// Slot addressing and append in one launch.  Workgroup (j, y) copies the
+// 16-byte chunks kAppendChunks*y .. kAppendChunks*(y+1)-1 of sequence j's new
+// rows (token-major, then KV head, then chunk), resolving each token's slot
+// from the block table as slot_mapping_kernel does and copying as
+// append_kernel does; the host sizes y from its bound on the rows per
+// sequence, so a long prompt gets many workgroups and a decode row one.
+#ifndef PKV_APPEND_PER_THREAD
+#define PKV_APPEND_PER_THREAD 2
+#endif
+constexpr int kAppendChunks = 256 * PKV_APPEND_PER_THREAD;  // chunks per workgroup
+
 __global__ __launch_bounds__(256) void append_mapped_kernel(
     const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
     const int32_t* __restrict__ bt, int max_pages, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ cu_k, int total, int page_size, int num_pages, int hkv,
-    int chunks_per_row, uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
-    int64_t num_slots, int32_t* __restrict__ slots_out) {
+    const int32_t* __restrict__ cu_k, int total, int max_q, int page_size, int num_pages,
+    unsigned per_token, unsigned chunks_per_row, uint4* __restrict__ k_pool,
+    uint4* __restrict__ v_pool, int64_t num_slots, int32_t* __restrict__ slots_out) {
+  constexpr int NC = kAppendChunks / 256;
   const int j = blockIdx.x;
-  const int q0 = cu_q[j], q1 = cu_q[j + 1];
+  const int q0 = cu_q[j];
+  const int lq = cu_q[j + 1] - q0;
   const int lk = cu_k[j + 1] - cu_k[j];
-  const int lq = q1 - q0;
-  const int64_t per_token = (int64_t)hkv * chunks_per_row;
-  const int64_t n = (int64_t)lq * per_token;
-  for (int64_t i = (int64_t)blockIdx.y * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.y * blockDim.x) {
-    const int r = (int)(i / per_token);
-    const int64_t rem = i - (int64_t)r * per_token;
-    const int t = q0 + r;
-    if (t < 0 || t >= total) continue;
-    const int pos = lk - lq + r;
-    int64_t slot = -1;
-    if (pos >= 0) {
-      const int lp = pos / page_size;
-      if (lp < max_pages) {
-        const int phys = bt[(int64_t)j * max_pages + lp];
+  const int rows = min(lq, max_q);  // rows past the host bound are not written
+  if (rows <= 0) return;
+  const unsigned n = (unsigned)rows * per_token;  // < 2^31 (checked on the host)
+  for (unsigned base = blockIdx.y * (unsigned)kAppendChunks; base < n;
+       base += gridDim.y * (unsigned)kAppendChunks) {
+    int64_t src[NC], dst[NC];
+    bool ok[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const unsigned k = base + c * 256u + threadIdx.x;
+      const unsigned r = k / per_token;
+      const unsigned rem = k - r * per_token;
+      const int t = q0 + (int)r;
+      const int pos = lk - lq + (int)r;
+      int64_t slot = -1;
+      if (k < n && pos >= 0 && pos / page_size < max_pages) {
+        const int phys = bt[(int64_t)j * max_pages + pos / page_size];
         if (phys >= 0 && phys < num_pages) slot = (int64_t)phys * page_size + pos % page_size;
       }
+      const bool tok_ok = k < n && t >= 0 && t < total;
+      if (slots_out != nullptr && tok_ok && rem == 0) slots_out[t] = (int32_t)slot;
+      ok[c] = tok_ok && slot >= 0 && slot < num_slots;
+      const unsigned h = rem / chunks_per_row;
+      src[c] = (int64_t)t * per_token + rem;
+      dst[c] = ((int64_t)h * num_slots + slot) * chunks_per_row + (rem - h * chunks_per_row);
     }
-    if (slots_out != nullptr && rem == 0) slots_out[t] = (int32_t)slot;
-    if (slot < 0 || slot >= num_slots) continue;
-    const int64_t h = rem / chunks_per_row;
-    const int64_t c = rem - h * chunks_per_row;
-    const int64_t src = (int64_t)t * per_token + rem;
-    const int64_t dst = (h * num_slots + slot) * chunks_per_row + c;
-    k_pool[dst] = k_new[src];
-    v_pool[dst] = v_new[src];
+    // all loads before the first store; a skipped chunk reads row 0 (the
+    // token count is > 0 here) so that the arrays stay in registers
+    uint4 kv[NC], vv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int64_t sc = ok[c] ? src[c] : 0;
+      kv[c] = k_new[sc];
+      vv[c] = v_new[sc];
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      if (ok[c]) {
+        k_pool[dst[c]] = kv[c];
+        v_pool[dst[c]] = vv[c];
+      }
   }
 }
 
@@ -103,18 +127,16 @@ __global__ __launch_bounds__(256) void append_mapped_kernel(
 
 hipError_t launch_append_mapped(const uint16_t* k_new, const uint16_t* v_new, const int32_t* bt,
                                 int max_pages, const int32_t* cu_q, const int32_t* cu_k,
-                                int num_seqs, int total, int page_size, int num_pages, int hkv,
-                                int d, uint16_t* k_pool, uint16_t* v_pool, int64_t num_slots,
-                                int32_t* slots_out, hipStream_t st) {
-  // enough workgroups per sequence for an even share of the chunks, at
-  // least one, at most 64 (the host does not know the per-sequence split)
-  const int cpr = d / 8;
-  const int64_t chunks = (int64_t)total * hkv * cpr;
-  int64_t y = (chunks / (num_seqs > 0 ? num_seqs : 1) + 2047) / 2048;
-  y = y < 1 ? 1 : (y > 64 ? 64 : y);
+                                int num_seqs, int total, int max_q, int page_size, int num_pages,
+                                int hkv, int d, uint16_t* k_pool, uint16_t* v_pool,
+                                int64_t num_slots, int32_t* slots_out, hipStream_t st) {
+  const unsigned cpr = (unsigned)d / 8;
+  const unsigned per_token = (unsigned)hkv * cpr;
+  int64_t y = ((int64_t)max_q * per_token + kAppendChunks - 1) / kAppendChunks;
+  if (y > 65535) y = 65535;  // workgroups stride over the rest
   hipLaunchKernelGGL(append_mapped_kernel, dim3(num_seqs, (unsigned)y), dim3(256), 0, st,
                      reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new),
-                     bt, max_pages, cu_q, cu_k, total, page_size, num_pages, hkv, cpr,
+                     bt, max_pages, cu_q, cu_k, total, max_q, page_size, num_pages, per_token, cpr,
                      reinterpret_cast<uint4*>(k_pool), reinterpret_cast<uint4*>(v_pool), num_slots,
                      slots_out);
   return hipGetLastError();

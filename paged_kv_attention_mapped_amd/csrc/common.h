@@ -119,9 +119,9 @@ hipError_t launch_slot_mapping(const int32_t* bt, int max_pages, const int32_t* 
                                int num_pages, int32_t* slots, hipStream_t st);
 hipError_t launch_append_mapped(const uint16_t* k_new, const uint16_t* v_new, const int32_t* bt,
                                 int max_pages, const int32_t* cu_q, const int32_t* cu_k,
-                                int num_seqs, int total, int page_size, int num_pages, int hkv,
-                                int d, uint16_t* k_pool, uint16_t* v_pool, int64_t num_slots,
-                                int32_t* slots_out, hipStream_t st);
+                                int num_seqs, int total, int max_q, int page_size, int num_pages,
+                                int hkv, int d, uint16_t* k_pool, uint16_t* v_pool,
+                                int64_t num_slots, int32_t* slots_out, hipStream_t st);
 hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* slots,
                          int num_tokens, int hkv, int d, uint16_t* k_pool, uint16_t* v_pool,
                          int64_t num_slots, hipStream_t st);

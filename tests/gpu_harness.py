@@ -80,7 +80,8 @@ class GpuPools:
                     (k.shape[0],), -7, dtype=torch.int32, device="cuda")
                 P.append_mapped(dev_bits(k), dev_bits(v), dev_i32(wl.block_tables[sub]),
                                 dev_i32(wl.cu_lens(lq)), dev_i32(wl.cu_lens(lk)), self.k, self.v,
-                                page_size=wl.page_size, slot_mapping_out=out)
+                                page_size=wl.page_size, max_seqlen_q=int(lq.max()),
+                                slot_mapping_out=out)
                 if slots_log is not None:
                     slots_log.append((sub, wl.cu_lens(lq), wl.cu_lens(lk), out))
                 continue

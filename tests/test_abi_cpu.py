@@ -137,20 +137,26 @@ def test_device_info_rejects_null(P):
 
 def test_append_mapped_validation(P):
     f = P.lib().pkv_append_mapped
-    args = [FAKE, FAKE, FAKE, 4, FAKE, FAKE, 2, 5, 32, 10, 2, 128, FAKE, FAKE, None, None]
+    args = [FAKE, FAKE, FAKE, 4, FAKE, FAKE, 2, 5, 3, 32, 10, 2, 128, FAKE, FAKE, None, None]
     a = list(args); a[0] = None
     assert f(*a) == 1
     a = list(args); a[2] = None
     assert f(*a) == 1
-    a = list(args); a[11] = 96
+    a = list(args); a[12] = 96
     assert f(*a) == 3
     a = list(args); a[3] = 0
     assert f(*a) == 2
-    a = list(args); a[9] = 0
+    a = list(args); a[10] = 0
     assert f(*a) == 2
-    a = list(args); a[8] = 1 << 20; a[9] = 1 << 12   # pool of 2^32 slots does not fit int32
+    a = list(args); a[8] = -1
+    assert f(*a) == 2
+    a = list(args); a[9] = 1 << 20; a[10] = 1 << 12  # pool of 2^32 slots does not fit int32
+    assert f(*a) == 2
+    a = list(args); a[8] = 1 << 26                   # 2^26 rows x 32 chunks >= 2^31
     assert f(*a) == 2
     a = list(args); a[7] = 0; a[0] = None            # no tokens: nothing to check or enqueue
+    assert f(*a) == 0
+    a = list(args); a[8] = 0; a[0] = None            # no rows per sequence
     assert f(*a) == 0
     a = list(args); a[6] = 0
     assert f(*a) == 0

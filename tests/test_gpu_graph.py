@@ -62,7 +62,7 @@ class DecodeBuffers:
         P, b = self.P, bucket
         ws = self.ws if ws is None else ws
         P.append_mapped(self.k_new[:b], self.v_new[:b], self.bt[:b], self.cu_q[:b + 1],
-                        self.cu_k[:b + 1], k_pool, v_pool, page_size=self.ps)
+                        self.cu_k[:b + 1], k_pool, v_pool, page_size=self.ps, max_seqlen_q=1)
         P.decode_stream(self.q[:b], k_pool, v_pool, self.bt[:b], self.seq_lens[:b],
                         page_size=self.ps, num_waves=self.waves[b], window=self.window,
                         workspace=ws, out=out[:b])

@@ -137,10 +137,21 @@ def test_append_mapped_edge_cases(P):
     gk, gv = dev_bits(pool0), dev_bits(pool0)
     out = torch.full((T,), -7, dtype=torch.int32, device="cuda")
     P.append_mapped(dev_bits(kn), dev_bits(vn), dev_i32(bt), dev_i32(cq), dev_i32(ck), gk, gv,
-                    page_size=ps, slot_mapping_out=out)
+                    page_size=ps, max_seqlen_q=20, slot_mapping_out=out)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().astype(np.int64), slots)
     assert np.array_equal(host_bits(gk), ok) and np.array_equal(host_bits(gv), ov)
+    # a host bound below a sequence's row count: only its first rows are written
+    rows = np.concatenate([np.arange(n) < 7 for n in lq])
+    k7, v7 = oracle.append(pool0, pool0, kn, vn, np.where(rows, slots, -1))
+    hk, hv = dev_bits(pool0), dev_bits(pool0)
+    out.fill_(-7)
+    P.append_mapped(dev_bits(kn), dev_bits(vn), dev_i32(bt), dev_i32(cq), dev_i32(ck), hk, hv,
+                    page_size=ps, max_seqlen_q=7, slot_mapping_out=out)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(hk), k7) and np.array_equal(host_bits(hv), v7)
+    assert np.array_equal(out.cpu().numpy()[rows].astype(np.int64), slots[rows])
+    assert np.all(out.cpu().numpy()[~rows] == -7)
     # zero new tokens, and zero sequences: nothing is enqueued
     P.append_mapped(dev_bits(kn[:0]), dev_bits(vn[:0]), dev_i32(bt), dev_i32(cq * 0),
                     dev_i32(ck), gk, gv, page_size=ps)
