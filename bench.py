@@ -118,7 +118,7 @@ def prefill_bytes(wl) -> int:
 # the step on the GPU
 # ---------------------------------------------------------------------------
 class Step:
-    def __init__(self, wl, torch, P, num_splits=0):
+    def __init__(self, wl, torch, P, num_splits=0, mixed="single"):
         self.wl, self.torch, self.P = wl, torch, P
         dev = torch.device("cuda")
         i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)  # noqa: E731
@@ -192,6 +192,13 @@ class Step:
         for layer in range(wl.num_layers):
             qd, qp = wl.queries(layer)
             self.q.append((bits(qd), bits(qp)))
+        # mixed steps in one varlen launch: decode rows are one-row sequences
+        self.single = mixed == "single" and self.B > 0 and self.N > 0
+        if self.single:
+            self.q_all = [bits(np.concatenate(wl.queries(layer))) for layer in range(wl.num_layers)]
+            self.out_all = torch.empty((self.B + wl.total_q(), wl.num_q_heads, wl.head_dim),
+                                       dtype=torch.bfloat16, device=dev)
+            self.max_k_all = int(wl.total_lens.max())
 
     def run(self, ev=None, pev=None):
         """One step.  ``ev`` / ``pev`` = (before, after) events bracketing the layer-0 decode
@@ -200,6 +207,17 @@ class Step:
         P.append_mapped(self.k_new, self.v_new, self.bt, self.cu_new_q, self.cu_new_k,
                         self.k_pool, self.v_pool, page_size=wl.page_size,
                         max_seqlen_q=self.max_new)
+        if self.single:
+            for layer in range(wl.num_layers):
+                if ev is not None and layer == 0:
+                    ev[0].record()
+                P.prefill_varlen(self.q_all[layer], self.k_pool, self.v_pool, self.bt,
+                                 self.cu_new_q, self.cu_new_k, self.max_new, self.max_k_all,
+                                 page_size=wl.page_size, scale=wl.scale, window=wl.window,
+                                 out=self.out_all)
+                if ev is not None and layer == 0:
+                    ev[1].record()
+            return
         for layer in range(wl.num_layers):
             qd, qp = self.q[layer]
             if self.B:
@@ -406,6 +424,9 @@ def main():
     ap.add_argument("--config", default="large_decode", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--num-splits", type=int, default=0,
                     help="0: automatic decomposition (stream-K); >= 1: split-K with that many splits")
+    ap.add_argument("--mixed", choices=["single", "separate"], default="single",
+                    help="a step with decode rows and prefill rows: one varlen launch per layer "
+                         "(decode rows as one-row sequences) or decode + prefill launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the long-prefill MFMA measurement")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
@@ -453,7 +474,7 @@ def main():
     wl = W.make(args.config)
     _log(f"[bench] setting up {args.config}: {DESCRIPTIONS[args.config]}")
     t0 = time.perf_counter()
-    st = Step(wl, torch, P, args.num_splits)
+    st = Step(wl, torch, P, args.num_splits, args.mixed)
     _log(f"[bench] set-up done in {time.perf_counter() - t0:.1f} s; warmup {args.warmup}, steps {args.steps}")
 
     for _ in range(args.warmup):
@@ -477,7 +498,7 @@ def main():
         if scrub:
             scratch.fill_(i & 0xff)
         sevs[i][0].record()
-        st.run(evs[i] if st.B else None, pevs[i] if st.N else None)
+        st.run(evs[i] if st.B else None, pevs[i] if st.N and not st.single else None)
         sevs[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -495,8 +516,9 @@ def main():
         # the same step captured once on a side stream and replayed; the new
         # rows go to the same slots every step, so every replay's output must
         # equal the eager step's bit for bit
-        ref_out = st.out_dec.clone() if st.B else None
-        ref_pre = st.out_pre.clone() if st.N else None
+        outs = [st.out_all] if st.single else (
+            ([st.out_dec] if st.B else []) + ([st.out_pre] if st.N else []))
+        refs = [t.clone() for t in outs]
         gs = torch.cuda.Stream()
         gs.wait_stream(torch.cuda.current_stream())
         graph = P.capture_graph(st.run, gs)
@@ -516,8 +538,7 @@ def main():
         gwall = time.perf_counter() - t0
         g_ms = np.array([a.elapsed_time(b) for a, b in gsevs])
         g_step = float(g_ms.mean()) if scrub else gwall / args.steps * 1e3
-        same = ((not st.B or bool(torch.equal(st.out_dec, ref_out))) and
-                (not st.N or bool(torch.equal(st.out_pre, ref_pre))))
+        same = all(bool(torch.equal(t, r)) for t, r in zip(outs, refs))
         kn, on = graph.nodes()
         graph.destroy()
         _log(f"[bench] graph replay: {g_step:.4f} ms/step (eager {ms_step:.4f}); "
@@ -554,7 +575,22 @@ def main():
         "step_graph": graph_info or {"used": False},
         "eager": eager,
     }
-    if st.B:
+    if st.single:
+        # one varlen launch per layer carries the decode rows and the prompts
+        kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        kb = decode_kernel_bytes(wl) + prefill_bytes(wl)
+        fl = prefill_flops(wl)
+        ach = kb / (kern_ms * 1e-3) / 1e9
+        out["decode_tokens_per_s"] = round(st.B / (ms_step * 1e-3), 1)
+        out["decode_plan"] = {"method": "single varlen launch (decode rows as one-row sequences)"}
+        out["roofline"] = {
+            "kernel": "prefill_kernel (decode rows + prefill rows in one launch)",
+            "bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+            "avg_kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": kb,
+            "prefill_tflops": round(fl / (kern_ms * 1e-3) / 1e12, 2),
+        }
+    elif st.B:
         kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
         kb = decode_kernel_bytes(wl)
         ach = kb / (kern_ms * 1e-3) / 1e9
@@ -574,7 +610,7 @@ def main():
             "avg_kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": kb,
             "kernel_source_sha256_16": src_hash,
         }
-    if st.N:
+    if st.N and not st.single:
         pk_ms = float(np.mean([a.elapsed_time(b) for a, b in pevs]))
         fl = prefill_flops(wl)
         tf = fl / (pk_ms * 1e-3) / 1e12

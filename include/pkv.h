@@ -319,6 +319,13 @@ pkv_status pkv_decode_stream_merge(const void* workspace, size_t workspace_bytes
  *   out            bf16 [total_q, num_q_heads, head_dim]        (device, written)
  *
  * Caller contract: 0 <= Lq_j <= Lk_j <= max_pages_per_seq*page_size.
+ *
+ * Decode rows may be packed into the same call as one-row sequences
+ * (Lq_j = 1, position Lk_j - 1): such a sequence is attended with the
+ * decode machinery (its pages split over the workgroup's waves) rather than
+ * with 32-row MFMA tiles, so a step mixing decode rows and prompts is one
+ * launch per layer (the CB paged kernel likewise takes the whole mixed
+ * batch through cu_seq_lens_q on every forward).
  */
 pkv_status pkv_prefill_varlen(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
                               const int32_t* block_tables, int32_t max_pages_per_seq,

@@ -45,6 +45,7 @@
 #include <math.h>
 
 #include "common.h"
+#include "decode_core.h"
 #include "prefill_common.h"
 
 namespace pkv {
@@ -85,6 +86,98 @@ struct PrefillCfg {
   static_assert(QB >= 1, "more heads than waves");
 };
 
+// A sequence with a single query row (a decode row packed into the varlen
+// batch, or a one-token prompt): the workgroup's NW waves take the allowed
+// pages round-robin with the decode machinery of decode_core.h (K on MFMA
+// as the A operand, the HW heads as columns, PV on the vector ALUs) and
+// merge their softmax states through LDS, instead of running 32-row MFMA
+// tiles for one row.  A mixed batch of decode rows and prompts is thereby
+// one launch.
+template <int D, int PS, int HW, int NW>
+__device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, int head0,
+                                           int q_row, int L, float* sm) {
+  constexpr int G = HW < 2 ? 2 : HW;
+  using W = WaveDecoder<D, PS, G, 16>;
+  float* sm_m = sm;                 // [NW][G]
+  float* sm_l = sm + NW * G;        // [NW][G]
+  float* sm_acc = sm + 2 * NW * G;  // [NW][G][D]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  W wd;
+  wd.init(lane);
+  wd.reset();
+  wd.load_q(a.q + ((int64_t)q_row * a.num_q_heads + head0) * D, HW);
+
+  const int first_key = a.window > 0 ? max(0, L - a.window) : 0;
+  const int p0 = first_key / PS;
+  const int pend = (L + PS - 1) / PS;
+  const uint16_t* kh = a.k_pool + (int64_t)hk * a.head_stride;
+  const uint16_t* vh = a.v_pool + (int64_t)hk * a.head_stride;
+  const int32_t* bt_row = a.block_tables + (int64_t)j * a.max_pages;
+  // this wave's pages: p0 + w, p0 + w + NW, ...; table entries 64 at a time
+  const int npw = pend - p0 > w ? (pend - p0 - w + NW - 1) / NW : 0;
+  const int nsteps = npw * W::UPP;
+  int phys_lane = 0;
+  int tok_of[2] = {0, 0};
+  bool ok_of[2] = {false, false};
+  auto load = [&](typename W::Buf& bf, int i_step, int slot) {
+    const int i = i_step / W::UPP, part = i_step - i * W::UPP;
+    if ((i & 63) == 0 && part == 0)
+      phys_lane = (i + lane < npw) ? bt_row[p0 + w + NW * (i + lane)] : -1;
+    int phys = __builtin_amdgcn_readlane(phys_lane, i & 63);
+    ok_of[slot] = phys >= 0 && phys < a.num_pages;
+    phys = ok_of[slot] ? phys : 0;  // an unusable entry reads page 0 and is masked out
+    tok_of[slot] = (p0 + w + NW * i) * PS + part * W::UT;
+    const int64_t row = (int64_t)phys * PS + part * W::UT;
+    wd.load(bf, kh + row * D, vh + row * D);
+  };
+  auto process = [&](const typename W::Buf& bf, int slot) {
+    wd.process(bf, tok_of[slot], ok_of[slot] ? first_key : INT_MAX, L, a.scale_log2);
+  };
+  typename W::Buf b0, b1;
+  if (nsteps > 0) load(b0, 0, 0);
+  for (int i = 0; i < nsteps; i += 2) {
+    if (i + 1 < nsteps) load(b1, i + 1, 1);
+    process(b0, 0);
+    if (i + 1 >= nsteps) break;
+    if (i + 2 < nsteps) load(b0, i + 2, 0);
+    process(b1, 1);
+  }
+
+  float M, lw;
+  wd.merge_rows(M, lw);
+  if (wd.jj == 0) {
+    if (wd.n < G) {
+      sm_m[w * G + wd.n] = M;
+      sm_l[w * G + wd.n] = lw;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < W::EPL; ++e) sm_acc[(w * G + h) * D + wd.dim_of(e)] = wd.acc[h][e];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < HW * D; idx += 64 * NW) {
+    const int h = idx / D, d = idx - h * D;
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) Mx = fmaxf(Mx, sm_m[ww * G + h]);
+    float o = 0.f, lsum = 0.f;
+    if (Mx != -INFINITY) {
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float mw = sm_m[ww * G + h];
+        if (mw == -INFINITY) continue;
+        const float wt = fast_exp2(mw - Mx);
+        o = fmaf(wt, sm_acc[(ww * G + h) * D + d], o);
+        lsum = fmaf(wt, sm_l[ww * G + h], lsum);
+      }
+    }
+    const float val = lsum > 0.f ? o / lsum : 0.f;
+    a.out[((int64_t)q_row * a.num_q_heads + head0 + h) * D + d] = (uint16_t)f32_to_bf16(val);
+  }
+}
+
 template <int D, int PS, int HW>
 __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(PrefillArgs a, int nqb) {
   using C = PrefillCfg<D, HW>;
@@ -92,7 +185,8 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   // grid: x = (KV head, head group), y = sequence, z = query block counted
-  // from the end, so the longest (latest) blocks of every sequence go first
+  // from the end, so the longest (latest) blocks of every sequence go first;
+  // a one-row sequence runs in the z = 0 block, among the first dispatched
   const int HG = a.group / HW;  // workgroups per KV head along the heads
   const int j = blockIdx.y;
   const int hk = blockIdx.x / HG;
@@ -103,6 +197,12 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   const int Lq = a.cu_q[j + 1] - q_start;
   int Lk = a.cu_k[j + 1] - a.cu_k[j];
   Lk = min(Lk, a.max_pages * PS);
+  if (Lq == 1) {
+    if (blockIdx.z == 0)
+      decode_row<D, PS, HW, C::NW>(a, j, hk, hk * a.group + hg * HW, q_start, Lk,
+                                   reinterpret_cast<float*>(smem));
+    return;
+  }
   const int q0 = qb * C::BM;
   if (q0 >= Lq) return;
 

@@ -298,6 +298,38 @@ def test_decode_shapes(P, shape):
     P.decode_stream_merge(ws, out, num_waves=5, num_kv_heads=wl.num_kv_heads)
     torch.cuda.synchronize()
     check_close(host_bits(out), ref, f"{name} decode, 5 waves")
+    # the same rows as one-row sequences of a varlen batch (single-row path)
+    lq = np.ones(wl.n_decode, np.int32)
+    out = P.prefill_varlen(dev_bits(qd), g.k, g.v, dev_i32(wl.block_tables[:wl.n_decode]),
+                           dev_i32(wl.cu_lens(lq)), dev_i32(wl.cu_lens(lens)), 1, int(lens.max()),
+                           page_size=wl.page_size, scale=wl.scale, window=wl.window)
+    torch.cuda.synchronize()
+    check_close(host_bits(out), ref, f"{name} decode rows through the varlen entry")
+
+
+@pytest.mark.parametrize("name", ["mixed_step", "window_shared"])
+def test_mixed_single_launch(P, name):
+    """Decode rows (one row each) and prompts/chunks in one varlen launch."""
+    g = state(name)
+    wl = g.wl
+    o = OraclePools(wl)
+    cq, ck = wl.cu_lens(wl.new_lens), wl.cu_lens(wl.total_lens)
+    for layer in range(wl.num_layers):
+        qd, qp = wl.queries(layer)
+        q = np.concatenate([qd, qp])   # sequence order: decoders, then prefill sequences
+        say(f"[mixed] {name} layer {layer}: {wl.n_decode} decode rows + {qp.shape[0]} prefill rows")
+        out = P.prefill_varlen(dev_bits(q), g.k, g.v, dev_i32(wl.block_tables), dev_i32(cq),
+                               dev_i32(ck), int(wl.new_lens.max()), int(wl.total_lens.max()),
+                               page_size=wl.page_size, scale=wl.scale, window=wl.window)
+        torch.cuda.synchronize()
+        got = host_bits(out)
+        ref = oracle.prefill_varlen(q, o.k, o.v, wl.block_tables, cq, ck, wl.page_size, wl.scale,
+                                    wl.window)
+        check_close(got, ref, f"{name} L{layer} single launch")
+        # the decode rows agree with the decode entry's result within the same bar
+        refd = oracle.decode(qd, o.k, o.v, wl.block_tables[:wl.n_decode], wl.decode_seq_lens(),
+                             wl.page_size, wl.scale, wl.window)
+        check_close(got[:wl.n_decode], refd, f"{name} L{layer} decode rows")
 
 
 @pytest.mark.parametrize("name", ["qwen3_decode", "window_shared"])
