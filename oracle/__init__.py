@@ -18,3 +18,11 @@ from .reference import (  # noqa: F401
     slot_mapping,
     split_page_range,
 )
+from .allocator import (  # noqa: F401
+    ALLOC_OK,
+    ALLOC_OUT_OF_PAGES,
+    ALLOC_TABLE_FULL,
+    FREE_OVERFLOW,
+    page_alloc,
+    page_free,
+)
