@@ -416,6 +416,50 @@ def prefill_measure(torch, P, iters=20, warmup=5):
             "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4), "flops_per_call": fl}
 
 
+def alloc_measure(torch, P, num_seqs=256, iters=200):
+    """Device page allocator: 256 fresh sequences of 1..128 tokens take their
+    pages (1..4 of 32 tokens each) from a 32768-page stack and release them
+    again; ``iters`` alloc + release pairs run back to back inside step
+    graphs between two HIP events."""
+    dev = "cuda"
+    ps, width, num_pages = 32, 256, 32768
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)  # noqa: E731
+    rng = np.random.default_rng(11)
+    lens = rng.integers(1, 4 * ps, num_seqs, endpoint=True)
+    cu = i32(np.concatenate([[0], np.cumsum(lens)]))
+    d_lens, rel = i32(lens), i32(np.ones(num_seqs, np.int32))
+    d_bt = i32(np.full((num_seqs, width), -1, np.int32))
+    d_free = i32(rng.permutation(num_pages))
+    d_count, d_status = i32([num_pages]), i32([0])
+
+    def pair():
+        P.page_alloc(cu, cu, d_bt, d_free, d_count, page_size=ps, status=d_status)
+        P.page_free(d_lens, rel, d_bt, d_free, d_count, page_size=ps, status=d_status)
+    for _ in range(5):
+        pair()
+    # 20 pairs captured in one step graph and replayed, so the figure is the
+    # GPU's (kernels and the gaps between them), not the Python loop's
+    per_graph = 20
+    gs = torch.cuda.Stream()
+    gs.wait_stream(torch.cuda.current_stream())
+    graph = P.capture_graph(lambda: [pair() for _ in range(per_graph)], gs)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(gs):
+        graph.launch(gs)
+        a.record()
+        for _ in range(iters // per_graph):
+            graph.launch(gs)
+        b.record()
+    torch.cuda.synchronize()
+    graph.destroy()
+    iters = (iters // per_graph) * per_graph
+    ok = int(d_status.item()) == 0 and int(d_count.item()) == num_pages
+    return {"num_seqs": num_seqs, "pages_per_alloc": int(np.sum(-(-lens // ps))),
+            "alloc_plus_free_us": round(a.elapsed_time(b) * 1e3 / iters, 2),
+            "state_ok": bool(ok),
+            "note": "one workgroup each; latency-bound (a scan over the batch, a few KB moved)"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -631,6 +675,7 @@ def main():
     if scratch is not None:
         del scratch
         torch.cuda.empty_cache()
+    out["page_allocator"] = alloc_measure(torch, P)
     out["hbm_copy_ceiling_gbs"] = copy_ceiling(torch)
     if not args.no_cpu_baseline:
         _log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s)")

@@ -152,6 +152,51 @@ pkv_status pkv_append_mapped(const uint16_t* k_new, const uint16_t* v_new,
                              int32_t* slot_mapping, hipStream_t stream);
 
 /*
+ * Device page allocator.  The pool is one set of pages and each sequence's
+ * block-table row maps its logical pages to physical ones; pages are handed
+ * out as sequences grow (commit log 1847125, flex_attention paged-KV engine
+ * entry, "Why this works" item 1 and "Files").  The free pages are a stack
+ * in device memory, free_pages[0 .. *free_count) with its top at
+ * free_pages[*free_count - 1]; both calls run on the device (one
+ * workgroup), read no host state and so can be captured in a step graph
+ * ahead of the append and the attention that read the tables.
+ *
+ * pkv_page_alloc: sequence j, with Lq_j new and Lk_j total tokens (the
+ * cu_seq_lens convention of pkv_slot_mapping), holds ceil((Lk_j-Lq_j)/
+ * page_size) pages and needs ceil(Lk_j/page_size); its missing logical
+ * pages, in increasing order, each take the page at the top of the stack,
+ * sequences served in batch order.  All or nothing: if some row needs more
+ * than max_pages_per_seq entries (*status = 1) or the stack holds fewer
+ * pages than the batch needs (*status = 2), nothing is written but status.
+ * On success *free_count drops by the pages taken and *status = 0.
+ *
+ * pkv_page_free: every sequence j with release[j] != 0 pushes its first
+ * ceil(seq_lens[j]/page_size) table entries onto the stack (sequences in
+ * batch order, logical order) and sets them to -1.  If the stack would
+ * exceed num_pages entries, nothing is written but *status = 3.
+ *
+ *   cu_seq_lens_q/k int32 [num_seqs+1]; seq_lens, release int32 [num_seqs]
+ *                   (device, read)
+ *   block_tables    int32 [num_seqs, max_pages_per_seq] (device, read/written)
+ *   free_pages      int32 [num_pages] (device; read by alloc, written by free)
+ *   free_count      int32 [1] (device, read and written)
+ *   status          int32 [1] (device, written) or NULL
+ *
+ * num_seqs = 0 enqueues nothing.  The stack's contents are the caller's
+ * contract (page numbers in [0, num_pages), each page either free or owned
+ * by one table row); *free_count is clamped to [0, num_pages] when read.
+ * Calls that overlap on one stack race: keep them on one stream.
+ */
+pkv_status pkv_page_alloc(const int32_t* cu_seq_lens_q, const int32_t* cu_seq_lens_k,
+                          int32_t num_seqs, int32_t* block_tables, int32_t max_pages_per_seq,
+                          int32_t page_size, int32_t* free_pages, int32_t* free_count,
+                          int32_t num_pages, int32_t* status, hipStream_t stream);
+pkv_status pkv_page_free(const int32_t* seq_lens, const int32_t* release, int32_t num_seqs,
+                         int32_t* block_tables, int32_t max_pages_per_seq, int32_t page_size,
+                         int32_t* free_pages, int32_t* free_count, int32_t num_pages,
+                         int32_t* status, hipStream_t stream);
+
+/*
  * Split-K planning.  Split-K cuts each row's keys into num_splits
  * partitions of pages_per_split logical pages (flash-decoding); the plan
  * depends only on host scalars.  num_splits_requested = 0 picks a count from

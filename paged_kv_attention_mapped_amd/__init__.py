@@ -36,6 +36,8 @@ __all__ = [
     "exported_symbols",
     "lib",
     "lib_path",
+    "page_alloc",
+    "page_free",
     "prefill_varlen",
     "slot_mapping",
 ]
@@ -49,6 +51,8 @@ EXPORTS = (
     "pkv_slot_mapping",
     "pkv_append",
     "pkv_append_mapped",
+    "pkv_page_alloc",
+    "pkv_page_free",
     "pkv_decode_plan",
     "pkv_decode_method",
     "pkv_decode_workspace_bytes",
@@ -87,6 +91,8 @@ _SIGS = {
     "pkv_slot_mapping": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "pkv_append": ([_P, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P], _I32),
     "pkv_append_mapped": ([_P, _P, _P, _I32, _P, _P] + [_I32] * 7 + [_P, _P, _P, _P], _I32),
+    "pkv_page_alloc": ([_P, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _P], _I32),
+    "pkv_page_free": ([_P, _P, _I32, _P, _I32, _I32, _P, _P, _I32, _P, _P], _I32),
     "pkv_decode_plan": ([_I32, _I32, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "pkv_decode_method": ([_I32] * 8 + [_P, _P], _I32),
     "pkv_decode_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
@@ -236,6 +242,40 @@ def append_mapped(k_new, v_new, block_tables, cu_seq_lens_q, cu_seq_lens_k, k_po
         T if max_seqlen_q is None else max_seqlen_q, page_size,
         k_pool.shape[1] // page_size, hkv, d, _ptr(k_pool), _ptr(v_pool),
         _ptr(slot_mapping_out), _stream(stream)))
+
+
+def page_alloc(cu_seq_lens_q, cu_seq_lens_k, block_tables, free_pages, free_count, *,
+               page_size, status=None, stream=None):
+    """Pages for every sequence's new tokens from the device free stack (``pkv_page_alloc``).
+
+    ``block_tables`` int32 ``[B, max_pages]``, ``free_pages`` int32 ``[num_pages]``
+    and ``free_count`` / ``status`` int32 ``[1]`` are device tensors updated in place.
+    """
+    for t, n in ((cu_seq_lens_q, "cu_q"), (cu_seq_lens_k, "cu_k"), (block_tables, "block_tables"),
+                 (free_pages, "free_pages"), (free_count, "free_count")):
+        _i32(t, n)
+    if status is not None:
+        _i32(status, "status")
+    _dev(cu_seq_lens_q, cu_seq_lens_k, block_tables, free_pages, free_count, status)
+    _check("pkv_page_alloc", lib().pkv_page_alloc(
+        _ptr(cu_seq_lens_q), _ptr(cu_seq_lens_k), cu_seq_lens_q.numel() - 1, _ptr(block_tables),
+        block_tables.shape[1], page_size, _ptr(free_pages), _ptr(free_count), free_pages.numel(),
+        _ptr(status), _stream(stream)))
+
+
+def page_free(seq_lens, release, block_tables, free_pages, free_count, *, page_size,
+              status=None, stream=None):
+    """Return the pages of released sequences to the device free stack (``pkv_page_free``)."""
+    for t, n in ((seq_lens, "seq_lens"), (release, "release"), (block_tables, "block_tables"),
+                 (free_pages, "free_pages"), (free_count, "free_count")):
+        _i32(t, n)
+    if status is not None:
+        _i32(status, "status")
+    _dev(seq_lens, release, block_tables, free_pages, free_count, status)
+    _check("pkv_page_free", lib().pkv_page_free(
+        _ptr(seq_lens), _ptr(release), seq_lens.numel(), _ptr(block_tables),
+        block_tables.shape[1], page_size, _ptr(free_pages), _ptr(free_count), free_pages.numel(),
+        _ptr(status), _stream(stream)))
 
 
 def device_info():

@@ -158,6 +158,34 @@ pkv_status pkv_append_mapped(const uint16_t* k_new, const uint16_t* v_new,
       (int64_t)num_pages * page_size, slot_mapping, stream));
 }
 
+pkv_status pkv_page_alloc(const int32_t* cu_seq_lens_q, const int32_t* cu_seq_lens_k,
+                          int32_t num_seqs, int32_t* block_tables, int32_t max_pages_per_seq,
+                          int32_t page_size, int32_t* free_pages, int32_t* free_count,
+                          int32_t num_pages, int32_t* status, hipStream_t stream) {
+  if (num_seqs < 0 || max_pages_per_seq <= 0 || page_size <= 0 || num_pages <= 0)
+    return PKV_ERR_BAD_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!cu_seq_lens_q || !cu_seq_lens_k || !block_tables || !free_pages || !free_count)
+    return PKV_ERR_NULL_ARG;
+  return hip_status(launch_page_alloc(cu_seq_lens_q, cu_seq_lens_k, num_seqs, block_tables,
+                                      max_pages_per_seq, page_size, free_pages, free_count,
+                                      num_pages, status, stream));
+}
+
+pkv_status pkv_page_free(const int32_t* seq_lens, const int32_t* release, int32_t num_seqs,
+                         int32_t* block_tables, int32_t max_pages_per_seq, int32_t page_size,
+                         int32_t* free_pages, int32_t* free_count, int32_t num_pages,
+                         int32_t* status, hipStream_t stream) {
+  if (num_seqs < 0 || max_pages_per_seq <= 0 || page_size <= 0 || num_pages <= 0)
+    return PKV_ERR_BAD_SHAPE;
+  if (num_seqs == 0) return PKV_OK;
+  if (!seq_lens || !release || !block_tables || !free_pages || !free_count)
+    return PKV_ERR_NULL_ARG;
+  return hip_status(launch_page_free(seq_lens, release, num_seqs, block_tables, max_pages_per_seq,
+                                     page_size, free_pages, free_count, num_pages, status,
+                                     stream));
+}
+
 pkv_status pkv_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t page_size,
                            int32_t max_seq_len, int32_t window, int32_t num_splits_requested,
                            int32_t* num_splits, int32_t* pages_per_split) {

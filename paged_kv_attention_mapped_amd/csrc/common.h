@@ -122,6 +122,12 @@ hipError_t launch_append_mapped(const uint16_t* k_new, const uint16_t* v_new, co
                                 int num_seqs, int total, int max_q, int page_size, int num_pages,
                                 int hkv, int d, uint16_t* k_pool, uint16_t* v_pool,
                                 int64_t num_slots, int32_t* slots_out, hipStream_t st);
+hipError_t launch_page_alloc(const int32_t* cu_q, const int32_t* cu_k, int num_seqs, int32_t* bt,
+                             int max_pages, int page_size, const int32_t* free_pages,
+                             int32_t* free_count, int num_pages, int32_t* status, hipStream_t st);
+hipError_t launch_page_free(const int32_t* seq_lens, const int32_t* release, int num_seqs,
+                            int32_t* bt, int max_pages, int page_size, int32_t* free_pages,
+                            int32_t* free_count, int num_pages, int32_t* status, hipStream_t st);
 hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* slots,
                          int num_tokens, int hkv, int d, uint16_t* k_pool, uint16_t* v_pool,
                          int64_t num_slots, hipStream_t st);

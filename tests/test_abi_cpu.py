@@ -33,7 +33,7 @@ def test_header_declares_the_entry_points():
         "pkv_append", "pkv_append_mapped", "pkv_decode", "pkv_decode_combine",
         "pkv_decode_method", "pkv_decode_plan", "pkv_decode_split",
         "pkv_device_info", "pkv_graph_begin", "pkv_graph_destroy", "pkv_graph_end",
-        "pkv_graph_launch", "pkv_graph_nodes",
+        "pkv_graph_launch", "pkv_graph_nodes", "pkv_page_alloc", "pkv_page_free",
         "pkv_decode_stream", "pkv_decode_stream_merge", "pkv_decode_stream_waves",
         "pkv_decode_stream_workspace_bytes", "pkv_decode_workspace_bytes", "pkv_prefill_varlen",
         "pkv_slot_mapping", "pkv_status_string"])
@@ -193,3 +193,18 @@ def test_decode_method(P):
     assert P.decode_method(4, 8, 2, 128, 32, 1000, 0, 1) == ("direct", 1)
     assert P.lib().pkv_decode_method(4, 8, 2, 96, 32, 100, 0, 0, None, None) == 3
     assert P.lib().pkv_decode_method(4, 8, 3, 128, 32, 100, 0, 0, None, None) == 2
+
+
+def test_page_allocator_validation(P):
+    L = P.lib()
+    a = [FAKE, FAKE, 3, FAKE, 4, 16, FAKE, FAKE, 32, None, None]
+    for i, code in ((0, 1), (3, 1), (6, 1), (7, 1)):
+        b = list(a); b[i] = None
+        assert L.pkv_page_alloc(*b) == code
+        assert L.pkv_page_free(*b) == code
+    for i, v in ((2, -1), (4, 0), (5, 0), (8, 0)):
+        b = list(a); b[i] = v
+        assert L.pkv_page_alloc(*b) == 2
+        assert L.pkv_page_free(*b) == 2
+    b = list(a); b[2] = 0; b[0] = None      # no sequences: nothing to do
+    assert L.pkv_page_alloc(*b) == 0 and L.pkv_page_free(*b) == 0
