@@ -50,6 +50,8 @@ DESCRIPTIONS = {
     "window_shared": "64 decoders ctx U[512,4096] + 4 chunks of 128 after U[512,4096], "
                      "8/1/256, page 32, window 512, 2 layers sharing the pool",
     "long_prefill": "16 prompts U[1024,4096], 32/8/128, page 32 (prefill only)",
+    "full512_decode": "64 decode seqs, ctx U[512,4096], Hq/Hkv/D 8/1/512, page 32 (full attention)",
+    "full512_prefill": "8 prompts U[1024,4096], 8/1/512, page 32 (full attention, prefill only)",
 }
 
 
@@ -647,6 +649,9 @@ def main():
                                "pages_per_split": st.pps})
         kname = ("decode_stream_kernel (stream-K)" if st.nw else
                  "decode_kernel (split-K partials)" if st.S > 1 else "decode_kernel (direct)")
+        if wl.head_dim == 512:
+            kname = "attn512_kernel (head-dim split, " + (
+                "split-K partials)" if st.S > 1 else "direct)")
         out["roofline"] = {
             "kernel": kname,
             "bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -658,7 +663,8 @@ def main():
         pk_ms = float(np.mean([a.elapsed_time(b) for a, b in pevs]))
         fl = prefill_flops(wl)
         tf = fl / (pk_ms * 1e-3) / 1e12
-        pre = {"kernel": "prefill_kernel", "bound": "mfma", "achieved": round(tf, 3),
+        pre = {"kernel": "attn512_kernel" if wl.head_dim == 512 else "prefill_kernel",
+               "bound": "mfma", "achieved": round(tf, 3),
                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                "traffic": None, "avg_kernel_ms": round(pk_ms, 5), "algorithmic_flops_per_launch": fl}
         if st.B:

@@ -12,7 +12,8 @@ using namespace pkv;
 
 namespace {
 
-bool supported_dim(int d) { return d == 64 || d == 128 || d == 256; }
+bool supported_dim(int d) { return d == 64 || d == 128 || d == 256 || d == 512; }
+bool stream_dim(int d) { return d == 64 || d == 128 || d == 256; }  // stream-K decode
 bool supported_ps(int ps) { return ps == 16 || ps == 32; }
 
 pkv_status check_heads(int hq, int hkv) {
@@ -221,7 +222,8 @@ pkv_status pkv_decode_method(int32_t num_seqs, int32_t num_q_heads, int32_t num_
   if (hs != PKV_OK) return hs;
   if (!supported_dim(head_dim) || !supported_ps(page_size)) return PKV_ERR_UNSUPPORTED;
   int32_t m = PKV_DECODE_SPLIT, c = 0;
-  if (num_splits_requested == 0 && num_seqs > 0 && num_seqs <= kStreamMaxSeqs) {
+  if (num_splits_requested == 0 && num_seqs > 0 && num_seqs <= kStreamMaxSeqs &&
+      stream_dim(head_dim)) {
     const int shift = stream_kv_shift(num_q_heads, num_kv_heads, head_dim);
     if (shift == 0 && (int64_t)num_seqs * num_kv_heads <= kDirectMaxRows) {
       m = PKV_DECODE_DIRECT;
@@ -407,7 +409,7 @@ pkv_status pkv_decode_stream_waves(int32_t num_seqs, int32_t num_q_heads, int32_
   if (num_seqs < 0 || max_seq_len < 0) return PKV_ERR_BAD_SHAPE;
   const pkv_status hs = check_heads(num_q_heads, num_kv_heads);
   if (hs != PKV_OK) return hs;
-  if (!supported_dim(head_dim) || !supported_ps(page_size)) return PKV_ERR_UNSUPPORTED;
+  if (!stream_dim(head_dim) || !supported_ps(page_size)) return PKV_ERR_UNSUPPORTED;
   const int64_t heads = (int64_t)num_kv_heads << stream_kv_shift(num_q_heads, num_kv_heads, head_dim);
   const int64_t units = (int64_t)num_seqs * heads * key_pages(page_size, max_seq_len, window);
   const int per_simd = head_dim == 256 ? 1 : kStreamWavesPerSimd;
@@ -452,7 +454,7 @@ pkv_status pkv_decode_stream(const uint16_t* q, const uint16_t* k_pool, const ui
                                num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
                                num_pages, 0);
   if (st != PKV_OK) return st;
-  if (num_seqs > kStreamMaxSeqs) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs > kStreamMaxSeqs || !stream_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
   if (num_waves <= 0 || num_waves > (1 << 20)) return PKV_ERR_BAD_SHAPE;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !workspace) return PKV_ERR_NULL_ARG;
@@ -475,7 +477,7 @@ pkv_status pkv_decode_stream_merge(const void* workspace, size_t workspace_bytes
                                    int32_t head_dim, uint16_t* out, hipStream_t stream) {
   pkv_status st = check_heads(num_q_heads, num_kv_heads);
   if (st != PKV_OK) return st;
-  if (!supported_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (!stream_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
   if (num_waves <= 0 || num_waves > (1 << 20)) return PKV_ERR_BAD_SHAPE;
   if (!workspace || !out) return PKV_ERR_NULL_ARG;
   if (workspace_bytes <

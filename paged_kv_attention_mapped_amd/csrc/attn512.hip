@@ -1,0 +1,333 @@
+// Paged attention for head_dim 512: the full-attention layers of the
+// dual-regime model, next to its head_dim-256 sliding layers (benchmarks
+// commit log 1847125, the Gemma-4-E2B-it engine entry, "Dual attention
+// regimes": full_attention with head_dim 512, sliding_attention with
+// head_dim 256 and window 512).
+//
+// At 512 dims the register and LDS budgets of the head_dim <= 256 kernels
+// do not hold: one wave's K/V step buffers alone would need 256 registers,
+// and the prefill kernel's Q operands and 32-row accumulators twice as
+// many.  Here the head dimension is split over the four waves of a
+// workgroup: wave w owns dims [128w, 128w + 128) of Q, K, V and O.
+//   S^T = K Q^T   each wave multiplies its 128-dim slices on
+//                 v_mfma_f32_32x32x16_bf16 (K rows as A, the query columns
+//                 as B) and the four partial score tiles are summed through
+//                 LDS (one barrier per 32-key tile);
+//   softmax       every wave runs the same online softmax on the full tile;
+//   O^T += V^T P^T each wave on its own 128 dims: V is staged row-major in
+//                 LDS and read transposed (ds_read_b64_tr_b16), and the
+//                 probabilities already sit in B-operand order because the
+//                 K rows are loaded in a permuted order.
+// The 32 MFMA columns are (row, head) pairs of one KV group: R = 32/g rows
+// times the g query heads, so every K/V tile is read once for the whole
+// group.  A decode row is one row (g columns), a prefill workgroup R rows.
+// Rows come through cu_seq_lens_q/k (varlen prefill, decode rows as
+// one-row sequences) or through seq_lens (decode), and decode may cut the
+// keys into splits whose partials go to the common combine kernel.
+#include <math.h>
+
+#include "common.h"
+#include "prefill_common.h"
+
+namespace pkv {
+namespace {
+
+using prefill_detail::half_max;
+using prefill_detail::half_sum;
+using prefill_detail::lds_s16x4;
+using prefill_detail::s16x4;
+
+constexpr int D5 = 512;
+constexpr int kWaves5 = 4;                  // waves per workgroup, 128 dims each
+constexpr int kSlice = D5 / kWaves5;         // dims per wave
+constexpr int kTile = 32;                    // keys per tile
+constexpr int kVStride = kSlice * 2 + 16;    // LDS bytes per staged V row (padded)
+constexpr int kVBytes = kTile * kVStride;    // one wave's staged V tile
+constexpr int kSBytes = 64 * 16 * 4;         // one wave's partial score tile
+// LDS: [2 tiles][4 waves] partial scores, then [2 tiles][4 waves] V slices
+constexpr int kLds5 = 2 * kWaves5 * kSBytes + 2 * kWaves5 * kVBytes;
+
+// Key (relative to its tile) that lane row i of the K operand loads.  With
+// this order, score register r of lane half h holds key 16(r/8) + 8h + r%8,
+// which is the B-operand order of the O^T += V^T P^T step.
+__device__ __forceinline__ int key_of_row(int i) {
+  const int a = i >> 3, h = (i >> 2) & 1, b = i & 3;
+  return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
+}
+
+template <int PS>
+__global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem5[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;     // lane half: k-group of the operands
+  const int col = lane & 31;   // MFMA column: (row, head) pair
+  const int g = a.group;
+  const int R = 32 / g;        // rows per workgroup
+  const int nsplit = a.num_splits;
+  const int s = blockIdx.x % nsplit;
+  const int rb = blockIdx.x / nsplit;
+  const int hk = blockIdx.y;
+  const int j = blockIdx.z;
+
+  int q_start, Lq, Lk;
+  if (a.cu_q != nullptr) {
+    q_start = a.cu_q[j];
+    Lq = a.cu_q[j + 1] - q_start;
+    Lk = a.cu_k[j + 1] - a.cu_k[j];
+  } else {
+    q_start = j;
+    Lq = 1;
+    Lk = a.seq_lens[j];
+  }
+  Lk = max(0, min(Lk, a.max_pages * PS));
+  const int row0 = rb * R;
+  if (row0 >= Lq) return;
+  const int nrows = min(R, Lq - row0);
+  const int shift = Lk - Lq;
+
+  // this lane's column
+  const int crow = col / g, chead = col - crow * g;
+  const bool col_ok = crow < nrows;
+  const int head = hk * g + chead;
+  const int pos = shift + row0 + crow;  // position of the column's row
+  const int qrow = q_start + row0 + (col_ok ? crow : 0);
+
+  // keys this workgroup may need: the rows' causal/window band, cut to the split
+  const int pmin = shift + row0, pmax = shift + row0 + nrows - 1;
+  int k_lo = a.window > 0 ? max(0, pmin - a.window + 1) : 0;
+  int k_hi = min(pmax + 1, Lk);
+  if (nsplit > 1) {
+    const int first_key = a.window > 0 ? max(0, Lk - a.window) : 0;
+    const int p0 = first_key / PS;
+    k_lo = max(k_lo, (p0 + s * a.pages_per_split) * PS);
+    k_hi = min(k_hi, (p0 + (s + 1) * a.pages_per_split) * PS);
+  }
+
+  // Q slice as the B operand: lane holds q[column][128w + 16ks + 8h .. +7]
+  bf16x8 qop[8];
+  {
+    const uint16_t* qp = a.q + ((int64_t)qrow * a.num_q_heads + head) * D5 + kSlice * w + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (col_ok) v = *reinterpret_cast<const uint4*>(qp + 16 * ks);
+      qop[ks] = as_bf16x8(v);
+    }
+  }
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c = a.scale_log2;
+
+  const uint16_t* kh = a.k_pool + (int64_t)hk * a.head_stride + kSlice * w;
+  const uint16_t* vh = a.v_pool + (int64_t)hk * a.head_stride + kSlice * w;
+  const int32_t* bt_row = a.block_tables + (int64_t)j * a.max_pages;
+  const int krel = key_of_row(lane & 31);  // key this lane loads as K operand row
+
+  // A 32-key tile spans one page (page_size 32) or two (16): their table
+  // entries, or -1 for an unusable entry.
+  constexpr int NPG = kTile / PS;
+  struct TileRegs {
+    uint4 k[8];     // K operand, k-steps of 16 dims
+    uint4 v[8];     // V slice rows, staged to LDS before use
+    int phys[NPG];  // pages of the tile
+  };
+  // pool row of key k (tile-relative kr) of the tile, or -1 when the key is
+  // outside [k_lo, k_hi) or its page is unusable
+  auto pool_row = [&](const TileRegs& tr, int kb, int kr) -> int64_t {
+    const int k = kb + kr;
+    const int ph = (NPG == 1 || kr < PS) ? tr.phys[0] : tr.phys[NPG - 1];
+    if (k < k_lo || k >= k_hi || ph < 0) return -1;
+    return (int64_t)ph * PS + k % PS;
+  };
+  auto load_tile = [&](TileRegs& tr, int t) {
+    const int kb = t * kTile;
+#pragma unroll
+    for (int pg = 0; pg < NPG; ++pg) {
+      // entries past the last page holding a key below k_hi are not read
+      const int ph = bt_row[max(0, min(kb / PS + pg, (k_hi - 1) / PS))];
+      tr.phys[pg] = (ph >= 0 && ph < a.num_pages) ? ph : -1;
+    }
+    const int64_t kr = pool_row(tr, kb, krel);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (kr >= 0) v = *reinterpret_cast<const uint4*>(kh + kr * D5 + 16 * ks + 8 * h);
+      tr.k[ks] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int chunk = lane + 64 * i, key = chunk >> 4, part = chunk & 15;
+      const int64_t vr = pool_row(tr, kb, key);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (vr >= 0) v = *reinterpret_cast<const uint4*>(vh + vr * D5 + 8 * part);
+      tr.v[i] = v;
+    }
+  };
+
+  float* sbuf = reinterpret_cast<float*>(smem5);
+  unsigned char* vbuf = smem5 + 2 * kWaves5 * kSBytes;
+
+  auto process = [&](const TileRegs& tr, int t) {
+    const int kb = t * kTile;
+    const int par = t & 1;
+    // partial scores of this wave's 128 dims
+    f32x16 sp = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) sp = mfma32(as_bf16x8(tr.k[ks]), qop[ks], sp);
+    float* my = sbuf + ((par * kWaves5 + w) * 64 + lane) * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<float4*>(my + 4 * q) = make_float4(sp[4 * q], sp[4 * q + 1], sp[4 * q + 2], sp[4 * q + 3]);
+    // this wave's V rows, row-major with a padded stride
+    unsigned char* vw = vbuf + (par * kWaves5 + w) * kVBytes;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int chunk = lane + 64 * i, key = chunk >> 4, part = chunk & 15;
+      *reinterpret_cast<uint4*>(vw + key * kVStride + 16 * part) = tr.v[i];
+    }
+    __syncthreads();
+    // full scores: the four partials of this lane's (column, keys)
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves5; ++ww) {
+      const float* src = sbuf + ((par * kWaves5 + ww) * 64 + lane) * 16;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(src + 4 * q);
+        x[4 * q] += v.x;
+        x[4 * q + 1] += v.y;
+        x[4 * q + 2] += v.z;
+        x[4 * q + 3] += v.w;
+      }
+    }
+    // mask: register r holds key kb + 16(r/8) + 8h + r%8 of this lane's column
+    float mt = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kr = 16 * (r >> 3) + 8 * h + (r & 7), k = kb + kr;
+      bool ok = col_ok && k <= pos && pool_row(tr, kb, kr) >= 0;
+      if (a.window > 0) ok = ok && pos - k < a.window;
+      x[r] = ok ? x[r] * c : -INFINITY;
+      mt = fmaxf(mt, x[r]);
+    }
+    mt = half_max(mt);
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      x[r] = fast_exp2(x[r] - m_use);
+      psum += x[r];
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+    // O^T += V^T P^T on this wave's dims
+    const int gi = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 pk;
+      pk.x = pack_bf16x2(x[8 * ks + 0], x[8 * ks + 1]);
+      pk.y = pack_bf16x2(x[8 * ks + 2], x[8 * ks + 3]);
+      pk.z = pack_bf16x2(x[8 * ks + 4], x[8 * ks + 5]);
+      pk.w = pack_bf16x2(x[8 * ks + 6], x[8 * ks + 7]);
+      const bf16x8 pop = as_bf16x8(pk);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        // transposed reads: source lane 4r'+a' of a 16-lane group points at
+        // V[key0 + r'][d0 + 4a']; output lane i gets V[key0 .. key0+3][d0 + i]
+        const int d0 = 32 * dt + 16 * (gi & 1) + 4 * (sl & 3);
+        uint2 part[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int key = 16 * ks + 8 * (gi >> 1) + 4 * q + (sl >> 2);
+          const s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(__attribute__((address_space(3))) unsigned char*)(vw + key * kVStride + 2 * d0));
+          part[q] = __builtin_bit_cast(uint2, v4);
+        }
+        const bf16x8 vop = as_bf16x8(make_uint4(part[0].x, part[0].y, part[1].x, part[1].y));
+        acc[dt] = mfma32(vop, pop, acc[dt]);
+      }
+    }
+  };
+
+  const int t0 = k_lo / kTile, t1 = k_hi > k_lo ? (k_hi + kTile - 1) / kTile : t0;
+  TileRegs ta, tb;
+  if (t0 < t1) load_tile(ta, t0);
+  for (int t = t0; t < t1; t += 2) {
+    if (t + 1 < t1) load_tile(tb, t + 1);
+    process(ta, t);
+    if (t + 1 >= t1) break;
+    if (t + 2 < t1) load_tile(ta, t + 2);
+    process(tb, t + 1);
+  }
+
+  // ---- write: lane holds dims 32dt + 8(r/4) + 4h + r%4 of its column ----
+  const float lt = half_sum(l_run);
+  if (!col_ok) return;
+  const int dbase = kSlice * w + 4 * h;
+  if (nsplit == 1) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    uint16_t* op = a.out + ((int64_t)qrow * a.num_q_heads + head) * D5 + dbase;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        uint2 pk;
+        pk.x = pack_bf16x2(acc[dt][4 * rq] * inv, acc[dt][4 * rq + 1] * inv);
+        pk.y = pack_bf16x2(acc[dt][4 * rq + 2] * inv, acc[dt][4 * rq + 3] * inv);
+        *reinterpret_cast<uint2*>(op + 32 * dt + 8 * rq) = pk;
+      }
+  } else {
+    const int64_t cell = ((int64_t)qrow * a.num_q_heads + head) * nsplit + s;
+    float* pa = a.part_acc + cell * D5 + dbase;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq)
+        *reinterpret_cast<float4*>(pa + 32 * dt + 8 * rq) =
+            make_float4(acc[dt][4 * rq], acc[dt][4 * rq + 1], acc[dt][4 * rq + 2], acc[dt][4 * rq + 3]);
+    if (w == 0 && h == 0) {
+      a.part_m[cell] = m_run;
+      a.part_l[cell] = lt;
+    }
+  }
+}
+
+template <int PS>
+hipError_t launch_ps(const Attn512Args& a, int num_seqs, int row_blocks, hipStream_t st) {
+  static bool attr_set = false;  // raise the dynamic LDS limit once (above 64 KB)
+  if (!attr_set) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn512_kernel<PS>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds5);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const dim3 grid(row_blocks * a.num_splits, a.num_kv_heads, num_seqs);
+  hipLaunchKernelGGL((attn512_kernel<PS>), grid, dim3(kWaves5 * 64), kLds5, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn512(const Attn512Args& a, int num_seqs, int max_rows, int page_size,
+                          hipStream_t st) {
+  const int R = 32 / a.group;
+  const int row_blocks = (max_rows + R - 1) / R;
+  return page_size == 16 ? launch_ps<16>(a, num_seqs, row_blocks, st)
+                         : launch_ps<32>(a, num_seqs, row_blocks, st);
+}
+
+}  // namespace pkv

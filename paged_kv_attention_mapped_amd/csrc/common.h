@@ -170,4 +170,33 @@ struct PrefillArgs {
 hipError_t launch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, int head_dim,
                           int page_size, hipStream_t st);
 
+// head_dim 512: one kernel for varlen rows (cu_q/cu_k set) and decode rows
+// (cu_q NULL: row j is the last position of seq_lens[j]); with num_splits
+// > 1 (decode) it writes split partials in the combine kernel's layout.
+struct Attn512Args {
+  const uint16_t* q;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  const int32_t* block_tables;
+  const int32_t* cu_q;      // varlen rows, or NULL
+  const int32_t* cu_k;
+  const int32_t* seq_lens;  // decode rows when cu_q is NULL
+  uint16_t* out;            // num_splits == 1
+  float* part_m;            // num_splits > 1
+  float* part_l;
+  float* part_acc;
+  int64_t head_stride;
+  int max_pages;
+  int num_pages;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;
+  int window;
+  int num_splits;
+  int pages_per_split;
+  float scale_log2;
+};
+hipError_t launch_attn512(const Attn512Args& a, int num_seqs, int max_rows, int page_size,
+                          hipStream_t st);
+
 }  // namespace pkv

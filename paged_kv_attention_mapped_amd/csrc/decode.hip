@@ -505,6 +505,29 @@ hipError_t launch_s(const StreamArgs& sa, int ps, hipStream_t st) {
 
 hipError_t launch_decode(const DecodeArgs& a, int num_seqs, int head_dim, int page_size,
                          bool split, hipStream_t st) {
+  if (head_dim == 512) {  // the head-dim-split kernel, decode rows
+    Attn512Args b = {};
+    b.q = a.q;
+    b.k_pool = a.k_pool;
+    b.v_pool = a.v_pool;
+    b.block_tables = a.block_tables;
+    b.seq_lens = a.seq_lens;
+    b.out = a.out;
+    b.part_m = a.part_m;
+    b.part_l = a.part_l;
+    b.part_acc = a.part_acc;
+    b.head_stride = a.head_stride;
+    b.max_pages = a.max_pages;
+    b.num_pages = a.num_pages;
+    b.num_q_heads = a.num_q_heads;
+    b.num_kv_heads = a.num_kv_heads;
+    b.group = a.group;
+    b.window = a.window;
+    b.num_splits = split ? a.num_splits : 1;
+    b.pages_per_split = a.pages_per_split;
+    b.scale_log2 = a.scale_log2;
+    return launch_attn512(b, num_seqs, 1, page_size, st);
+  }
   switch (head_dim) {
     case 64: return launch_d<64>(a, num_seqs, page_size, split, st);
     case 128: return launch_d<128>(a, num_seqs, page_size, split, st);
@@ -520,7 +543,8 @@ hipError_t launch_combine(const float* m, const float* l, const float* acc, int 
   switch (d) {
     case 64: hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(256), 0, st, m, l, acc, rows, splits, out); break;
     case 128: hipLaunchKernelGGL(combine_kernel<128>, grid, dim3(256), 0, st, m, l, acc, rows, splits, out); break;
-    default: hipLaunchKernelGGL(combine_kernel<256>, grid, dim3(256), 0, st, m, l, acc, rows, splits, out); break;
+    case 256: hipLaunchKernelGGL(combine_kernel<256>, grid, dim3(256), 0, st, m, l, acc, rows, splits, out); break;
+    default: hipLaunchKernelGGL(combine_kernel<512>, grid, dim3(256), 0, st, m, l, acc, rows, splits, out); break;
   }
   return hipGetLastError();
 }

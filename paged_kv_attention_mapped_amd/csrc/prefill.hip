@@ -557,6 +557,26 @@ hipError_t launch_p1(const PrefillArgs& a, int num_seqs, int max_q, int ps, hipS
 
 hipError_t launch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, int head_dim,
                           int page_size, hipStream_t st) {
+  if (head_dim == 512) {  // the head-dim-split kernel, varlen rows
+    Attn512Args b = {};
+    b.q = a.q;
+    b.k_pool = a.k_pool;
+    b.v_pool = a.v_pool;
+    b.block_tables = a.block_tables;
+    b.cu_q = a.cu_q;
+    b.cu_k = a.cu_k;
+    b.out = a.out;
+    b.head_stride = a.head_stride;
+    b.max_pages = a.max_pages;
+    b.num_pages = a.num_pages;
+    b.num_q_heads = a.num_q_heads;
+    b.num_kv_heads = a.num_kv_heads;
+    b.group = a.group;
+    b.window = a.window;
+    b.num_splits = 1;
+    b.scale_log2 = a.scale_log2;
+    return launch_attn512(b, num_seqs, max_seqlen_q, page_size, st);
+  }
   switch (head_dim) {
     case 64: return launch_p1<64>(a, num_seqs, max_seqlen_q, page_size, st);
     case 128: return launch_p1<128>(a, num_seqs, max_seqlen_q, page_size, st);

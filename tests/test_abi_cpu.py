@@ -208,3 +208,13 @@ def test_page_allocator_validation(P):
         assert L.pkv_page_free(*b) == 2
     b = list(a); b[2] = 0; b[0] = None      # no sequences: nothing to do
     assert L.pkv_page_alloc(*b) == 0 and L.pkv_page_free(*b) == 0
+
+
+def test_head_dim_512_plans(P):
+    # head_dim 512 runs the head-dim-split kernel: direct or split-K, never stream-K
+    assert P.decode_method(4, 8, 1, 512, 32, 100) == ("direct", 1)
+    m, c = P.decode_method(256, 8, 1, 512, 32, 8192)
+    assert m == "split" and c > 1
+    assert P.lib().pkv_decode_stream_waves(4, 8, 1, 512, 32, 100, 0, None) == 3
+    assert P.lib().pkv_decode_stream_workspace_bytes(8, 8, 1, 512) > 0
+    assert P.decode_workspace_bytes(256, 8, 512, 1, 32, 8192) == 256 * 8 * c * 514 * 4

@@ -1,0 +1,95 @@
+"""head_dim 512 (the full-attention layers of the dual-regime model) against
+the oracle: append bit-exact, decode (direct, automatic splits, explicit
+splits + combine, decode rows through the varlen entry), varlen prefill with
+fresh prompts, chunks after a cached prefix and mixed batches, for groups 1,
+3, 4 and 8, pages 16 and 32, with and without a window."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import workloads as W  # noqa: E402
+from gpu_harness import (GpuPools, OraclePools, check_close, dev_bits, dev_i32,  # noqa: E402
+                         host_bits, say)
+
+SHAPES = [  # name, Hq, Hkv, page, window
+    ("g8_p32", 8, 1, 32, 0),
+    ("g4_p16_win", 8, 2, 16, 300),
+    ("g3_p32", 3, 1, 32, 0),
+    ("g1_p16", 2, 2, 16, 0),
+]
+
+
+@pytest.fixture(scope="module")
+def P():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import paged_kv_attention_mapped_amd as P
+    P.lib()
+    return P
+
+
+def build(name, hq, hkv, ps, win, **kw):
+    cfg = W.Config("d512_" + name, 20261205, hq, hkv, 512, ps, window=win, **kw)
+    wl = W.build(cfg)
+    g = GpuPools(wl)
+    g.write("prefix")
+    g.write("new")
+    return wl, g, OraclePools(wl)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_d512_decode(P, shape):
+    name, hq, hkv, ps, win = shape
+    wl, g, o = build(name, hq, hkv, ps, win,
+                     decode_ctx=("fixed", (1, 15, 16, 17, 33, 64, 300, 777, 1500)))
+    assert np.array_equal(host_bits(g.k), o.k) and np.array_equal(host_bits(g.v), o.v)
+    qd, _ = wl.queries(0)
+    lens = wl.decode_seq_lens()
+    bt = dev_i32(wl.block_tables[:wl.n_decode])
+    ref = oracle.decode(qd, o.k, o.v, wl.block_tables[:wl.n_decode], lens, ps, wl.scale, win)
+    assert P.decode_method(wl.n_decode, hq, hkv, 512, ps, int(lens.max()), win)[0] != "stream"
+    for splits in (0, 1, 3):
+        say(f"[d512 decode] {name} num_splits={splits}")
+        out = P.decode(dev_bits(qd), g.k, g.v, bt, dev_i32(lens), int(lens.max()), page_size=ps,
+                       scale=wl.scale, window=win, num_splits=splits)
+        torch.cuda.synchronize()
+        check_close(host_bits(out), ref, f"d512 {name} decode, splits {splits}")
+    # the same rows as one-row sequences of a varlen batch
+    one = np.ones(wl.n_decode, np.int32)
+    out = P.prefill_varlen(dev_bits(qd), g.k, g.v, bt, dev_i32(wl.cu_lens(one)),
+                           dev_i32(wl.cu_lens(lens)), 1, int(lens.max()), page_size=ps,
+                           scale=wl.scale, window=win)
+    torch.cuda.synchronize()
+    check_close(host_bits(out), ref, f"d512 {name} decode rows through the varlen entry")
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_d512_prefill(P, shape):
+    name, hq, hkv, ps, win = shape
+    wl, g, o = build(name, hq, hkv, ps, win, decode_ctx=("fixed", (40, 500)),
+                     prefill_new=("fixed", (1, 31, 33, 64, 0, 130)),
+                     chunk=("uniform", 2, 100, 700, 50))
+    qd, qp = wl.queries(0)
+    seqs = wl.prefill_ids()
+    say(f"[d512 prefill] {name}: N={len(seqs)} Tq={qp.shape[0]}")
+    out = P.prefill_varlen(dev_bits(qp), g.k, g.v, dev_i32(wl.block_tables[seqs]),
+                           dev_i32(wl.prefill_cu_q()), dev_i32(wl.prefill_cu_k()),
+                           int(wl.new_lens[seqs].max()), int(wl.total_lens[seqs].max()),
+                           page_size=ps, scale=wl.scale, window=win)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_varlen(qp, o.k, o.v, wl.block_tables[seqs], wl.prefill_cu_q(),
+                                wl.prefill_cu_k(), ps, wl.scale, win)
+    check_close(host_bits(out), ref, f"d512 {name} prefill")
+    # decoders and prompts in one launch
+    q = np.concatenate([qd, qp])
+    cq, ck = wl.cu_lens(wl.new_lens), wl.cu_lens(wl.total_lens)
+    out = P.prefill_varlen(dev_bits(q), g.k, g.v, dev_i32(wl.block_tables), dev_i32(cq),
+                           dev_i32(ck), int(wl.new_lens.max()), int(wl.total_lens.max()),
+                           page_size=ps, scale=wl.scale, window=win)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_varlen(q, o.k, o.v, wl.block_tables, cq, ck, ps, wl.scale, win)
+    check_close(host_bits(out), ref, f"d512 {name} mixed single launch")

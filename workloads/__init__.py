@@ -248,6 +248,12 @@ CONFIGS = {
     # enough that the matrix cores, not launch latency, bound it.
     "long_prefill": Config("long_prefill", 20260006, 32, 8, 128, 32,
                            prefill_new=("uniform", 16, 1024, 4096)),
+    # the same model's full-attention layers: head_dim 512, no window; the
+    # 64 decoders of the windowed case, and 8 prompts for the prefill side
+    "full512_decode": Config("full512_decode", 20260007, 8, 1, 512, 32,
+                             decode_ctx=("uniform", 64, 512, 4096)),
+    "full512_prefill": Config("full512_prefill", 20260008, 8, 1, 512, 32,
+                              prefill_new=("uniform", 8, 1024, 4096)),
 }
 
 
