@@ -30,7 +30,9 @@
  * (commit log 1847125, the entry that builds one block mask per attention
  * regime).  Query head h reads KV head h / (Hq/Hkv).
  *
- * Supported shapes: head_dim in {64, 128, 256}; page_size in {16, 32};
+ * Supported shapes: head_dim in {64, 128, 256, 512} (512: the full-attention
+ * layers of the dual-regime model, commit log 1847125, Gemma-4-E2B-it engine
+ * entry, "Dual attention regimes"; no stream-K decode); page_size in {16, 32};
  * Hq a multiple of Hkv with Hq/Hkv <= 8.  Anything else returns
  * PKV_ERR_UNSUPPORTED before any HIP call.
  *
@@ -215,7 +217,8 @@ pkv_status pkv_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t page_
  *             PKV_DECODE_STREAM  stream-K + merge (*count = persistent waves).
  * With num_splits_requested = 0 a batch of at most 256 (sequence, KV head)
  * rows whose query-head group is not split in two by stream-K goes direct,
- * up to 2048 sequences go stream-K, larger batches split-K.  Either output
+ * up to 2048 sequences go stream-K, larger batches split-K; head_dim 512
+ * always takes split-K (direct when one split suffices).  Either output
  * pointer may be NULL.
  */
 enum { PKV_DECODE_DIRECT = 0, PKV_DECODE_SPLIT = 1, PKV_DECODE_STREAM = 2 };

@@ -126,7 +126,10 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a)
 
   const uint16_t* kh = a.k_pool + (int64_t)hk * a.head_stride + kSlice * w;
   const uint16_t* vh = a.v_pool + (int64_t)hk * a.head_stride + kSlice * w;
-  const int32_t* bt_row = a.block_tables + (int64_t)j * a.max_pages;
+  // block-table row read through the scalar cache (never written here), so
+  // that waiting for an entry does not wait for the K/V loads in flight
+  const __attribute__((address_space(4))) int32_t* bt_row =
+      (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)j * a.max_pages);
   const int krel = key_of_row(lane & 31);  // key this lane loads as K operand row
 
   // A 32-key tile spans one page (page_size 32) or two (16): their table
@@ -136,6 +139,7 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a)
     uint4 k[8];     // K operand, k-steps of 16 dims
     uint4 v[8];     // V slice rows, staged to LDS before use
     int phys[NPG];  // pages of the tile
+    uint32_t vok;   // bit i: V chunk i belongs to a usable key
   };
   // pool row of key k (tile-relative kr) of the tile, or -1 when the key is
   // outside [k_lo, k_hi) or its page is unusable
@@ -153,20 +157,21 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a)
       const int ph = bt_row[max(0, min(kb / PS + pg, (k_hi - 1) / PS))];
       tr.phys[pg] = (ph >= 0 && ph < a.num_pages) ? ph : -1;
     }
+    // Loads are issued unconditionally (an unusable key reads pool row 0,
+    // which always exists) so that the compiler can count them exactly and
+    // keep the next tile in flight; K rows of such keys only meet masked
+    // scores, and V rows are zeroed when staged.
     const int64_t kr = pool_row(tr, kb, krel);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (kr >= 0) v = *reinterpret_cast<const uint4*>(kh + kr * D5 + 16 * ks + 8 * h);
-      tr.k[ks] = v;
-    }
+    for (int ks = 0; ks < 8; ++ks)
+      tr.k[ks] = *reinterpret_cast<const uint4*>(kh + max(kr, (int64_t)0) * D5 + 16 * ks + 8 * h);
+    tr.vok = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int chunk = lane + 64 * i, key = chunk >> 4, part = chunk & 15;
       const int64_t vr = pool_row(tr, kb, key);
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (vr >= 0) v = *reinterpret_cast<const uint4*>(vh + vr * D5 + 8 * part);
-      tr.v[i] = v;
+      tr.vok |= (vr >= 0 ? 1u : 0u) << i;
+      tr.v[i] = *reinterpret_cast<const uint4*>(vh + max(vr, (int64_t)0) * D5 + 8 * part);
     }
   };
 
@@ -189,9 +194,13 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int chunk = lane + 64 * i, key = chunk >> 4, part = chunk & 15;
-      *reinterpret_cast<uint4*>(vw + key * kVStride + 16 * part) = tr.v[i];
+      *reinterpret_cast<uint4*>(vw + key * kVStride + 16 * part) =
+          ((tr.vok >> i) & 1u) ? tr.v[i] : make_uint4(0, 0, 0, 0);
     }
-    __syncthreads();
+    // LDS writes done, then the barrier; no wait for the next tile's global
+    // loads (a __syncthreads would drain them and serialise the prefetch)
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
     // full scores: the four partials of this lane's (column, keys)
     float x[16];
 #pragma unroll
@@ -263,14 +272,18 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a)
     }
   };
 
+  // Two register sets, one tile ahead.  The prefetch is issued on every
+  // step, also past the last tile (those keys are all unusable: row-0 reads,
+  // masked), so every path issues the same loads and the compiler waits for
+  // exactly the tile being processed.
   const int t0 = k_lo / kTile, t1 = k_hi > k_lo ? (k_hi + kTile - 1) / kTile : t0;
   TileRegs ta, tb;
   if (t0 < t1) load_tile(ta, t0);
   for (int t = t0; t < t1; t += 2) {
-    if (t + 1 < t1) load_tile(tb, t + 1);
+    load_tile(tb, t + 1);
     process(ta, t);
     if (t + 1 >= t1) break;
-    if (t + 2 < t1) load_tile(ta, t + 2);
+    load_tile(ta, t + 2);
     process(tb, t + 1);
   }
 
