@@ -321,13 +321,10 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a)
 
 template <int PS>
 hipError_t launch_ps(const Attn512Args& a, int num_seqs, int row_blocks, hipStream_t st) {
-  static bool attr_set = false;  // raise the dynamic LDS limit once (above 64 KB)
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn512_kernel<PS>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds5);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_raised{0};
+  const hipError_t e =
+      raise_lds_limit(reinterpret_cast<const void*>(&attn512_kernel<PS>), kLds5, lds_raised);
+  if (e != hipSuccess) return e;
   const dim3 grid(row_blocks * a.num_splits, a.num_kv_heads, num_seqs);
   hipLaunchKernelGGL((attn512_kernel<PS>), grid, dim3(kWaves5 * 64), kLds5, st, a);
   return hipGetLastError();

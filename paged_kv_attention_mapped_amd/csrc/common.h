@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stdint.h>
 
 #include <type_traits>
@@ -91,6 +93,20 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 // ---------------------------------------------------------------------------
 // launchers (host side; arguments already validated by the C ABI layer)
 // ---------------------------------------------------------------------------
+
+// Raise a kernel's dynamic LDS limit (64 KB by default) once per device;
+// thread-safe, and a no-op after the first call on a device.
+inline hipError_t raise_lds_limit(const void* kernel, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
+
 struct DecodeArgs {
   const uint16_t* q;
   const uint16_t* k_pool;

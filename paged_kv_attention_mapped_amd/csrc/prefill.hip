@@ -525,14 +525,10 @@ hipError_t launch_p3(const PrefillArgs& a, int num_seqs, int max_q, hipStream_t 
   const int nqb = (max_q + C::BM - 1) / C::BM;
   dim3 grid(a.num_kv_heads * (a.group / HW), num_seqs, nqb);
   const size_t smem = C::LDS_BYTES;
-  static bool attr_set = false;  // raise the dynamic LDS limit once (above 64 KB)
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&prefill_kernel<D, PS, HW>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_raised{0};
+  const hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&prefill_kernel<D, PS, HW>),
+                                       (int)smem, lds_raised);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((prefill_kernel<D, PS, HW>), grid, dim3(C::NT), smem, st, a, nqb);
   return hipGetLastError();
 }
