@@ -41,7 +41,9 @@ constexpr int D5 = 512;
 constexpr int kWaves5 = 4;                  // waves per workgroup, 128 dims each
 constexpr int kSlice = D5 / kWaves5;         // dims per wave
 constexpr int kTile = 32;                    // keys per tile
-constexpr int kVStride = kSlice * 2 + 16;    // LDS bytes per staged V row (padded)
+// LDS bytes per staged V row: 256 + 64, so that the four rows and two dim
+// groups one transposed read touches fall in eight disjoint 8-bank windows
+constexpr int kVStride = kSlice * 2 + 64;
 constexpr int kVBytes = kTile * kVStride;    // one wave's staged V tile
 constexpr int kSBytes = 64 * 16 * 4;         // one wave's partial score tile
 // LDS: [2 tiles][4 waves] partial scores, then [2 tiles][4 waves] V slices
@@ -185,10 +187,13 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a)
     f32x16 sp = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) sp = mfma32(as_bf16x8(tr.k[ks]), qop[ks], sp);
-    float* my = sbuf + ((par * kWaves5 + w) * 64 + lane) * 16;
+    // partial tile as [4 quads][64 lanes] float4s: each store and load
+    // instruction covers 1 KB contiguous (no bank conflicts)
+    float* my = sbuf + (par * kWaves5 + w) * 64 * 16;
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<float4*>(my + 4 * q) = make_float4(sp[4 * q], sp[4 * q + 1], sp[4 * q + 2], sp[4 * q + 3]);
+      *reinterpret_cast<float4*>(my + (q * 64 + lane) * 4) =
+          make_float4(sp[4 * q], sp[4 * q + 1], sp[4 * q + 2], sp[4 * q + 3]);
     // this wave's V rows, row-major with a padded stride
     unsigned char* vw = vbuf + (par * kWaves5 + w) * kVBytes;
 #pragma unroll
@@ -207,10 +212,10 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a)
     for (int r = 0; r < 16; ++r) x[r] = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kWaves5; ++ww) {
-      const float* src = sbuf + ((par * kWaves5 + ww) * 64 + lane) * 16;
+      const float* src = sbuf + (par * kWaves5 + ww) * 64 * 16;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(src + 4 * q);
+        const float4 v = *reinterpret_cast<const float4*>(src + (q * 64 + lane) * 4);
         x[4 * q] += v.x;
         x[4 * q + 1] += v.y;
         x[4 * q + 2] += v.z;
