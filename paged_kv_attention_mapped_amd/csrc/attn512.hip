@@ -32,7 +32,9 @@
 namespace pkv {
 namespace {
 
+using prefill_detail::bf16x2;
 using prefill_detail::half_max;
+using prefill_detail::kRescaleSlack;
 using prefill_detail::half_sum;
 using prefill_detail::lds_s16x4;
 using prefill_detail::s16x4;
@@ -138,42 +140,47 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a)
   // entries, or -1 for an unusable entry.
   constexpr int NPG = kTile / PS;
   struct TileRegs {
-    uint4 k[8];     // K operand, k-steps of 16 dims
-    uint4 v[8];     // V slice rows, staged to LDS before use
-    int phys[NPG];  // pages of the tile
-    uint32_t vok;   // bit i: V chunk i belongs to a usable key
+    uint4 k[8];       // K operand, k-steps of 16 dims
+    uint4 v[8];       // V slice rows, staged to LDS before use
+    uint32_t usable;  // bit kr: key kb + kr is in [k_lo, k_hi) on a usable page
   };
-  // pool row of key k (tile-relative kr) of the tile, or -1 when the key is
-  // outside [k_lo, k_hi) or its page is unusable
-  auto pool_row = [&](const TileRegs& tr, int kb, int kr) -> int64_t {
-    const int k = kb + kr;
-    const int ph = (NPG == 1 || kr < PS) ? tr.phys[0] : tr.phys[NPG - 1];
-    if (k < k_lo || k >= k_hi || ph < 0) return -1;
-    return (int64_t)ph * PS + k % PS;
-  };
+  // Lane-constant parts of the load addresses (elements from a page base).
+  // K: lane row i loads key key_of_row(i); V chunk i is key 4i + lane/16,
+  // dims 8 * (lane % 16) .. +7.  A tile starts on a page boundary.
+  const int k_off = (krel % PS) * D5 + 8 * h;
+  int v_off[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v_off[i] = ((4 * i + (lane >> 4)) % PS) * D5 + 8 * (lane & 15);
   auto load_tile = [&](TileRegs& tr, int t) {
     const int kb = t * kTile;
+    // pages of the tile (wave-uniform); an unusable entry reads page 0
+    int ph[NPG];
+    uint32_t usable = 0;
 #pragma unroll
     for (int pg = 0; pg < NPG; ++pg) {
       // entries past the last page holding a key below k_hi are not read
-      const int ph = bt_row[max(0, min(kb / PS + pg, (k_hi - 1) / PS))];
-      tr.phys[pg] = (ph >= 0 && ph < a.num_pages) ? ph : -1;
+      const int e = bt_row[max(0, min(kb / PS + pg, (k_hi - 1) / PS))];
+      const bool ok = e >= 0 && e < a.num_pages;
+      ph[pg] = ok ? e : 0;
+      // keys of this page inside [k_lo, k_hi)
+      const int lo = max(k_lo - kb - pg * PS, 0), hi = min(k_hi - kb - pg * PS, PS);
+      if (ok && hi > lo)
+        usable |= (hi - lo >= 32 ? 0xffffffffu : ((1u << (hi - lo)) - 1u)) << (pg * PS + lo);
     }
-    // Loads are issued unconditionally (an unusable key reads pool row 0,
-    // which always exists) so that the compiler can count them exactly and
-    // keep the next tile in flight; K rows of such keys only meet masked
-    // scores, and V rows are zeroed when staged.
-    const int64_t kr = pool_row(tr, kb, krel);
+    tr.usable = usable;
+    // Loads are issued unconditionally (unusable keys read their page base
+    // or page 0, which always exists) so that the compiler can count them
+    // exactly and keep the next tile in flight; K rows of such keys only
+    // meet masked scores, and V rows are zeroed when staged.
+    const int phk = (NPG == 1 || krel < PS) ? ph[0] : ph[NPG - 1];
+    const uint16_t* kp = kh + (int64_t)phk * PS * D5;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
-      tr.k[ks] = *reinterpret_cast<const uint4*>(kh + max(kr, (int64_t)0) * D5 + 16 * ks + 8 * h);
-    tr.vok = 0;
+      tr.k[ks] = *reinterpret_cast<const uint4*>(kp + k_off + 16 * ks);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int chunk = lane + 64 * i, key = chunk >> 4, part = chunk & 15;
-      const int64_t vr = pool_row(tr, kb, key);
-      tr.vok |= (vr >= 0 ? 1u : 0u) << i;
-      tr.v[i] = *reinterpret_cast<const uint4*>(vh + max(vr, (int64_t)0) * D5 + 8 * part);
+      const uint16_t* vp = vh + (int64_t)ph[NPG == 1 ? 0 : (i * 4 >= PS ? NPG - 1 : 0)] * PS * D5;
+      tr.v[i] = *reinterpret_cast<const uint4*>(vp + v_off[i]);
     }
   };
 
@@ -200,7 +207,7 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a)
     for (int i = 0; i < 8; ++i) {
       const int chunk = lane + 64 * i, key = chunk >> 4, part = chunk & 15;
       *reinterpret_cast<uint4*>(vw + key * kVStride + 16 * part) =
-          ((tr.vok >> i) & 1u) ? tr.v[i] : make_uint4(0, 0, 0, 0);
+          ((tr.usable >> key) & 1u) ? tr.v[i] : make_uint4(0, 0, 0, 0);
     }
     // LDS writes done, then the barrier; no wait for the next tile's global
     // loads (a __syncthreads would drain them and serialise the prefetch)
@@ -222,21 +229,39 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a)
         x[4 * q + 3] += v.w;
       }
     }
-    // mask: register r holds key kb + 16(r/8) + 8h + r%8 of this lane's column
+    // mask: register r holds key kb + 16(r/8) + 8h + r%8 of this lane's
+    // column.  A tile whose keys are all usable and visible to every row of
+    // the workgroup needs no per-key test (columns past the rows are never
+    // written, whatever their scores).
+    const bool full = tr.usable == 0xffffffffu && kb + kTile - 1 <= pmin &&
+                      (a.window <= 0 || pmax - kb < a.window);
     float mt = -INFINITY;
+    if (full) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kr = 16 * (r >> 3) + 8 * h + (r & 7), k = kb + kr;
-      bool ok = col_ok && k <= pos && pool_row(tr, kb, kr) >= 0;
-      if (a.window > 0) ok = ok && pos - k < a.window;
-      x[r] = ok ? x[r] * c : -INFINITY;
-      mt = fmaxf(mt, x[r]);
+      for (int r = 0; r < 16; ++r) {
+        x[r] *= c;
+        mt = fmaxf(mt, x[r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = 16 * (r >> 3) + 8 * h + (r & 7), k = kb + kr;
+        bool ok = col_ok && k <= pos && ((tr.usable >> kr) & 1u);
+        if (a.window > 0) ok = ok && pos - k < a.window;
+        x[r] = ok ? x[r] * c : -INFINITY;
+        mt = fmaxf(mt, x[r]);
+      }
     }
     mt = half_max(mt);
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
+    // the running max moves only when a tile exceeds it by more than the
+    // slack, so p <= 2^slack and the accumulators are rarely rescaled
+    const bool raise = mt > m_run + kRescaleSlack;
+    float alpha = 1.f;
+    if (raise) {
+      alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - mt);
+      m_run = mt;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -244,19 +269,26 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a)
       psum += x[r];
     }
     l_run = l_run * alpha + psum;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+    }
     // O^T += V^T P^T on this wave's dims
     const int gi = lane >> 4, sl = lane & 15;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      // p in [0, 2^slack]: the hardware round-to-nearest conversion suffices
+      const bf16x2 p01 = {(__bf16)x[8 * ks + 0], (__bf16)x[8 * ks + 1]};
+      const bf16x2 p23 = {(__bf16)x[8 * ks + 2], (__bf16)x[8 * ks + 3]};
+      const bf16x2 p45 = {(__bf16)x[8 * ks + 4], (__bf16)x[8 * ks + 5]};
+      const bf16x2 p67 = {(__bf16)x[8 * ks + 6], (__bf16)x[8 * ks + 7]};
       uint4 pk;
-      pk.x = pack_bf16x2(x[8 * ks + 0], x[8 * ks + 1]);
-      pk.y = pack_bf16x2(x[8 * ks + 2], x[8 * ks + 3]);
-      pk.z = pack_bf16x2(x[8 * ks + 4], x[8 * ks + 5]);
-      pk.w = pack_bf16x2(x[8 * ks + 6], x[8 * ks + 7]);
+      pk.x = __builtin_bit_cast(uint32_t, p01);
+      pk.y = __builtin_bit_cast(uint32_t, p23);
+      pk.z = __builtin_bit_cast(uint32_t, p45);
+      pk.w = __builtin_bit_cast(uint32_t, p67);
       const bf16x8 pop = as_bf16x8(pk);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
