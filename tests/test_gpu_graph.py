@@ -147,3 +147,70 @@ def test_decode_step_graph_buckets(P, name):
 
     for gr in graphs.values():
         gr.destroy()
+
+
+def test_mixed_step_graph_replays(P):
+    """A mixed step (fused append of every new row, then decode rows and a
+    chunk in one varlen launch) captured once and replayed with new queries
+    and new rows: each replay equals the eager calls bit for bit and the oracle
+    within the bar.  Prefill launches size their grid from host bounds only,
+    so they are replay-safe like the decode launches."""
+    hq, hkv, d, ps = 8, 2, 128, 16
+    rng = np.random.default_rng(4242)
+    nseq, maxp = 5, 16
+    num_pages = nseq * maxp
+    bt = rng.permutation(num_pages).astype(np.int32).reshape(nseq, maxp)
+    prefix = np.array([40, 0, 100, 7, 60])
+    new = np.array([1, 1, 1, 33, 1])          # four decode rows and a 33-row chunk
+    total = prefix + new
+    scale = 1.0 / np.sqrt(d)
+    shape = (hkv, num_pages * ps, d)
+    ok = np.full(shape, W.BF16_NAN, np.uint16)
+    ov = np.full(shape, W.BF16_NAN, np.uint16)
+    cu_p = np.concatenate([[0], np.cumsum(prefix)])
+    kc = W.bf16_bits(rng.standard_normal((int(cu_p[-1]), hkv, d), dtype=np.float32))
+    vc = W.bf16_bits(rng.standard_normal((int(cu_p[-1]), hkv, d), dtype=np.float32))
+    ok, ov = oracle.append(ok, ov, kc, vc, oracle.slot_mapping(bt, cu_p, cu_p, ps))
+    gk, gv, ek, ev = dev_bits(ok), dev_bits(ov), dev_bits(ok), dev_bits(ov)
+    T = int(new.sum())
+    cq_h = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    ck_h = np.concatenate([[0], np.cumsum(total)]).astype(np.int32)
+    q = torch.zeros((T, hq, d), dtype=torch.int16, device="cuda")
+    kn = torch.zeros((T, hkv, d), dtype=torch.int16, device="cuda")
+    vn = torch.zeros((T, hkv, d), dtype=torch.int16, device="cuda")
+    d_bt = torch.from_numpy(bt).cuda()
+    cq = torch.from_numpy(cq_h).cuda()
+    ck = torch.from_numpy(ck_h).cuda()
+    g_out = torch.zeros((T, hq, d), dtype=torch.bfloat16, device="cuda")
+    e_out = torch.zeros_like(g_out)
+
+    def step(kp, vp, out):
+        P.append_mapped(kn, vn, d_bt, cq, ck, kp, vp, page_size=ps, max_seqlen_q=int(new.max()))
+        P.prefill_varlen(q, kp, vp, d_bt, cq, ck, int(new.max()), int(total.max()),
+                         page_size=ps, scale=scale, out=out)
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        step(gk, gv, g_out)          # warm-up launch before capture
+        s.synchronize()
+        graph = P.capture_graph(lambda: step(gk, gv, g_out), s)
+    assert graph.nodes() == (2, 0)
+    for i in range(4):
+        qh = W.bf16_bits(rng.standard_normal((T, hq, d), dtype=np.float32))
+        knh = W.bf16_bits(rng.standard_normal((T, hkv, d), dtype=np.float32))
+        vnh = W.bf16_bits(rng.standard_normal((T, hkv, d), dtype=np.float32))
+        with torch.cuda.stream(s):
+            q.copy_(dev_bits(qh)); kn.copy_(dev_bits(knh)); vn.copy_(dev_bits(vnh))
+            g_out.fill_(5.0)
+            e_out.fill_(5.0)
+            graph.launch(s)
+            step(ek, ev, e_out)
+        s.synchronize()
+        say(f"[graph] mixed step replay {i}")
+        assert torch.equal(g_out, e_out)
+        assert torch.equal(gk, ek) and torch.equal(gv, ev)
+        ok, ov = oracle.append(ok, ov, knh, vnh, oracle.slot_mapping(bt, cq_h, ck_h, ps))
+        assert np.array_equal(host_bits(gk), ok) and np.array_equal(host_bits(gv), ov)
+        ref = oracle.prefill_varlen(qh, ok, ov, bt, cq_h, ck_h, ps, scale)
+        check_close(host_bits(g_out), ref, f"mixed step replay {i}")
+    graph.destroy()
