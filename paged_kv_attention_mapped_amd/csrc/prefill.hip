@@ -64,6 +64,9 @@ using namespace prefill_detail;
 #ifndef PKV_PREFILL_SETPRIO
 #define PKV_PREFILL_SETPRIO 0   // raise the matrix-phase wave's issue priority
 #endif
+#ifndef PKV_PREFILL_ZGROUP
+#define PKV_PREFILL_ZGROUP 8    // consecutive query blocks of one sequence dispatched together
+#endif
 
 template <int D, int HW>
 struct PrefillCfg {
@@ -188,17 +191,31 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   // from the end, so the longest (latest) blocks of every sequence go first;
   // a one-row sequence runs in the z = 0 block, among the first dispatched
   const int HG = a.group / HW;  // workgroups per KV head along the heads
-  const int j = blockIdx.y;
-  const int hk = blockIdx.x / HG;
-  const int hg = blockIdx.x - hk * HG;
-  const int qb = nqb - 1 - (int)blockIdx.z;
+  constexpr int ZG = PKV_PREFILL_ZGROUP;
+  int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+  if constexpr (ZG > 1) {
+    // dispatch order: groups of ZG query blocks (largest first), and within
+    // a group every sequence's ZG blocks back to back, so the workgroups
+    // that run together on one XCD stream the same K/V pages through its L2
+    const uint32_t X = gridDim.x, Y = gridDim.y;
+    const uint32_t lin = blockIdx.x + X * (blockIdx.y + Y * blockIdx.z);
+    const uint32_t r = lin / X, rest = r / ZG;
+    bx = (int)(lin - r * X);
+    by = (int)(rest % Y);
+    bz = (int)((rest / Y) * ZG + (r - rest * ZG));
+    if (bz >= nqb) return;  // padding of the last group
+  }
+  const int j = by;
+  const int hk = bx / HG;
+  const int hg = bx - hk * HG;
+  const int qb = nqb - 1 - bz;
 
   const int q_start = a.cu_q[j];
   const int Lq = a.cu_q[j + 1] - q_start;
   int Lk = a.cu_k[j + 1] - a.cu_k[j];
   Lk = min(Lk, a.max_pages * PS);
   if (Lq == 1) {
-    if (blockIdx.z == 0)
+    if (bz == 0)
       decode_row<D, PS, HW, C::NW>(a, j, hk, hk * a.group + hg * HW, q_start, Lk,
                                    reinterpret_cast<float*>(smem));
     return;
@@ -232,9 +249,6 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
     }
   }
 
-  // Q has landed before any tile request is issued (those are not counted
-  // by the compiler's own waits)
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
   // keys any row of this workgroup may see
   const int wg_last = min(q0 + C::BM, Lq) - 1;
@@ -404,7 +418,10 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
       dma_tile(t_first + 1, p1);
       dma_tile(t_first + 2, p2);
     }
-    phase_barrier<VM_AHEAD>();         // tile t_first of both tensors in LDS
+    // the Q loads and the first three tiles travel together; waiting for all
+    // of them costs about one memory latency (the tiles were requested at
+    // once) and leaves no load that the compiler's own waits do not count
+    phase_barrier<0>();                // Q, and tile t_first of both tensors in LDS
     if (grp_b) phase_barrier<63>();
 
     f32x16 st[C::KT];
@@ -523,7 +540,8 @@ template <int D, int PS, int HW>
 hipError_t launch_p3(const PrefillArgs& a, int num_seqs, int max_q, hipStream_t st) {
   using C = PrefillCfg<D, HW>;
   const int nqb = (max_q + C::BM - 1) / C::BM;
-  dim3 grid(a.num_kv_heads * (a.group / HW), num_seqs, nqb);
+  constexpr int ZG = PKV_PREFILL_ZGROUP;
+  dim3 grid(a.num_kv_heads * (a.group / HW), num_seqs, (nqb + ZG - 1) / ZG * ZG);
   const size_t smem = C::LDS_BYTES;
   static std::atomic<uint64_t> lds_raised{0};
   const hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&prefill_kernel<D, PS, HW>),
