@@ -182,7 +182,7 @@ __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, 
 }
 
 template <int D, int PS, int HW>
-__global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(PrefillArgs a, int nqb) {
+__global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(PrefillArgs a, int nqb, int zg) {
   using C = PrefillCfg<D, HW>;
   // [K ring: NB tiles][V ring: NB tiles]
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
@@ -191,18 +191,18 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   // from the end, so the longest (latest) blocks of every sequence go first;
   // a one-row sequence runs in the z = 0 block, among the first dispatched
   const int HG = a.group / HW;  // workgroups per KV head along the heads
-  constexpr int ZG = PKV_PREFILL_ZGROUP;
   int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
-  if constexpr (ZG > 1) {
-    // dispatch order: groups of ZG query blocks (largest first), and within
-    // a group every sequence's ZG blocks back to back, so the workgroups
-    // that run together on one XCD stream the same K/V pages through its L2
-    const uint32_t X = gridDim.x, Y = gridDim.y;
+  if (zg > 1) {
+    // dispatch order: groups of zg query blocks (largest first), and within
+    // a group every sequence's zg blocks back to back, so the workgroups
+    // that run together on one XCD (the same KV head when the x extent is a
+    // multiple of 8) stream the same K/V pages through its L2
+    const uint32_t X = gridDim.x, Y = gridDim.y, Z = (uint32_t)zg;
     const uint32_t lin = blockIdx.x + X * (blockIdx.y + Y * blockIdx.z);
-    const uint32_t r = lin / X, rest = r / ZG;
+    const uint32_t r = lin / X, rest = r / Z;
     bx = (int)(lin - r * X);
     by = (int)(rest % Y);
-    bz = (int)((rest / Y) * ZG + (r - rest * ZG));
+    bz = (int)((rest / Y) * Z + (r - rest * Z));
     if (bz >= nqb) return;  // padding of the last group
   }
   const int j = by;
@@ -540,14 +540,17 @@ template <int D, int PS, int HW>
 hipError_t launch_p3(const PrefillArgs& a, int num_seqs, int max_q, hipStream_t st) {
   using C = PrefillCfg<D, HW>;
   const int nqb = (max_q + C::BM - 1) / C::BM;
-  constexpr int ZG = PKV_PREFILL_ZGROUP;
-  dim3 grid(a.num_kv_heads * (a.group / HW), num_seqs, (nqb + ZG - 1) / ZG * ZG);
+  // grouping pays where a sequence has many query blocks; with few blocks
+  // (mixed decode/prefill steps) the first z slice, where one-row sequences
+  // run, stays first in the dispatch order
+  const int zg = nqb >= 2 * PKV_PREFILL_ZGROUP ? PKV_PREFILL_ZGROUP : 1;
+  dim3 grid(a.num_kv_heads * (a.group / HW), num_seqs, (nqb + zg - 1) / zg * zg);
   const size_t smem = C::LDS_BYTES;
   static std::atomic<uint64_t> lds_raised{0};
   const hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&prefill_kernel<D, PS, HW>),
                                        (int)smem, lds_raised);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((prefill_kernel<D, PS, HW>), grid, dim3(C::NT), smem, st, a, nqb);
+  hipLaunchKernelGGL((prefill_kernel<D, PS, HW>), grid, dim3(C::NT), smem, st, a, nqb, zg);
   return hipGetLastError();
 }
 
