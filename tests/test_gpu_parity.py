@@ -469,6 +469,37 @@ def test_prefill_long_sampled_rows(P):
         check_close(got[cq[j] + rows], ref, f"long_prefill seq {j} rows")
 
 
+@pytest.mark.parametrize("shape", [(8, 2, 128, 32, 0), (4, 1, 64, 16, 0), (8, 1, 256, 32, 300)])
+def test_prefill_many_blocks_every_row(P, shape):
+    """A launch whose longest sequence has many query blocks (the grouped
+    dispatch order of the query blocks): decode rows, fresh prompts of ragged
+    lengths (one of them empty), and chunks after a cached prefix in one
+    batch.  The output starts as NaN, so a block that no workgroup took stays
+    non-finite; every row is compared."""
+    hq, hkv, d, ps, window = shape
+    cfg = W.Config("many_blocks", 20260101, hq, hkv, d, ps, window=window,
+                   decode_ctx=("fixed", (5, 300, 1000)),
+                   prefill_new=("fixed", (1100, 1, 64, 65, 0, 700, 1025, 33)),
+                   chunk=("uniform", 2, 200, 900, 1000))
+    wl = W.build(cfg)
+    g = GpuPools(wl)
+    g.write("prefix")
+    g.write("new")
+    o = OraclePools(wl)
+    cq, ck = wl.cu_lens(wl.new_lens), wl.cu_lens(wl.total_lens)
+    qd, qp = wl.queries(0)
+    q = np.concatenate([qd, qp])
+    say(f"[prefill] many blocks {shape}: {wl.num_seqs} seqs, {q.shape[0]} rows")
+    out = torch.full(q.shape, int(W.BF16_NAN), dtype=torch.int16, device="cuda")
+    P.prefill_varlen(dev_bits(q), g.k, g.v, dev_i32(wl.block_tables), dev_i32(cq), dev_i32(ck),
+                     int(wl.new_lens.max()), int(wl.total_lens.max()), page_size=wl.page_size,
+                     scale=wl.scale, window=wl.window, out=out)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_varlen(q, o.k, o.v, wl.block_tables, cq, ck, wl.page_size, wl.scale,
+                                wl.window)
+    check_close(host_bits(out), ref, f"many blocks {shape}")
+
+
 def test_prefill_edge_cases(P):
     # ragged lengths around tile sizes, an empty sequence, a chunk after a prefix
     wl = W.make("mixed_step", decode_ctx=("fixed", ()), prefill_new=("fixed", (1, 31, 32, 0, 33, 127, 129)),
