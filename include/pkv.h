@@ -386,6 +386,42 @@ pkv_status pkv_prefill_varlen(const uint16_t* q, const uint16_t* k_pool, const u
                               uint16_t* out, hipStream_t stream);
 
 /*
+ * pkv_prefill_varlen with each workgroup's keys cut into num_splits runs of
+ * whole key tiles (flash-decoding's split of the key range, applied to the
+ * varlen batch).  A short prefill whose workgroups are few (a handful of
+ * chunks with long cached prefixes under a sliding window fill a few dozen
+ * of the 256 compute units) spreads its key range over more workgroups;
+ * every (query row, head, split) leaves a partial (running max in log2
+ * units, sum, unnormalised accumulator) and a second launch merges them
+ * with the split-K combine of pkv_decode_combine, in fixed split order.
+ * One-row sequences in the batch are not split (split 0 carries the whole
+ * row).  The result equals pkv_prefill_varlen's within floating-point
+ * order, and is deterministic for a given num_splits.
+ *
+ * Arguments are those of pkv_prefill_varlen, plus:
+ *   num_splits       1..64; 1 is exactly pkv_prefill_varlen (no workspace)
+ *   workspace        device memory of at least
+ *                    pkv_prefill_split_workspace_bytes(total_q, num_q_heads,
+ *                    head_dim, num_splits) bytes, owned by the caller,
+ *                    overwritten (it needs no clearing); used only when
+ *                    num_splits > 1
+ * Errors: as pkv_prefill_varlen; BAD_SHAPE for num_splits outside 1..64;
+ * UNSUPPORTED for num_splits > 1 at head_dim 512; NULL_ARG or
+ * WORKSPACE_TOO_SMALL for the workspace.
+ */
+size_t pkv_prefill_split_workspace_bytes(int32_t total_q, int32_t num_q_heads, int32_t head_dim,
+                                         int32_t num_splits);
+pkv_status pkv_prefill_varlen_split(const uint16_t* q, const uint16_t* k_pool,
+                                    const uint16_t* v_pool, const int32_t* block_tables,
+                                    int32_t max_pages_per_seq, const int32_t* cu_seq_lens_q,
+                                    const int32_t* cu_seq_lens_k, int32_t num_seqs, int32_t total_q,
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t page_size, int32_t num_pages, float scale,
+                                    int32_t window, int32_t num_splits, void* workspace,
+                                    size_t workspace_bytes, uint16_t* out, hipStream_t stream);
+
+/*
  * Step graphs.  The rollout engine captures one decode step per batch-size
  * bucket (1, 2, 4, 8, ...) during warm-up, dispatches each step to the
  * nearest bucket at or above the live batch, pads it with no-op rows and

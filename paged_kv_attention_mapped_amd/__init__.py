@@ -64,6 +64,8 @@ EXPORTS = (
     "pkv_decode_stream",
     "pkv_decode_stream_merge",
     "pkv_prefill_varlen",
+    "pkv_prefill_split_workspace_bytes",
+    "pkv_prefill_varlen_split",
     "pkv_graph_begin",
     "pkv_graph_end",
     "pkv_graph_launch",
@@ -108,6 +110,9 @@ _SIGS = {
     "pkv_decode_stream_merge": ([_P, _SZ, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "pkv_prefill_varlen": ([_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                             _I32, _I32, _I32, _F, _I32, _P, _P], _I32),
+    "pkv_prefill_split_workspace_bytes": ([_I32, _I32, _I32, _I32], _SZ),
+    "pkv_prefill_varlen_split": ([_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                  _I32, _I32, _I32, _I32, _F, _I32, _I32, _P, _SZ, _P, _P], _I32),
     "pkv_graph_begin": ([_P], _I32),
     "pkv_graph_end": ([_P, _P], _I32),
     "pkv_graph_launch": ([_P, _P], _I32),
@@ -441,6 +446,38 @@ def prefill_varlen(q, k_pool, v_pool, block_tables, cu_seq_lens_q, cu_seq_lens_k
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
         _ptr(cu_seq_lens_q), _ptr(cu_seq_lens_k), n, Tq, max_seqlen_q, max_seqlen_k, hq, hkv, d,
         page_size, num_pages, float(scale), window, _ptr(out), _stream(stream)))
+    return out
+
+
+def prefill_split_workspace_bytes(total_q, num_q_heads, head_dim, num_splits):
+    """Workspace bytes of ``pkv_prefill_varlen_split`` (0 when ``num_splits`` <= 1)."""
+    return int(lib().pkv_prefill_split_workspace_bytes(total_q, num_q_heads, head_dim, num_splits))
+
+
+def prefill_varlen_split(q, k_pool, v_pool, block_tables, cu_seq_lens_q, cu_seq_lens_k,
+                         max_seqlen_q, max_seqlen_k, *, page_size, num_splits, scale=None, window=0,
+                         out=None, workspace=None, stream=None):
+    """``pkv_prefill_varlen_split``: varlen prefill with each workgroup's keys cut into
+    ``num_splits`` runs and merged by the split-K combine; returns bf16 [Tq, Hq, D]."""
+    _bf16(q, "q"); _bf16(k_pool, "k_pool"); _bf16(v_pool, "v_pool")
+    _i32(block_tables, "block_tables"); _i32(cu_seq_lens_q, "cu_q"); _i32(cu_seq_lens_k, "cu_k")
+    Tq, hq, d = q.shape
+    hkv, num_pages, _ = _pool_shape(k_pool, page_size)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out is None:
+        out = torch.empty((Tq, hq, d), dtype=torch.bfloat16, device=q.device)
+    nbytes = prefill_split_workspace_bytes(Tq, hq, d, num_splits)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _dev(q, k_pool, v_pool, block_tables, cu_seq_lens_q, cu_seq_lens_k, out)
+    n = cu_seq_lens_q.numel() - 1
+    ws = _ptr(workspace) if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("pkv_prefill_varlen_split", lib().pkv_prefill_varlen_split(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
+        _ptr(cu_seq_lens_q), _ptr(cu_seq_lens_k), n, Tq, max_seqlen_q, max_seqlen_k, hq, hkv, d,
+        page_size, num_pages, float(scale), window, num_splits, ws, wsb, _ptr(out),
+        _stream(stream)))
     return out
 
 

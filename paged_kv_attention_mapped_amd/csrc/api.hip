@@ -44,6 +44,7 @@ constexpr int kStreamMaxSeqs = 2048;     // row lengths are scanned in LDS
 // workgroup per row with no second kernel: at that size a stream-K launch
 // is no faster and its merge launch costs more than the balance it buys.
 constexpr int kDirectMaxRows = 256;
+constexpr int kMaxPrefillSplits = 64;      // key splits per prefill workgroup
 constexpr int kStreamMinUnitsPerWave = 4;
 constexpr int kStreamWavesPerSimd = 2;   // matches the stream kernel's register budget
 
@@ -493,19 +494,30 @@ pkv_status pkv_decode_stream_merge(const void* workspace, size_t workspace_bytes
   return hip_status(launch_stream_merge(sa, head_dim, stream));
 }
 
-pkv_status pkv_prefill_varlen(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
-                              const int32_t* block_tables, int32_t max_pages_per_seq,
-                              const int32_t* cu_seq_lens_q, const int32_t* cu_seq_lens_k,
-                              int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
-                              int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads,
-                              int32_t head_dim, int32_t page_size, int32_t num_pages,
-                              float scale, int32_t window, uint16_t* out, hipStream_t stream) {
+static size_t split_region(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
+
+size_t pkv_prefill_split_workspace_bytes(int32_t total_q, int32_t num_q_heads, int32_t head_dim,
+                                         int32_t num_splits) {
+  if (total_q <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_splits <= 1) return 0;
+  const size_t cells = (size_t)total_q * num_q_heads * num_splits;
+  return 2 * split_region(cells * sizeof(float)) + cells * (size_t)head_dim * sizeof(float);
+}
+
+static pkv_status prefill_entry(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                                const int32_t* block_tables, int32_t max_pages_per_seq,
+                                const int32_t* cu_seq_lens_q, const int32_t* cu_seq_lens_k,
+                                int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                                int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t page_size, int32_t num_pages,
+                                float scale, int32_t window, int32_t num_splits, void* workspace,
+                                size_t workspace_bytes, uint16_t* out, hipStream_t stream) {
   if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 ||
-      max_pages_per_seq <= 0 || num_pages <= 0)
+      max_pages_per_seq <= 0 || num_pages <= 0 || num_splits < 1 || num_splits > kMaxPrefillSplits)
     return PKV_ERR_BAD_SHAPE;
   pkv_status st = check_heads(num_q_heads, num_kv_heads);
   if (st != PKV_OK) return st;
   if (!supported_dim(head_dim) || !supported_ps(page_size)) return PKV_ERR_UNSUPPORTED;
+  if (num_splits > 1 && head_dim == 512) return PKV_ERR_UNSUPPORTED;
   if ((int64_t)max_pages_per_seq * page_size > INT32_MAX) return PKV_ERR_BAD_SHAPE;
   if (num_seqs > 65535) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PKV_OK;
@@ -528,7 +540,47 @@ pkv_status pkv_prefill_varlen(const uint16_t* q, const uint16_t* k_pool, const u
   a.total_q = total_q;
   a.window = window;
   a.scale_log2 = scale * kLog2e;
+  a.nsplit = num_splits;
+  a.part_m = a.part_l = a.part_acc = nullptr;
+  if (num_splits > 1) {
+    if (!workspace) return PKV_ERR_NULL_ARG;
+    if (workspace_bytes < pkv_prefill_split_workspace_bytes(total_q, num_q_heads, head_dim, num_splits))
+      return PKV_ERR_WORKSPACE_TOO_SMALL;
+    const size_t cells = (size_t)total_q * num_q_heads * num_splits;
+    char* w = static_cast<char*>(workspace);
+    a.part_m = reinterpret_cast<float*>(w);
+    a.part_l = reinterpret_cast<float*>(w + split_region(cells * sizeof(float)));
+    a.part_acc = reinterpret_cast<float*>(w + 2 * split_region(cells * sizeof(float)));
+  }
   return hip_status(launch_prefill(a, num_seqs, max_seqlen_q, head_dim, page_size, stream));
+}
+
+pkv_status pkv_prefill_varlen(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                              const int32_t* block_tables, int32_t max_pages_per_seq,
+                              const int32_t* cu_seq_lens_q, const int32_t* cu_seq_lens_k,
+                              int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                              int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t page_size, int32_t num_pages,
+                              float scale, int32_t window, uint16_t* out, hipStream_t stream) {
+  return prefill_entry(q, k_pool, v_pool, block_tables, max_pages_per_seq, cu_seq_lens_q,
+                       cu_seq_lens_k, num_seqs, total_q, max_seqlen_q, max_seqlen_k, num_q_heads,
+                       num_kv_heads, head_dim, page_size, num_pages, scale, window, 1, nullptr, 0,
+                       out, stream);
+}
+
+pkv_status pkv_prefill_varlen_split(const uint16_t* q, const uint16_t* k_pool,
+                                    const uint16_t* v_pool, const int32_t* block_tables,
+                                    int32_t max_pages_per_seq, const int32_t* cu_seq_lens_q,
+                                    const int32_t* cu_seq_lens_k, int32_t num_seqs, int32_t total_q,
+                                    int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t page_size, int32_t num_pages, float scale,
+                                    int32_t window, int32_t num_splits, void* workspace,
+                                    size_t workspace_bytes, uint16_t* out, hipStream_t stream) {
+  return prefill_entry(q, k_pool, v_pool, block_tables, max_pages_per_seq, cu_seq_lens_q,
+                       cu_seq_lens_k, num_seqs, total_q, max_seqlen_q, max_seqlen_k, num_q_heads,
+                       num_kv_heads, head_dim, page_size, num_pages, scale, window, num_splits,
+                       workspace, workspace_bytes, out, stream);
 }
 
 }  // extern "C"

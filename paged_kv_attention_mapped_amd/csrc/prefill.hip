@@ -99,6 +99,9 @@ struct PrefillCfg {
 template <int D, int PS, int HW, int NW>
 __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, int head0,
                                            int q_row, int L, float* sm) {
+  // with key splits (a.nsplit > 1) the row is not split: this call writes
+  // the whole result as split 0's partial (max in log2 units, sum, and the
+  // unnormalised accumulator), the other splits write empty partials
   constexpr int G = HW < 2 ? 2 : HW;
   using W = WaveDecoder<D, PS, G, 16>;
   float* sm_m = sm;                 // [NW][G]
@@ -176,6 +179,15 @@ __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, 
         lsum = fmaf(wt, sm_l[ww * G + h], lsum);
       }
     }
+    if (a.nsplit > 1) {
+      const int64_t cell = ((int64_t)q_row * a.num_q_heads + head0 + h) * a.nsplit;
+      a.part_acc[cell * D + d] = o;
+      if (d == 0) {
+        a.part_m[cell] = Mx;
+        a.part_l[cell] = lsum;
+      }
+      continue;
+    }
     const float val = lsum > 0.f ? o / lsum : 0.f;
     a.out[((int64_t)q_row * a.num_q_heads + head0 + h) * D + d] = (uint16_t)f32_to_bf16(val);
   }
@@ -205,6 +217,10 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
     bz = (int)((rest / Y) * Z + (r - rest * Z));
     if (bz >= nqb) return;  // padding of the last group
   }
+  // key split (x extent = KV heads x head groups x splits)
+  const int X0 = a.num_kv_heads * HG;
+  const int split = bx / X0;
+  bx -= split * X0;
   const int j = by;
   const int hk = bx / HG;
   const int hg = bx - hk * HG;
@@ -215,9 +231,17 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   int Lk = a.cu_k[j + 1] - a.cu_k[j];
   Lk = min(Lk, a.max_pages * PS);
   if (Lq == 1) {
-    if (bz == 0)
-      decode_row<D, PS, HW, C::NW>(a, j, hk, hk * a.group + hg * HW, q_start, Lk,
-                                   reinterpret_cast<float*>(smem));
+    if (bz == 0) {
+      if (split == 0) {
+        decode_row<D, PS, HW, C::NW>(a, j, hk, hk * a.group + hg * HW, q_start, Lk,
+                                     reinterpret_cast<float*>(smem));
+      } else if (threadIdx.x < HW) {  // split > 0: an empty partial per head
+        const int64_t cell =
+            ((int64_t)q_start * a.num_q_heads + hk * a.group + hg * HW + threadIdx.x) * a.nsplit + split;
+        a.part_m[cell] = -INFINITY;
+        a.part_l[cell] = 0.f;
+      }
+    }
     return;
   }
   const int q0 = qb * C::BM;
@@ -253,8 +277,17 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   // keys any row of this workgroup may see
   const int wg_last = min(q0 + C::BM, Lq) - 1;
   const int pmin = shift + q0, pmax = shift + wg_last;
-  const int kstart = a.window > 0 ? max(0, pmin - a.window + 1) : 0;
-  const int kend = min(pmax + 1, Lk);  // exclusive
+  int kstart = a.window > 0 ? max(0, pmin - a.window + 1) : 0;
+  int kend = min(pmax + 1, Lk);  // exclusive
+  if (a.nsplit > 1 && kend > kstart) {
+    // this split's share of the workgroup's key tiles: contiguous runs of
+    // whole tiles, so no tile straddles two splits (an empty share leaves
+    // an empty partial)
+    const int tf = kstart / C::BN, tl = (kend - 1) / C::BN;
+    const int per = (tl - tf + a.nsplit) / a.nsplit;
+    kstart = max(kstart, (tf + split * per) * C::BN);
+    kend = min(kend, (tf + (split + 1) * per) * C::BN);
+  }
   // this wave's rows
   const int w_last = min(r0 + 31, Lq - 1);
   const int wpmin = shift + r0, wpmax = shift + w_last;
@@ -521,6 +554,23 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
 
   // ---- normalise and write: lane holds d = 32dt + 8(r/4) + 4hh + r%4 ----
   const float lt = half_sum(l_run);
+  if (a.nsplit > 1) {  // the split's partial: max in log2 units, sum, unnormalised accumulator
+    if (qrow < Lq) {
+      const int64_t cell = ((int64_t)(q_start + qrow) * a.num_q_heads + head) * a.nsplit + split;
+      float* pa = a.part_acc + cell * D + 4 * hh;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+          *reinterpret_cast<float4*>(pa + 32 * dt + 8 * rb) =
+              make_float4(acc[dt][4 * rb], acc[dt][4 * rb + 1], acc[dt][4 * rb + 2], acc[dt][4 * rb + 3]);
+      if (hh == 0) {
+        a.part_m[cell] = m_run == -INFINITY ? -INFINITY : m_run * c;
+        a.part_l[cell] = lt;
+      }
+    }
+    return;
+  }
   if (qrow < Lq) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     uint16_t* op = a.out + ((int64_t)(q_start + qrow) * a.num_q_heads + head) * D + 4 * hh;
@@ -544,7 +594,7 @@ hipError_t launch_p3(const PrefillArgs& a, int num_seqs, int max_q, hipStream_t 
   // (mixed decode/prefill steps) the first z slice, where one-row sequences
   // run, stays first in the dispatch order
   const int zg = nqb >= 2 * PKV_PREFILL_ZGROUP ? PKV_PREFILL_ZGROUP : 1;
-  dim3 grid(a.num_kv_heads * (a.group / HW), num_seqs, (nqb + zg - 1) / zg * zg);
+  dim3 grid(a.num_kv_heads * (a.group / HW) * a.nsplit, num_seqs, (nqb + zg - 1) / zg * zg);
   const size_t smem = C::LDS_BYTES;
   static std::atomic<uint64_t> lds_raised{0};
   const hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&prefill_kernel<D, PS, HW>),
@@ -594,11 +644,16 @@ hipError_t launch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, 
     b.scale_log2 = a.scale_log2;
     return launch_attn512(b, num_seqs, max_seqlen_q, page_size, st);
   }
+  hipError_t e;
   switch (head_dim) {
-    case 64: return launch_p1<64>(a, num_seqs, max_seqlen_q, page_size, st);
-    case 128: return launch_p1<128>(a, num_seqs, max_seqlen_q, page_size, st);
-    default: return launch_p1<256>(a, num_seqs, max_seqlen_q, page_size, st);
+    case 64: e = launch_p1<64>(a, num_seqs, max_seqlen_q, page_size, st); break;
+    case 128: e = launch_p1<128>(a, num_seqs, max_seqlen_q, page_size, st); break;
+    default: e = launch_p1<256>(a, num_seqs, max_seqlen_q, page_size, st); break;
   }
+  if (e != hipSuccess || a.nsplit <= 1) return e;
+  // key splits: merge every row's partials (the split-K combine, rows = packed query rows)
+  return launch_combine(a.part_m, a.part_l, a.part_acc, a.total_q, a.num_q_heads, head_dim, a.nsplit,
+                        a.out, st);
 }
 
 }  // namespace pkv

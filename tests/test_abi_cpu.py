@@ -36,6 +36,7 @@ def test_header_declares_the_entry_points():
         "pkv_graph_launch", "pkv_graph_nodes", "pkv_page_alloc", "pkv_page_free",
         "pkv_decode_stream", "pkv_decode_stream_merge", "pkv_decode_stream_waves",
         "pkv_decode_stream_workspace_bytes", "pkv_decode_workspace_bytes", "pkv_prefill_varlen",
+        "pkv_prefill_split_workspace_bytes", "pkv_prefill_varlen_split",
         "pkv_slot_mapping", "pkv_status_string"])
 
 
@@ -218,3 +219,28 @@ def test_head_dim_512_plans(P):
     assert P.lib().pkv_decode_stream_waves(4, 8, 1, 512, 32, 100, 0, None) == 3
     assert P.lib().pkv_decode_stream_workspace_bytes(8, 8, 1, 512) > 0
     assert P.decode_workspace_bytes(256, 8, 512, 1, 32, 8192) == 256 * 8 * c * 514 * 4
+
+
+def test_prefill_split_validation(P):
+    L = P.lib()
+    # workspace: two 256-byte aligned [Tq, Hq, S] float arrays, then [Tq, Hq, S, D] floats
+    cells = 576 * 8 * 4
+    assert L.pkv_prefill_split_workspace_bytes(576, 8, 256, 4) == 2 * ((cells * 4 + 255) // 256 * 256) + cells * 256 * 4
+    assert L.pkv_prefill_split_workspace_bytes(576, 8, 256, 1) == 0
+    assert L.pkv_prefill_split_workspace_bytes(0, 8, 256, 4) == 0
+    need = L.pkv_prefill_split_workspace_bytes(100, 8, 128, 3)
+    # q, k, v, bt, max_pages, cu_q, cu_k, N, Tq, max_q, max_k, Hq, Hkv, D, ps, P, scale, W, S, ws, ws_bytes, out, stream
+    args = [FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 2, 100, 60, 200, 8, 2, 128, 32, 64, 0.1, 0, 3,
+            FAKE, need, FAKE, None]
+    f = L.pkv_prefill_varlen_split
+    for s_bad in (0, -1, 65):
+        a = list(args); a[18] = s_bad
+        assert f(*a) == 2
+    a = list(args); a[13] = 512                        # head_dim 512 is not split
+    assert f(*a) == 3
+    a = list(args); a[19] = None                       # splitting needs the workspace
+    assert f(*a) == 1
+    a = list(args); a[20] = need - 1
+    assert f(*a) == 4
+    a = list(args); a[8] = 0; a[0] = None              # no rows: nothing to check or enqueue
+    assert f(*a) == 0

@@ -332,6 +332,58 @@ def test_mixed_single_launch(P, name):
         check_close(got[:wl.n_decode], refd, f"{name} L{layer} decode rows")
 
 
+@pytest.mark.parametrize("name", ["mixed_step", "window_shared"])
+@pytest.mark.parametrize("splits", [2, 4, 7])
+def test_prefill_split_parity(P, name, splits):
+    """pkv_prefill_varlen_split (each workgroup's keys in `splits` runs of
+    tiles, partials merged by the split-K combine) on a mixed batch: within
+    the bar of the oracle, and bit-identical on a second call."""
+    g = state(name)
+    wl = g.wl
+    o = OraclePools(wl)
+    cq, ck = wl.cu_lens(wl.new_lens), wl.cu_lens(wl.total_lens)
+    for layer in range(wl.num_layers):
+        qd, qp = wl.queries(layer)
+        q = np.concatenate([qd, qp])
+        say(f"[split prefill] {name} layer {layer}: {splits} splits")
+        args = (dev_bits(q), g.k, g.v, dev_i32(wl.block_tables), dev_i32(cq), dev_i32(ck),
+                int(wl.new_lens.max()), int(wl.total_lens.max()))
+        kw = dict(page_size=wl.page_size, num_splits=splits, scale=wl.scale, window=wl.window)
+        got = host_bits(P.prefill_varlen_split(*args, **kw))
+        again = host_bits(P.prefill_varlen_split(*args, **kw))
+        torch.cuda.synchronize()
+        ref = oracle.prefill_varlen(q, o.k, o.v, wl.block_tables, cq, ck, wl.page_size, wl.scale,
+                                    wl.window)
+        check_close(got, ref, f"{name} L{layer} {splits} splits")
+        assert np.array_equal(got, again)
+
+
+def test_prefill_split_many_blocks_every_row(P):
+    """Key splits on the batch of test_prefill_many_blocks_every_row (grouped
+    query blocks, decode rows, an empty prompt, chunks): every row written
+    and within the bar."""
+    cfg = W.Config("many_blocks", 20260101, 8, 2, 128, 32,
+                   decode_ctx=("fixed", (5, 300, 1000)),
+                   prefill_new=("fixed", (1100, 1, 64, 65, 0, 700, 1025, 33)),
+                   chunk=("uniform", 2, 200, 900, 1000))
+    wl = W.build(cfg)
+    g = GpuPools(wl)
+    g.write("prefix")
+    g.write("new")
+    o = OraclePools(wl)
+    cq, ck = wl.cu_lens(wl.new_lens), wl.cu_lens(wl.total_lens)
+    qd, qp = wl.queries(0)
+    q = np.concatenate([qd, qp])
+    out = torch.full(q.shape, int(W.BF16_NAN), dtype=torch.int16, device="cuda")
+    P.prefill_varlen_split(dev_bits(q), g.k, g.v, dev_i32(wl.block_tables), dev_i32(cq), dev_i32(ck),
+                           int(wl.new_lens.max()), int(wl.total_lens.max()), page_size=wl.page_size,
+                           num_splits=3, scale=wl.scale, window=wl.window, out=out)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_varlen(q, o.k, o.v, wl.block_tables, cq, ck, wl.page_size, wl.scale,
+                                wl.window)
+    check_close(host_bits(out), ref, "many blocks, 3 splits")
+
+
 @pytest.mark.parametrize("name", ["qwen3_decode", "window_shared"])
 def test_decode_split_partials(P, name):
     g = state(name)
