@@ -54,6 +54,10 @@ DESCRIPTIONS = {
     "full512_prefill": "8 prompts U[1024,4096], 8/1/512, page 32 (full attention, prefill only)",
 }
 
+# key splits of the single varlen launch per workload (pkv_prefill_varlen_split);
+# workloads not listed use one (pkv_prefill_varlen)
+PREFILL_SPLITS = {}
+
 
 def _log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -120,7 +124,7 @@ def prefill_bytes(wl) -> int:
 # the step on the GPU
 # ---------------------------------------------------------------------------
 class Step:
-    def __init__(self, wl, torch, P, num_splits=0, mixed="single"):
+    def __init__(self, wl, torch, P, num_splits=0, mixed="single", prefill_splits=1):
         self.wl, self.torch, self.P = wl, torch, P
         dev = torch.device("cuda")
         i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)  # noqa: E731
@@ -190,6 +194,10 @@ class Step:
             self.max_k = int(wl.total_lens[seqs].max())
             self.out_pre = torch.empty((wl.total_q(), wl.num_q_heads, wl.head_dim),
                                        dtype=torch.bfloat16, device=dev)
+            self.psplits = max(1, int(prefill_splits))
+            nb = P.prefill_split_workspace_bytes(wl.total_q(), wl.num_q_heads, wl.head_dim,
+                                                 self.psplits)
+            self.pws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
         self.q = []
         for layer in range(wl.num_layers):
             qd, qp = wl.queries(layer)
@@ -201,6 +209,11 @@ class Step:
             self.out_all = torch.empty((self.B + wl.total_q(), wl.num_q_heads, wl.head_dim),
                                        dtype=torch.bfloat16, device=dev)
             self.max_k_all = int(wl.total_lens.max())
+            # key splits of the single launch (pkv_prefill_varlen_split) and their workspace
+            self.psplits = max(1, int(prefill_splits))
+            nb = P.prefill_split_workspace_bytes(self.B + wl.total_q(), wl.num_q_heads,
+                                                 wl.head_dim, self.psplits)
+            self.pws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
 
     def run(self, ev=None, pev=None):
         """One step.  ``ev`` / ``pev`` = (before, after) events bracketing the layer-0 decode
@@ -213,10 +226,18 @@ class Step:
             for layer in range(wl.num_layers):
                 if ev is not None and layer == 0:
                     ev[0].record()
-                P.prefill_varlen(self.q_all[layer], self.k_pool, self.v_pool, self.bt,
-                                 self.cu_new_q, self.cu_new_k, self.max_new, self.max_k_all,
-                                 page_size=wl.page_size, scale=wl.scale, window=wl.window,
-                                 out=self.out_all)
+                if self.psplits > 1:
+                    P.prefill_varlen_split(self.q_all[layer], self.k_pool, self.v_pool, self.bt,
+                                           self.cu_new_q, self.cu_new_k, self.max_new,
+                                           self.max_k_all, page_size=wl.page_size,
+                                           num_splits=self.psplits, scale=wl.scale,
+                                           window=wl.window, out=self.out_all,
+                                           workspace=self.pws)
+                else:
+                    P.prefill_varlen(self.q_all[layer], self.k_pool, self.v_pool, self.bt,
+                                     self.cu_new_q, self.cu_new_k, self.max_new, self.max_k_all,
+                                     page_size=wl.page_size, scale=wl.scale, window=wl.window,
+                                     out=self.out_all)
                 if ev is not None and layer == 0:
                     ev[1].record()
             return
@@ -250,9 +271,16 @@ class Step:
             if self.N:
                 if pev is not None and layer == 0:
                     pev[0].record()
-                P.prefill_varlen(qp, self.k_pool, self.v_pool, self.bt_pre, self.cu_q, self.cu_k,
-                                 self.max_q, self.max_k, page_size=wl.page_size, scale=wl.scale,
-                                 window=wl.window, out=self.out_pre)
+                if self.psplits > 1:
+                    P.prefill_varlen_split(qp, self.k_pool, self.v_pool, self.bt_pre, self.cu_q,
+                                           self.cu_k, self.max_q, self.max_k,
+                                           page_size=wl.page_size, num_splits=self.psplits,
+                                           scale=wl.scale, window=wl.window, out=self.out_pre,
+                                           workspace=self.pws)
+                else:
+                    P.prefill_varlen(qp, self.k_pool, self.v_pool, self.bt_pre, self.cu_q,
+                                     self.cu_k, self.max_q, self.max_k, page_size=wl.page_size,
+                                     scale=wl.scale, window=wl.window, out=self.out_pre)
                 if pev is not None and layer == 0:
                     pev[1].record()
 
@@ -473,6 +501,9 @@ def main():
     ap.add_argument("--mixed", choices=["single", "separate"], default="single",
                     help="a step with decode rows and prefill rows: one varlen launch per layer "
                          "(decode rows as one-row sequences) or decode + prefill launches")
+    ap.add_argument("--prefill-splits", type=int, default=0,
+                    help="key splits of the single varlen launch (pkv_prefill_varlen_split); "
+                         "0: the workload's default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the long-prefill MFMA measurement")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
@@ -520,7 +551,8 @@ def main():
     wl = W.make(args.config)
     _log(f"[bench] setting up {args.config}: {DESCRIPTIONS[args.config]}")
     t0 = time.perf_counter()
-    st = Step(wl, torch, P, args.num_splits, args.mixed)
+    psplits = args.prefill_splits if args.prefill_splits > 0 else PREFILL_SPLITS.get(args.config, 1)
+    st = Step(wl, torch, P, args.num_splits, args.mixed, psplits)
     _log(f"[bench] set-up done in {time.perf_counter() - t0:.1f} s; warmup {args.warmup}, steps {args.steps}")
 
     for _ in range(args.warmup):
@@ -628,9 +660,12 @@ def main():
         fl = prefill_flops(wl)
         ach = kb / (kern_ms * 1e-3) / 1e9
         out["decode_tokens_per_s"] = round(st.B / (ms_step * 1e-3), 1)
-        out["decode_plan"] = {"method": "single varlen launch (decode rows as one-row sequences)"}
+        out["decode_plan"] = {"method": "single varlen launch (decode rows as one-row sequences)",
+                              "prefill_key_splits": st.psplits}
         out["roofline"] = {
-            "kernel": "prefill_kernel (decode rows + prefill rows in one launch)",
+            "kernel": ("prefill_kernel (decode rows + prefill rows in one launch)" if st.psplits == 1
+                       else f"prefill_kernel with {st.psplits} key splits + combine_kernel "
+                            "(decode rows + prefill rows)"),
             "bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
             "avg_kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": kb,
