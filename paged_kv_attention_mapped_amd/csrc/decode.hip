@@ -29,7 +29,7 @@ namespace {
 #define PKV_DECODE_UNIT 16          // tokens per step (half a 32-token page)
 #endif
 #ifndef PKV_DECODE_WAVES
-#define PKV_DECODE_WAVES 4          // waves per split-K workgroup
+#define PKV_DECODE_WAVES 8          // waves per split-K workgroup
 #endif
 #ifndef PKV_DECODE_OCCUPANCY
 #define PKV_DECODE_OCCUPANCY 2      // waves per SIMD the split-K registers are sized for
