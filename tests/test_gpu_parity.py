@@ -358,11 +358,13 @@ def test_prefill_split_parity(P, name, splits):
         assert np.array_equal(got, again)
 
 
-def test_prefill_split_many_blocks_every_row(P):
+@pytest.mark.parametrize("shape", [(8, 2, 128, 32, 0, 3), (4, 1, 64, 16, 0, 5), (8, 1, 256, 32, 300, 2)])
+def test_prefill_split_many_blocks_every_row(P, shape):
     """Key splits on the batch of test_prefill_many_blocks_every_row (grouped
     query blocks, decode rows, an empty prompt, chunks): every row written
-    and within the bar."""
-    cfg = W.Config("many_blocks", 20260101, 8, 2, 128, 32,
+    and within the bar, for three head shapes (one windowed)."""
+    hq, hkv, d, ps, window, splits = shape
+    cfg = W.Config("many_blocks", 20260101, hq, hkv, d, ps, window=window,
                    decode_ctx=("fixed", (5, 300, 1000)),
                    prefill_new=("fixed", (1100, 1, 64, 65, 0, 700, 1025, 33)),
                    chunk=("uniform", 2, 200, 900, 1000))
@@ -377,11 +379,11 @@ def test_prefill_split_many_blocks_every_row(P):
     out = torch.full(q.shape, int(W.BF16_NAN), dtype=torch.int16, device="cuda")
     P.prefill_varlen_split(dev_bits(q), g.k, g.v, dev_i32(wl.block_tables), dev_i32(cq), dev_i32(ck),
                            int(wl.new_lens.max()), int(wl.total_lens.max()), page_size=wl.page_size,
-                           num_splits=3, scale=wl.scale, window=wl.window, out=out)
+                           num_splits=splits, scale=wl.scale, window=wl.window, out=out)
     torch.cuda.synchronize()
     ref = oracle.prefill_varlen(q, o.k, o.v, wl.block_tables, cq, ck, wl.page_size, wl.scale,
                                 wl.window)
-    check_close(host_bits(out), ref, "many blocks, 3 splits")
+    check_close(host_bits(out), ref, f"many blocks {shape[:5]}, {splits} splits")
 
 
 @pytest.mark.parametrize("name", ["qwen3_decode", "window_shared"])
