@@ -394,9 +394,9 @@ pkv_status pkv_prefill_varlen(const uint16_t* q, const uint16_t* k_pool, const u
  * every (query row, head, split) leaves a partial (running max in log2
  * units, sum, unnormalised accumulator) and a second launch merges them
  * with the split-K combine of pkv_decode_combine, in fixed split order.
- * One-row sequences in the batch are not split (split 0 carries the whole
- * row).  The result equals pkv_prefill_varlen's within floating-point
- * order, and is deterministic for a given num_splits.
+ * A one-row sequence (a decode row) has its pages cut into num_splits runs
+ * the same way.  The result equals pkv_prefill_varlen's within
+ * floating-point order, and is deterministic for a given num_splits.
  *
  * Arguments are those of pkv_prefill_varlen, plus:
  *   num_splits       1..64; 1 is exactly pkv_prefill_varlen (no workspace)

@@ -98,10 +98,10 @@ struct PrefillCfg {
 // one launch.
 template <int D, int PS, int HW, int NW>
 __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, int head0,
-                                           int q_row, int L, float* sm) {
-  // with key splits (a.nsplit > 1) the row is not split: this call writes
-  // the whole result as split 0's partial (max in log2 units, sum, and the
-  // unnormalised accumulator), the other splits write empty partials
+                                           int q_row, int L, int split, float* sm) {
+  // with key splits (a.nsplit > 1) split s takes the s-th run of the row's
+  // pages and writes its partial (max in log2 units, sum, unnormalised
+  // accumulator); a split with no pages writes an empty partial
   constexpr int G = HW < 2 ? 2 : HW;
   using W = WaveDecoder<D, PS, G, 16>;
   float* sm_m = sm;                 // [NW][G]
@@ -115,8 +115,13 @@ __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, 
   wd.load_q(a.q + ((int64_t)q_row * a.num_q_heads + head0) * D, HW);
 
   const int first_key = a.window > 0 ? max(0, L - a.window) : 0;
-  const int p0 = first_key / PS;
-  const int pend = (L + PS - 1) / PS;
+  int p0 = first_key / PS;
+  int pend = (L + PS - 1) / PS;
+  if (a.nsplit > 1) {
+    const int per = (pend - p0 + a.nsplit - 1) / a.nsplit;
+    p0 = min(pend, p0 + split * per);
+    pend = min(pend, p0 + per);
+  }
   const uint16_t* kh = a.k_pool + (int64_t)hk * a.head_stride;
   const uint16_t* vh = a.v_pool + (int64_t)hk * a.head_stride;
   const int32_t* bt_row = a.block_tables + (int64_t)j * a.max_pages;
@@ -180,7 +185,7 @@ __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, 
       }
     }
     if (a.nsplit > 1) {
-      const int64_t cell = ((int64_t)q_row * a.num_q_heads + head0 + h) * a.nsplit;
+      const int64_t cell = ((int64_t)q_row * a.num_q_heads + head0 + h) * a.nsplit + split;
       a.part_acc[cell * D + d] = o;
       if (d == 0) {
         a.part_m[cell] = Mx;
@@ -231,17 +236,9 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   int Lk = a.cu_k[j + 1] - a.cu_k[j];
   Lk = min(Lk, a.max_pages * PS);
   if (Lq == 1) {
-    if (bz == 0) {
-      if (split == 0) {
-        decode_row<D, PS, HW, C::NW>(a, j, hk, hk * a.group + hg * HW, q_start, Lk,
-                                     reinterpret_cast<float*>(smem));
-      } else if (threadIdx.x < HW) {  // split > 0: an empty partial per head
-        const int64_t cell =
-            ((int64_t)q_start * a.num_q_heads + hk * a.group + hg * HW + threadIdx.x) * a.nsplit + split;
-        a.part_m[cell] = -INFINITY;
-        a.part_l[cell] = 0.f;
-      }
-    }
+    if (bz == 0)
+      decode_row<D, PS, HW, C::NW>(a, j, hk, hk * a.group + hg * HW, q_start, Lk, split,
+                                   reinterpret_cast<float*>(smem));
     return;
   }
   const int q0 = qb * C::BM;
