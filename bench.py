@@ -295,7 +295,7 @@ SCRUB_BYTES = 1 << 30
 
 
 def copy_ceiling(torch, nbytes=1 << 31, reps=5):
-    """Read+write GB/s of a plain 2 GiB device copy: the box's practical HBM
+    """Read+write GB/s of a plain 2 GiB device copy: the device's practical HBM
     ceiling, context for the roofline (whose peak stays at 8 TB/s)."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     src.fill_(1)
@@ -519,7 +519,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
     world = int(os.environ.get("WORLD_SIZE", "1"))
