@@ -270,7 +270,6 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
     }
   }
 
-
   // keys any row of this workgroup may see
   const int wg_last = min(q0 + C::BM, Lq) - 1;
   const int pmin = shift + q0, pmax = shift + wg_last;
