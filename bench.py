@@ -91,6 +91,13 @@ def decode_kernel_bytes(wl) -> int:
     return kv + q + 4 * int(pages.sum()) + 4 * wl.n_decode
 
 
+def fused_append_bytes(wl) -> int:
+    """The decode step's append done inside the decode launch: each new K/V
+    row read from k_new/v_new and written to the pool (the table entry is
+    already counted by the decode)."""
+    return 2 * 2 * wl.n_decode * wl.num_kv_heads * wl.head_dim * 2
+
+
 def decode_bytes(wl) -> int:
     return decode_kernel_bytes(wl) + wl.n_decode * wl.num_q_heads * wl.head_dim * 2  # + out
 
@@ -124,7 +131,8 @@ def prefill_bytes(wl) -> int:
 # the step on the GPU
 # ---------------------------------------------------------------------------
 class Step:
-    def __init__(self, wl, torch, P, num_splits=0, mixed="single", prefill_splits=1):
+    def __init__(self, wl, torch, P, num_splits=0, mixed="single", prefill_splits=1,
+                 append="fused"):
         self.wl, self.torch, self.P = wl, torch, P
         dev = torch.device("cuda")
         i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)  # noqa: E731
@@ -202,6 +210,14 @@ class Step:
         for layer in range(wl.num_layers):
             qd, qp = wl.queries(layer)
             self.q.append((bits(qd), bits(qp)))
+        # a decode-only step appends its new rows inside the decode launch
+        # (pkv_decode_append); the workspace is whatever the decomposition needs
+        self.fused = append == "fused" and self.B > 0 and self.N == 0
+        if self.fused:
+            need = P.decode_workspace_bytes(self.B, wl.num_q_heads, wl.head_dim, wl.num_kv_heads,
+                                            wl.page_size, self.max_len, wl.window, num_splits)
+            self.fws = torch.empty(max(1, need), dtype=torch.uint8, device=dev)
+            self.num_splits = num_splits
         # mixed steps in one varlen launch: decode rows are one-row sequences
         self.single = mixed == "single" and self.B > 0 and self.N > 0
         if self.single:
@@ -219,6 +235,25 @@ class Step:
         """One step.  ``ev`` / ``pev`` = (before, after) events bracketing the layer-0 decode
         kernel / prefill kernel."""
         P, wl = self.P, self.wl
+        if self.fused:
+            for layer in range(wl.num_layers):
+                qd, _ = self.q[layer]
+                if ev is not None and layer == 0:
+                    ev[0].record()
+                if layer == 0:   # later layers share the pool: no second append
+                    P.decode_append(qd, self.k_new, self.v_new, self.k_pool, self.v_pool,
+                                    self.bt_dec, self.seq_lens, self.max_len,
+                                    page_size=wl.page_size, scale=wl.scale, window=wl.window,
+                                    num_splits=self.num_splits, workspace=self.fws,
+                                    out=self.out_dec)
+                else:
+                    P.decode(qd, self.k_pool, self.v_pool, self.bt_dec, self.seq_lens,
+                             self.max_len, page_size=wl.page_size, scale=wl.scale,
+                             window=wl.window, num_splits=self.num_splits, workspace=self.fws,
+                             out=self.out_dec)
+                if ev is not None and layer == 0:
+                    ev[1].record()
+            return
         P.append_mapped(self.k_new, self.v_new, self.bt, self.cu_new_q, self.cu_new_k,
                         self.k_pool, self.v_pool, page_size=wl.page_size,
                         max_seqlen_q=self.max_new)
@@ -407,8 +442,9 @@ def _subset(wl, seqs):
 # ---------------------------------------------------------------------------
 # measured traffic (rocprofv3 counters, recorded under profiles/)
 # ---------------------------------------------------------------------------
-def recorded_traffic(config: str, src_hash: str):
-    path = os.path.join(ROOT, "profiles", f"{config}_decode_traffic.txt")
+def recorded_traffic(config: str, src_hash: str, fused: bool = False):
+    path = os.path.join(ROOT, "profiles",
+                        f"{config}_decode{'_append' if fused else ''}_traffic.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -426,26 +462,77 @@ def recorded_traffic(config: str, src_hash: str):
 
 # ---------------------------------------------------------------------------
 def prefill_measure(torch, P, iters=20, warmup=5):
+    """The long prefill's MFMA fraction: each launch timed by its own event
+    pair, back to back on resident K/V, and the same kernel inside the
+    long-prefill step (its prompts' rows appended just before it); medians
+    over the launches."""
     import workloads as W
     wl = W.make("long_prefill")
     st = Step(wl, torch, P)
     for _ in range(warmup):
         st.run_prefill()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(iters):
+
+    def evpair():
+        return (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    evs = [evpair() for _ in range(iters)]
+    for a, b in evs:
+        a.record()
         st.run_prefill()
-    b.record()
+        b.record()
     torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / iters
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    sevs = [evpair() for _ in range(iters)]
+    for pe in sevs:
+        st.run(None, pe)
+    torch.cuda.synchronize()
+    sms = np.array([a.elapsed_time(b) for a, b in sevs])
     fl = prefill_flops(wl)
-    tf = fl / (ms * 1e-3) / 1e12
+    med, smed = float(np.median(ms)), float(np.median(sms))
+    tf, stf = fl / (med * 1e-3) / 1e12, fl / (smed * 1e-3) / 1e12
     del st
     torch.cuda.empty_cache()
-    return {"workload": "long_prefill: " + DESCRIPTIONS["long_prefill"], "ms_per_call": round(ms, 4),
-            "tflops": round(tf, 2), "peak_tflops": BF16_PEAK_TFLOPS,
-            "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4), "flops_per_call": fl}
+    return {"workload": "long_prefill: " + DESCRIPTIONS["long_prefill"],
+            "ms_per_call": round(med, 4), "mean_ms": round(float(ms.mean()), 4),
+            "min_ms": round(float(ms.min()), 4), "tflops": round(tf, 2),
+            "peak_tflops": BF16_PEAK_TFLOPS, "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "flops_per_call": fl,
+            "timing": f"median of {iters} launches back to back, each between its own events",
+            "in_step": {"ms_per_call": round(smed, 4), "tflops": round(stf, 2),
+                        "mfma_frac": round(stf / BF16_PEAK_TFLOPS, 4),
+                        "timing": "median of the prefill launch inside the long-prefill step "
+                                  "(the prompts' rows appended first), its own events"}}
+
+
+def read_ceiling(torch, P, nbytes=4 << 30, reps=5):
+    """A plain streaming read of 4 GiB (pkv_stream_read): the device's
+    practical HBM read ceiling (context; the roofline's peak stays 8 TB/s).
+    The best workgroup count of a short sweep; median of ``reps`` reads."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(3)
+    cus, _ = P.device_info()
+    best = None
+    for per_cu in (4, 8, 16):
+        wg = cus * per_cu
+        sink = torch.empty(4 * wg, dtype=torch.int32, device="cuda")
+        for _ in range(2):
+            P.stream_read(buf, wg, sink)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a, b in evs:
+            a.record()
+            P.stream_read(buf, wg, sink)
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in evs]))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        if best is None or gbs > best["gbs"]:
+            best = {"gbs": round(gbs, 1), "bytes": nbytes, "workgroups": wg, "ms": round(ms, 4)}
+    del buf
+    torch.cuda.empty_cache()
+    best["frac_of_peak"] = round(best["gbs"] / HBM_PEAK_GBS, 4)
+    best["kernel"] = "stream_read_kernel (pkv_stream_read): 16-byte nontemporal loads, 8 in flight"
+    return best
 
 
 def alloc_measure(torch, P, num_seqs=256, iters=200):
@@ -503,6 +590,9 @@ def main():
     ap.add_argument("--mixed", choices=["single", "separate"], default="single",
                     help="a step with decode rows and prefill rows: one varlen launch per layer "
                          "(decode rows as one-row sequences) or decode + prefill launches")
+    ap.add_argument("--append", choices=["fused", "separate"], default="fused",
+                    help="a decode-only step: new rows written inside the decode launch "
+                         "(pkv_decode_append) or by a separate append launch first")
     ap.add_argument("--prefill-splits", type=int, default=0,
                     help="key splits of the single varlen launch (pkv_prefill_varlen_split); "
                          "0: the workload's default")
@@ -554,7 +644,7 @@ def main():
     _log(f"[bench] setting up {args.config}: {DESCRIPTIONS[args.config]}")
     t0 = time.perf_counter()
     psplits = args.prefill_splits if args.prefill_splits > 0 else PREFILL_SPLITS.get(args.config, 1)
-    st = Step(wl, torch, P, args.num_splits, args.mixed, psplits)
+    st = Step(wl, torch, P, args.num_splits, args.mixed, psplits, args.append)
     _log(f"[bench] set-up done in {time.perf_counter() - t0:.1f} s; warmup {args.warmup}, steps {args.steps}")
 
     for _ in range(args.warmup):
@@ -674,28 +764,55 @@ def main():
             "prefill_tflops": round(fl / (kern_ms * 1e-3) / 1e12, 2),
         }
     elif st.B:
-        kern_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
-        kb = decode_kernel_bytes(wl)
+        k_ms = np.array([a.elapsed_time(b) for a, b in evs])
+        kern_ms = float(k_ms.mean())
+        kb = decode_kernel_bytes(wl) + (fused_append_bytes(wl) if st.fused else 0)
         ach = kb / (kern_ms * 1e-3) / 1e9
         src_hash = _src_hash("decode.hip", "decode_core.h", "common.h")
-        traffic = recorded_traffic(args.config, src_hash)
+        traffic = recorded_traffic(args.config, src_hash, st.fused)
         out["decode_tokens_per_s"] = round(st.B / (ms_step * 1e-3), 1)
         out["decode_plan"] = ({"method": "stream", "stream_k_waves": st.nw} if st.nw else
                               {"method": "direct"} if st.S == 1 else
                               {"method": "split", "num_splits": st.S,
                                "pages_per_split": st.pps})
+        out["decode_plan"]["append"] = ("fused into the decode launch (pkv_decode_append)"
+                                        if st.fused else "separate launch (pkv_append_mapped)")
         kname = ("decode_stream_kernel (stream-K)" if st.nw else
                  "decode_kernel (split-K partials)" if st.S > 1 else "decode_kernel (direct)")
         if wl.head_dim == 512:
             kname = "attn512_kernel (head-dim split, " + (
                 "split-K partials)" if st.S > 1 else "direct)")
+        if st.fused:
+            kname = ("pkv_decode_append: " + kname +
+                     (" + stream_merge_kernel" if st.nw else " + combine_kernel" if st.S > 1 else "") +
+                     ", the step's new rows appended inside the launch")
         out["roofline"] = {
             "kernel": kname,
             "bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "avg_kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": kb,
+            "avg_kernel_ms": round(kern_ms, 5), "median_kernel_ms": round(float(np.median(k_ms)), 5),
+            "algorithmic_bytes_per_launch": kb,
             "kernel_source_sha256_16": src_hash,
         }
+        if not scrub:
+            # the same decode call with the last-level caches scrubbed before
+            # each launch (1 GiB write outside the events): shows whether the
+            # back-to-back figure leans on data left in the 256 MB MALL
+            sc = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda")
+            sev = [evpair() for _ in range(args.steps)]
+            for i in range(args.steps):
+                sc.fill_(i & 0xff)
+                st.run(sev[i])
+            torch.cuda.synchronize()
+            s_ms = np.array([a.elapsed_time(b) for a, b in sev])
+            del sc
+            torch.cuda.empty_cache()
+            sach = kb / (float(np.median(s_ms)) * 1e-3) / 1e9
+            out["roofline_scrubbed"] = {
+                "achieved": round(sach, 2), "frac": round(sach / HBM_PEAK_GBS, 4),
+                "median_kernel_ms": round(float(np.median(s_ms)), 5),
+                "note": "the decode call of the same step, each launch preceded by a 1 GiB "
+                        "cache scrub (outside its events); median over the launches"}
     if st.N and not st.single:
         pk_ms = float(np.mean([a.elapsed_time(b) for a, b in pevs]))
         fl = prefill_flops(wl)
@@ -720,6 +837,7 @@ def main():
         torch.cuda.empty_cache()
     out["page_allocator"] = alloc_measure(torch, P)
     out["hbm_copy_ceiling_gbs"] = copy_ceiling(torch)
+    out["hbm_read_ceiling"] = read_ceiling(torch, P)
     if not args.no_cpu_baseline:
         _log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, 256)

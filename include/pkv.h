@@ -79,6 +79,21 @@ const char* pkv_status_string(pkv_status s);
 pkv_status pkv_device_info(int32_t* compute_units, int32_t* max_clock_khz);
 
 /*
+ * Measurement aid: a plain streaming read of `bytes` bytes at `buffer`
+ * (device memory, 16-byte aligned, bytes a multiple of 16) by `workgroups`
+ * workgroups of 256 threads, each lane reading 16-byte chunks with the
+ * streaming (nontemporal) cache policy of the decode kernels and folding
+ * them into a checksum; workgroup w writes words 4w .. 4w+3 of `sink`
+ * (device memory of 4*workgroups uint32).  The time it takes is the
+ * device's practical HBM read ceiling, the context for the decode
+ * kernels' fraction of the 8 TB/s peak.  BAD_SHAPE for a size that is not
+ * a multiple of 16 or a workgroup count outside 1..2^20; bytes = 0
+ * enqueues nothing.
+ */
+pkv_status pkv_stream_read(const void* buffer, size_t bytes, int32_t workgroups, uint32_t* sink,
+                           hipStream_t stream);
+
+/*
  * Slot addressing: the physical pool row of every new token.
  *
  * Sequence j contributes Lq_j = cu_seq_lens_q[j+1]-cu_seq_lens_q[j] new
@@ -107,6 +122,10 @@ pkv_status pkv_slot_mapping(const int32_t* block_tables, int32_t max_pages_per_s
 /*
  * Append: bit-exact copy of new K/V rows into their pool slots,
  * k_pool[h, slot_mapping[t], :] = k_new[t, h, :] (and V), for every KV head.
+ * This is the engine's cache write at a physical row address (commit log
+ * 1847125, flex_attention paged-KV engine entry, "Files": k_cache[addr] =
+ * k_val), into the one contiguous pool the page table indexes (same entry,
+ * "Why this works" item 1).
  *
  *   k_new, v_new   bf16 [num_tokens, num_kv_heads, head_dim]   (device, read)
  *   slot_mapping   int32 [num_tokens]; a slot < 0 or >= num_slots is skipped
@@ -200,8 +219,12 @@ pkv_status pkv_page_free(const int32_t* seq_lens, const int32_t* release, int32_
 
 /*
  * Split-K planning.  Split-K cuts each row's keys into num_splits
- * partitions of pages_per_split logical pages (flash-decoding); the plan
- * depends only on host scalars.  num_splits_requested = 0 picks a count from
+ * partitions of pages_per_split logical pages: the flash-decoding split of
+ * a long context's keys over more workgroups than the batch has rows, which
+ * the decode path of the rollout engine needs at small batch (its decode
+ * attention runs over the pages of a block table, commit log 1847125,
+ * flex_attention paged-KV engine entry, "Why this works" items 1-2).  The
+ * plan depends only on host scalars.  num_splits_requested = 0 picks a count from
  * the grid size; 1 disables splitting.  Writes the plan through the two
  * output pointers (either may be NULL).
  */
@@ -227,7 +250,18 @@ pkv_status pkv_decode_method(int32_t num_seqs, int32_t num_q_heads, int32_t num_
                              int32_t window, int32_t num_splits_requested, int32_t* method,
                              int32_t* count);
 
-/* Bytes of workspace pkv_decode needs for these arguments (0 when it needs none). */
+/*
+ * Bytes of device workspace pkv_decode (and pkv_decode_append) needs for
+ * these arguments: the partials of the decomposition pkv_decode_method
+ * picks (split-K partials, or stream-K partials and merge descriptors; the
+ * flash-decoding split of the keys, sized from host scalars only as the
+ * engine's capture-time reservation needs, commit log 1847125,
+ * flex_attention paged-KV engine entry, "Why this works" item 3).  The
+ * decomposition depends on the KV-head count (stream-K counts units per KV
+ * head and splits wide query-head groups) and on the window (it bounds the
+ * pages a row's keys span), so both are arguments.  Returns 0 when no
+ * workspace is needed or an argument is invalid.
+ */
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                   int32_t num_kv_heads, int32_t page_size, int32_t max_seq_len,
                                   int32_t window, int32_t num_splits_requested);
@@ -269,7 +303,46 @@ pkv_status pkv_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t*
                       uint16_t* out, hipStream_t stream);
 
 /*
- * Decode, split-K half: for split s of row b, over the allowed keys on
+ * Decode step with its append fused in: what pkv_append_mapped of one new
+ * token per row followed by pkv_decode computes, in the decode launch.  The
+ * engine writes the new token's K/V into the cache from inside its captured
+ * decode step (commit log 1847125, flex_attention paged-KV engine entry,
+ * "Files": the in-kernel k_cache[addr] = k_val write; "Why this works" item
+ * 3: the step replayed as one graph per batch-size bucket), and here that
+ * write happens in the decode kernel itself: the wave that attends a row's
+ * last page takes the new token's K and V from k_new / v_new rather than from
+ * the pool and writes them to the token's slot.  No other wave of the launch
+ * reads that pool row, so no ordering inside the launch is needed.
+ *
+ *   k_new, v_new   bf16 [num_seqs, num_kv_heads, head_dim] (device, read):
+ *                  row b's new token, at position seq_lens[b] - 1
+ *   k_pool, v_pool bf16 [num_kv_heads, num_pages*page_size, head_dim]
+ *                  (device, read, and the new rows written)
+ * Other arguments, the workspace and the result: as pkv_decode.
+ *
+ * Row b's new token goes to slot block_tables[b][p/page_size]*page_size +
+ * p%page_size with p = seq_lens[b] - 1, exactly as pkv_append_mapped with
+ * cu_seq_lens_q = 0, 1, .., num_seqs and cu_seq_lens_k = the running sum of
+ * seq_lens places it.  A row with seq_lens[b] == 0 (a padded graph-bucket
+ * row) appends nothing and is written as zeros; a row whose table entry for
+ * that page is unusable, or whose length exceeds its table, writes nothing
+ * to the pool.  At head_dim 512 the rows are appended by a launch of their
+ * own before the decode (same result).  num_pages*page_size must stay below
+ * 2^31.
+ */
+pkv_status pkv_decode_append(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                             uint16_t* k_pool, uint16_t* v_pool, const int32_t* block_tables,
+                             int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t page_size, int32_t num_pages, int32_t max_seq_len,
+                             float scale, int32_t window, int32_t num_splits, void* workspace,
+                             size_t workspace_bytes, uint16_t* out, hipStream_t stream);
+
+/*
+ * Decode, split-K half (the partial pass of flash-decoding over the
+ * block-table pages of each row, commit log 1847125, flex_attention
+ * paged-KV engine entry, "Why this works" items 1-2): for split s of row b,
+ * over the allowed keys on
  * logical pages [p0 + s*pages_per_split, p0 + (s+1)*pages_per_split) where
  * p0 is the page of the row's first allowed key (0 without a window),
  * writes in float32
@@ -292,8 +365,11 @@ pkv_status pkv_decode_split(const uint16_t* q, const uint16_t* k_pool, const uin
                             hipStream_t stream);
 
 /*
- * Decode, combine half: merges the partials of pkv_decode_split in a fixed
- * split order, out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s with
+ * Decode, combine half (the log-sum-exp merge of flash-decoding's
+ * partials, in a fixed order so that reruns are bit-identical: the engine's
+ * drift verification asserts deterministic inference, commit log 1847125,
+ * Gemma-4-E2B-it engine entry):
+ * merges the partials of pkv_decode_split in a fixed split order, out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s with
  * M = max_s m_s; a row whose splits are all empty is written as zeros.
  *   out  bf16 [num_seqs, num_q_heads, head_dim]
  */
@@ -302,7 +378,11 @@ pkv_status pkv_decode_combine(const float* part_m, const float* part_l, const fl
                               int32_t num_splits, uint16_t* out, hipStream_t stream);
 
 /*
- * Decode, stream-K half.  The units of the batch -- every logical page that
+ * Decode, stream-K half: the flash-decoding split of pkv_decode_split with
+ * the split points chosen over the whole batch instead of per row, so that
+ * a batch of mixed lengths (the continuous-batching decode step, commit log
+ * 1847125, flex_attention paged-KV engine entry, "Why this works" items
+ * 1-2) keeps every wave equally busy.  The units of the batch -- every logical page that
  * holds an allowed key, for every KV head of every row, ordered by row,
  * then KV head, then page -- are cut into num_waves contiguous ranges of
  * equal size (unit counts differ by at most one), one per persistent wave,
@@ -339,8 +419,9 @@ pkv_status pkv_decode_stream(const uint16_t* q, const uint16_t* k_pool, const ui
                              uint16_t* out, hipStream_t stream);
 
 /*
- * Decode, stream-K merge half: combines the pieces of every cut (row, KV
- * head) left by pkv_decode_stream (same workspace, num_waves and shapes),
+ * Decode, stream-K merge half (the same log-sum-exp merge as
+ * pkv_decode_combine, in fixed wave order): combines the pieces of every
+ * cut (row, KV head) left by pkv_decode_stream (same workspace, num_waves and shapes),
  * in wave order, into out.  Rows pkv_decode_stream finished are untouched.
  */
 pkv_status pkv_decode_stream_merge(const void* workspace, size_t workspace_bytes,

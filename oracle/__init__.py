@@ -9,6 +9,7 @@ from .reference import (  # noqa: F401
     allowed_keys,
     append,
     attend_rows,
+    attend_rows_matrix,
     bf16_to_f64,
     combine_partials,
     decode,

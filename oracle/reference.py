@@ -135,6 +135,45 @@ def attend_rows(q_rows, K, V, positions, scale, window) -> np.ndarray:
     return out
 
 
+def attend_rows_matrix(q_rows, K, V, positions, scale, window, block=512) -> np.ndarray:
+    """``attend_rows`` evaluated for many rows of a query head at once.
+
+    The same definition as ``attend_rows`` -- scores ``scale * (k . q)``
+    over the allowed keys of each row, the row maximum subtracted, the
+    exponentials normalised by their sum, KV head ``h // (Hq // Hkv)`` --
+    written with matrix products over a block of rows (``block`` rows at a
+    time bound the ``[rows, keys]`` score matrix); a key outside a row's
+    allowed set gets score ``-inf`` and so weight 0.  A row with no allowed
+    key is zero.  Used where a per-row loop would take too long (prompts of
+    thousands of rows).
+    """
+    R, Hq, D = q_rows.shape
+    Hkv = K.shape[0]
+    g = Hq // Hkv
+    pos = np.asarray(positions, dtype=np.int64)
+    out = np.zeros((R, Hq, D), dtype=np.float64)
+    for r0 in range(0, R, block):
+        p = pos[r0:r0 + block]
+        hi = int(min(K.shape[1], p.max() + 1)) if p.size else 0
+        if hi <= 0:
+            continue
+        keys = np.arange(hi, dtype=np.int64)
+        allowed = keys[None, :] <= p[:, None]
+        if window > 0:
+            allowed &= (p[:, None] - keys[None, :]) < window
+        has = allowed.any(axis=1)
+        for h in range(Hq):
+            kh = h // g
+            s = (q_rows[r0:r0 + block, h, :] @ K[kh, :hi, :].T) * scale
+            s = np.where(allowed, s, -np.inf)
+            m = np.where(has, s.max(axis=1), 0.0)
+            e = np.exp(s - m[:, None])
+            tot = e.sum(axis=1)
+            o = (e @ V[kh, :hi, :]) / np.where(has, tot, 1.0)[:, None]
+            out[r0:r0 + block, h, :] = np.where(has[:, None], o, 0.0)
+    return out
+
+
 def decode(q, k_pool, v_pool, block_tables, seq_lens, page_size, scale, window=0) -> np.ndarray:
     """One decode row per sequence: ``q [B, Hq, D]`` attends its ``seq_lens[b]``
     cached tokens (the new token included) at position ``seq_lens[b] - 1``."""

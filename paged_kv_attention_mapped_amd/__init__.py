@@ -25,6 +25,7 @@ __all__ = [
     "append_mapped",
     "capture_graph",
     "decode",
+    "decode_append",
     "decode_combine",
     "decode_method",
     "decode_plan",
@@ -40,6 +41,7 @@ __all__ = [
     "page_free",
     "prefill_varlen",
     "slot_mapping",
+    "stream_read",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -48,6 +50,7 @@ _LIB_PATH = os.path.join(_HERE, "libpkv.so")
 EXPORTS = (
     "pkv_status_string",
     "pkv_device_info",
+    "pkv_stream_read",
     "pkv_slot_mapping",
     "pkv_append",
     "pkv_append_mapped",
@@ -57,6 +60,7 @@ EXPORTS = (
     "pkv_decode_method",
     "pkv_decode_workspace_bytes",
     "pkv_decode",
+    "pkv_decode_append",
     "pkv_decode_split",
     "pkv_decode_combine",
     "pkv_decode_stream_waves",
@@ -90,6 +94,7 @@ _SZ = ctypes.c_size_t
 _SIGS = {
     "pkv_status_string": ([_I32], ctypes.c_char_p),
     "pkv_device_info": ([_P, _P], _I32),
+    "pkv_stream_read": ([_P, _SZ, _I32, _P, _P], _I32),
     "pkv_slot_mapping": ([_P, _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _P], _I32),
     "pkv_append": ([_P, _P, _P, _I32, _I32, _I32, _P, _P, _I64, _P], _I32),
     "pkv_append_mapped": ([_P, _P, _P, _I32, _P, _P] + [_I32] * 7 + [_P, _P, _P, _P], _I32),
@@ -100,6 +105,8 @@ _SIGS = {
     "pkv_decode_workspace_bytes": ([_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32], _SZ),
     "pkv_decode": ([_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                     _F, _I32, _I32, _P, _SZ, _P, _P], _I32),
+    "pkv_decode_append": ([_P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                           _I32, _F, _I32, _I32, _P, _SZ, _P, _P], _I32),
     "pkv_decode_split": ([_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                           _F, _I32, _I32, _I32, _P, _P, _P, _P], _I32),
     "pkv_decode_combine": ([_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P], _I32),
@@ -290,6 +297,17 @@ def device_info():
     return cus.value, khz.value
 
 
+def stream_read(buffer, workgroups, sink, stream=None):
+    """Streaming read of a device buffer (``pkv_stream_read``): the practical
+    HBM read ceiling; ``sink`` is int32/uint32 ``[4 * workgroups]``."""
+    _dev(buffer, sink)
+    if sink.numel() < 4 * workgroups:
+        raise ValueError("sink needs 4 words per workgroup")
+    _check("pkv_stream_read", lib().pkv_stream_read(
+        _ptr(buffer), buffer.numel() * buffer.element_size(), workgroups, _ptr(sink),
+        _stream(stream)))
+
+
 DECODE_METHODS = {0: "direct", 1: "split", 2: "stream"}
 
 
@@ -347,6 +365,39 @@ def decode(q, k_pool, v_pool, block_tables, seq_lens, max_seq_len, *, page_size,
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
         _ptr(seq_lens), B, hq, hkv, d, page_size, num_pages, max_seq_len, float(scale), window,
         num_splits, _ptr(workspace), wsb, _ptr(out), _stream(stream)))
+    return out
+
+
+def decode_append(q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens, max_seq_len, *,
+                  page_size, scale=None, window=0, num_splits=0, workspace=None, out=None,
+                  stream=None):
+    """Decode step with its append fused into the decode launch (``pkv_decode_append``).
+
+    Row ``b``'s new token (``k_new``/``v_new`` ``[B, Hkv, D]``) sits at position
+    ``seq_lens[b] - 1``: it is written to its pool slot and attended in the same
+    launch.  Returns bf16 ``[B, Hq, D]``.
+    """
+    _bf16(q, "q"); _bf16(k_new, "k_new"); _bf16(v_new, "v_new")
+    _bf16(k_pool, "k_pool"); _bf16(v_pool, "v_pool")
+    _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
+    B, hq, d = q.shape
+    hkv, num_pages, d2 = _pool_shape(k_pool, page_size)
+    if d2 != d or v_pool.shape != k_pool.shape or block_tables.shape[0] < B or seq_lens.numel() < B:
+        raise ValueError("shape mismatch")
+    if k_new.shape != (B, hkv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new / v_new must be [B, Hkv, D]")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=q.device)
+    need = decode_workspace_bytes(B, hq, d, hkv, page_size, max_seq_len, window, num_splits)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _dev(q, k_new, v_new, k_pool, v_pool, block_tables, seq_lens, out, workspace)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pkv_decode_append", lib().pkv_decode_append(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+        block_tables.shape[1], _ptr(seq_lens), B, hq, hkv, d, page_size, num_pages, max_seq_len,
+        float(scale), window, num_splits, _ptr(workspace), wsb, _ptr(out), _stream(stream)))
     return out
 
 

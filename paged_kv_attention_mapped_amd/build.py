@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
-SOURCES = ["alloc.hip", "api.hip", "append.hip", "attn512.hip", "decode.hip", "graph.hip", "prefill.hip"]
+SOURCES = ["alloc.hip", "api.hip", "append.hip", "attn512.hip", "decode.hip", "graph.hip",
+           "prefill.hip", "probe.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

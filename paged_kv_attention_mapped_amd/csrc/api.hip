@@ -96,6 +96,14 @@ const char* pkv_status_string(pkv_status s) {
   }
 }
 
+pkv_status pkv_stream_read(const void* buffer, size_t bytes, int32_t workgroups,
+                           uint32_t* sink, hipStream_t stream) {
+  if (workgroups <= 0 || workgroups > (1 << 20) || bytes % 16 != 0) return PKV_ERR_BAD_SHAPE;
+  if (bytes == 0) return PKV_OK;
+  if (!buffer || !sink) return PKV_ERR_NULL_ARG;
+  return hip_status(launch_stream_read(buffer, (int64_t)bytes, sink, workgroups, stream));
+}
+
 pkv_status pkv_device_info(int32_t* compute_units, int32_t* max_clock_khz) {
   if (compute_units == nullptr || max_clock_khz == nullptr) return PKV_ERR_NULL_ARG;
   int dev = 0, cus = 0, khz = 0;
@@ -307,8 +315,30 @@ static DecodeArgs decode_args(const uint16_t* q, const uint16_t* k_pool, const u
   a.pages_per_split = pps;
   a.window = window;
   a.scale_log2 = scale * kLog2e;
+  a.k_new = a.v_new = nullptr;
+  a.k_pool_w = a.v_pool_w = nullptr;
   return a;
 }
+
+// The decode step's new rows, when the append is fused into the decode.
+struct FusedAppend {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_pool;
+  uint16_t* v_pool;
+};
+
+static void set_fused(DecodeArgs& a, const FusedAppend* f) {
+  if (f == nullptr) return;
+  a.k_new = f->k_new;
+  a.v_new = f->v_new;
+  a.k_pool_w = f->k_pool;
+  a.v_pool_w = f->v_pool;
+}
+
+// forward declarations of the stream-K helpers below
+static void stream_heads(DecodeArgs& a, int head_dim);
+static void stream_layout(StreamArgs& sa, void* workspace, int num_waves, int group, int head_dim);
 
 pkv_status pkv_decode_split(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
                             const int32_t* block_tables, int32_t max_pages_per_seq,
@@ -347,13 +377,14 @@ pkv_status pkv_decode_combine(const float* part_m, const float* part_l, const fl
                                    num_splits, out, stream));
 }
 
-pkv_status pkv_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
-                      const int32_t* block_tables, int32_t max_pages_per_seq,
-                      const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
-                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
-                      int32_t num_pages, int32_t max_seq_len, float scale, int32_t window,
-                      int32_t num_splits, void* workspace, size_t workspace_bytes,
-                      uint16_t* out, hipStream_t stream) {
+// pkv_decode, and pkv_decode_append when `fused` is set.
+static pkv_status decode_impl(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                              const int32_t* block_tables, int32_t max_pages_per_seq,
+                              const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                              int32_t num_pages, int32_t max_seq_len, float scale, int32_t window,
+                              int32_t num_splits, void* workspace, size_t workspace_bytes,
+                              uint16_t* out, hipStream_t stream, const FusedAppend* fused) {
   pkv_status st = check_decode(q, k_pool, v_pool, block_tables, max_pages_per_seq, seq_lens,
                                num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
                                num_pages, max_seq_len);
@@ -363,36 +394,49 @@ pkv_status pkv_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t*
   st = pkv_decode_method(num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, max_seq_len,
                          window, num_splits, &method, &nw);
   if (st != PKV_OK) return st;
-  if (method == PKV_DECODE_STREAM) {
-    if (!out) return PKV_ERR_NULL_ARG;
-    if (!workspace) return PKV_ERR_NULL_ARG;
-    if (workspace_bytes <
-        pkv_decode_stream_workspace_bytes(nw, num_q_heads, num_kv_heads, head_dim))
-      return PKV_ERR_WORKSPACE_TOO_SMALL;
-    st = pkv_decode_stream(q, k_pool, v_pool, block_tables, max_pages_per_seq, seq_lens,
-                           num_seqs, num_q_heads, num_kv_heads, head_dim, page_size, num_pages,
-                           scale, window, nw, workspace, workspace_bytes, out, stream);
-    if (st != PKV_OK) return st;
-    return pkv_decode_stream_merge(workspace, workspace_bytes, nw, num_q_heads, num_kv_heads,
-                                   head_dim, out, stream);
-  }
-  int32_t s = 1, pps = 0;
-  st = pkv_decode_plan(num_seqs, num_kv_heads, page_size, max_seq_len, window,
-                       method == PKV_DECODE_DIRECT ? 1 : num_splits, &s, &pps);
-  if (st != PKV_OK) return st;
   if (num_seqs == 0) return PKV_OK;
   if (!out) return PKV_ERR_NULL_ARG;
+  int32_t s = 1, pps = 0;
+  size_t need = 0;
+  if (method == PKV_DECODE_STREAM) {
+    need = pkv_decode_stream_workspace_bytes(nw, num_q_heads, num_kv_heads, head_dim);
+  } else {
+    st = pkv_decode_plan(num_seqs, num_kv_heads, page_size, max_seq_len, window,
+                         method == PKV_DECODE_DIRECT ? 1 : num_splits, &s, &pps);
+    if (st != PKV_OK) return st;
+    if (s > 1)
+      need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, num_kv_heads, page_size,
+                                        max_seq_len, window, num_splits);
+  }
+  if (need > 0) {
+    if (!workspace) return PKV_ERR_NULL_ARG;
+    if (workspace_bytes < need) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  }
+  // head_dim 512 has no fused decode kernel: the step's rows are appended by
+  // a launch of their own first (same result)
+  if (fused != nullptr && head_dim == 512) {
+    const pkv_status ast = hip_status(launch_append_last(
+        fused->k_new, fused->v_new, block_tables, max_pages_per_seq, seq_lens, num_seqs, page_size,
+        num_pages, num_kv_heads, head_dim, fused->k_pool, fused->v_pool, stream));
+    if (ast != PKV_OK) return ast;
+    fused = nullptr;
+  }
   DecodeArgs a = decode_args(q, k_pool, v_pool, block_tables, max_pages_per_seq, seq_lens,
                              num_q_heads, num_kv_heads, head_dim, page_size, num_pages, scale,
                              window, s, pps);
-  if (s <= 1) {
-    a.out = out;
-    return hip_status(launch_decode(a, num_seqs, head_dim, page_size, false, stream));
+  set_fused(a, fused);
+  a.out = out;
+  if (method == PKV_DECODE_STREAM) {
+    StreamArgs sa;
+    sa.base = a;
+    sa.num_seqs = num_seqs;
+    stream_heads(sa.base, head_dim);
+    stream_layout(sa, workspace, nw, sa.base.group, head_dim);
+    st = hip_status(launch_decode_stream(sa, head_dim, page_size, stream));
+    if (st != PKV_OK) return st;
+    return hip_status(launch_stream_merge(sa, head_dim, stream));
   }
-  const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, num_kv_heads,
-                                                 page_size, max_seq_len, window, num_splits);
-  if (!workspace) return PKV_ERR_NULL_ARG;
-  if (workspace_bytes < need) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  if (s <= 1) return hip_status(launch_decode(a, num_seqs, head_dim, page_size, false, stream));
   const size_t cells = (size_t)num_seqs * num_q_heads * s;
   float* ws = static_cast<float*>(workspace);
   a.part_acc = ws;
@@ -402,6 +446,33 @@ pkv_status pkv_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t*
   if (r != PKV_OK) return r;
   return hip_status(launch_combine(a.part_m, a.part_l, a.part_acc, num_seqs, num_q_heads,
                                    head_dim, s, out, stream));
+}
+
+pkv_status pkv_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                      const int32_t* block_tables, int32_t max_pages_per_seq,
+                      const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                      int32_t num_pages, int32_t max_seq_len, float scale, int32_t window,
+                      int32_t num_splits, void* workspace, size_t workspace_bytes,
+                      uint16_t* out, hipStream_t stream) {
+  return decode_impl(q, k_pool, v_pool, block_tables, max_pages_per_seq, seq_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, page_size, num_pages, max_seq_len,
+                     scale, window, num_splits, workspace, workspace_bytes, out, stream, nullptr);
+}
+
+pkv_status pkv_decode_append(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
+                             uint16_t* k_pool, uint16_t* v_pool, const int32_t* block_tables,
+                             int32_t max_pages_per_seq, const int32_t* seq_lens, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t page_size, int32_t num_pages, int32_t max_seq_len,
+                             float scale, int32_t window, int32_t num_splits, void* workspace,
+                             size_t workspace_bytes, uint16_t* out, hipStream_t stream) {
+  if (num_seqs > 0 && (!k_new || !v_new)) return PKV_ERR_NULL_ARG;
+  if ((int64_t)num_pages * page_size > INT32_MAX) return PKV_ERR_BAD_SHAPE;
+  const FusedAppend f = {k_new, v_new, k_pool, v_pool};
+  return decode_impl(q, k_pool, v_pool, block_tables, max_pages_per_seq, seq_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, page_size, num_pages, max_seq_len,
+                     scale, window, num_splits, workspace, workspace_bytes, out, stream, &f);
 }
 
 pkv_status pkv_decode_stream_waves(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

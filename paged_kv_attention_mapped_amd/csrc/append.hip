@@ -123,7 +123,46 @@ __global__ __launch_bounds__(256) void append_mapped_kernel(
   }
 }
 
+// The decode step's append on its own: row b's one new token, at position
+// seq_lens[b] - 1, goes to its slot (what the fused decode does inside the
+// attention launch, for the shapes whose decode kernel does not fuse it).
+// One workgroup per row; threads stride over the 16-byte chunks of its
+// KV heads' rows.  A row with length 0, or whose page is past its table or
+// unusable, writes nothing.
+__global__ __launch_bounds__(256) void append_last_kernel(
+    const uint4* __restrict__ k_new, const uint4* __restrict__ v_new,
+    const int32_t* __restrict__ bt, int max_pages, const int32_t* __restrict__ seq_lens,
+    int page_size, int num_pages, unsigned per_token, unsigned chunks_per_row,
+    uint4* __restrict__ k_pool, uint4* __restrict__ v_pool, int64_t num_slots) {
+  const int b = blockIdx.x;
+  const int pos = seq_lens[b] - 1;
+  if (pos < 0 || pos / page_size >= max_pages) return;
+  const int phys = bt[(int64_t)b * max_pages + pos / page_size];
+  if (phys < 0 || phys >= num_pages) return;
+  const int64_t slot = (int64_t)phys * page_size + pos % page_size;
+  for (unsigned k = threadIdx.x; k < per_token; k += blockDim.x) {
+    const unsigned h = k / chunks_per_row;
+    const int64_t src = (int64_t)b * per_token + k;
+    const int64_t dst = ((int64_t)h * num_slots + slot) * chunks_per_row + (k - h * chunks_per_row);
+    k_pool[dst] = k_new[src];
+    v_pool[dst] = v_new[src];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_append_last(const uint16_t* k_new, const uint16_t* v_new, const int32_t* bt,
+                              int max_pages, const int32_t* seq_lens, int num_seqs, int page_size,
+                              int num_pages, int hkv, int d, uint16_t* k_pool, uint16_t* v_pool,
+                              hipStream_t st) {
+  const unsigned cpr = (unsigned)d / 8;
+  hipLaunchKernelGGL(append_last_kernel, dim3(num_seqs), dim3(256), 0, st,
+                     reinterpret_cast<const uint4*>(k_new), reinterpret_cast<const uint4*>(v_new),
+                     bt, max_pages, seq_lens, page_size, num_pages, (unsigned)hkv * cpr, cpr,
+                     reinterpret_cast<uint4*>(k_pool), reinterpret_cast<uint4*>(v_pool),
+                     (int64_t)num_pages * page_size);
+  return hipGetLastError();
+}
 
 hipError_t launch_append_mapped(const uint16_t* k_new, const uint16_t* v_new, const int32_t* bt,
                                 int max_pages, const int32_t* cu_q, const int32_t* cu_k,

@@ -76,8 +76,10 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a)
 
   int q_start, Lq, Lk;
   if (a.cu_q != nullptr) {
-    q_start = a.cu_q[j];
-    Lq = a.cu_q[j + 1] - q_start;
+    // clamped to the packed rows [0, total_q), so that no q read or out
+    // write leaves its buffer whatever cu_seq_lens_q holds
+    q_start = min(max(a.cu_q[j], 0), a.total_q);
+    Lq = min(max(a.cu_q[j + 1], q_start), a.total_q) - q_start;
     Lk = a.cu_k[j + 1] - a.cu_k[j];
   } else {
     q_start = j;

@@ -128,6 +128,14 @@ struct DecodeArgs {
   int pages_per_split;
   int window;
   float scale_log2;   // scale * log2(e)
+  // fused append (k_new != NULL): row b's new token, at position
+  // seq_lens[b] - 1, is attended from k_new / v_new [num_seqs, Hkv, D]
+  // instead of the pool, and the wave that attends it (for its first
+  // virtual KV head) also writes it to its pool slot
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_pool_w;  // the same pools, writable
+  uint16_t* v_pool_w;
 };
 
 hipError_t launch_slot_mapping(const int32_t* bt, int max_pages, const int32_t* cu_q,
@@ -144,6 +152,13 @@ hipError_t launch_page_alloc(const int32_t* cu_q, const int32_t* cu_k, int num_s
 hipError_t launch_page_free(const int32_t* seq_lens, const int32_t* release, int num_seqs,
                             int32_t* bt, int max_pages, int page_size, int32_t* free_pages,
                             int32_t* free_count, int num_pages, int32_t* status, hipStream_t st);
+hipError_t launch_append_last(const uint16_t* k_new, const uint16_t* v_new, const int32_t* bt,
+                              int max_pages, const int32_t* seq_lens, int num_seqs, int page_size,
+                              int num_pages, int hkv, int d, uint16_t* k_pool, uint16_t* v_pool,
+                              hipStream_t st);
+int stream_read_sink_words(int workgroups);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int workgroups,
+                              hipStream_t st);
 hipError_t launch_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* slots,
                          int num_tokens, int hkv, int d, uint16_t* k_pool, uint16_t* v_pool,
                          int64_t num_slots, hipStream_t st);
@@ -218,6 +233,7 @@ struct Attn512Args {
   int window;
   int num_splits;
   int pages_per_split;
+  int total_q;              // varlen rows: packed query rows (cu_q is clamped to it)
   float scale_log2;
 };
 hipError_t launch_attn512(const Attn512Args& a, int num_seqs, int max_rows, int page_size,

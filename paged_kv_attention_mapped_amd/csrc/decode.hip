@@ -61,8 +61,10 @@ void decode_kernel(DecodeArgs a) {
   wd.reset();
   wd.load_q(a.q + ((int64_t)b * a.num_q_heads + hk * g) * D, g);
 
-  int L = a.seq_lens[b];
-  L = max(0, min(L, a.max_pages * PS));
+  const int Lraw = a.seq_lens[b];
+  const int L = max(0, min(Lraw, a.max_pages * PS));
+  // fused append only for a row inside its table (a length past it writes nothing)
+  const bool fuse = a.k_new != nullptr && Lraw == L;
   const int first_key = a.window > 0 ? max(0, L - a.window) : 0;
   const int p0 = first_key / PS;
   const int pend = (L + PS - 1) / PS;
@@ -80,6 +82,8 @@ void decode_kernel(DecodeArgs a) {
   int phys_lane = 0;
   int tok_of[2] = {0, 0};
   bool ok_of[2] = {false, false};
+  int tn_of[2] = {-1, -1};       // fused append: the new token's index in the step, or -1
+  int64_t row_of[2] = {0, 0};    // pool row of the step's first token (within the head)
   auto load = [&](typename W::Buf& bf, int j, int slot) {
     const int i = j / W::UPP, part = j - i * W::UPP;
     if ((i & 63) == 0 && part == 0)
@@ -89,9 +93,19 @@ void decode_kernel(DecodeArgs a) {
     phys = ok_of[slot] ? phys : 0;  // an unusable entry reads page 0 and is masked out
     tok_of[slot] = (pa + w + NW * i) * PS + part * W::UT;
     const int64_t row = (int64_t)phys * PS + part * W::UT;
+    row_of[slot] = row;
+    const int t = L - 1 - tok_of[slot];
+    tn_of[slot] = (fuse && ok_of[slot] && t >= 0 && t < W::UT) ? t : -1;
     wd.load(bf, kh + row * D, vh + row * D);
   };
-  auto process = [&](const typename W::Buf& bf, int slot) {
+  auto process = [&](typename W::Buf& bf, int slot) {
+    if (tn_of[slot] >= 0) {  // the row's new token: from k_new / v_new, and written to the pool
+      const int tn = tn_of[slot];
+      const int64_t nrow = ((int64_t)b * a.num_kv_heads + hk) * D;
+      wd.inject(bf, tn, a.k_new + nrow, a.v_new + nrow);
+      const int64_t prow = (int64_t)hk * a.head_stride + (row_of[slot] + tn) * D;
+      wd.store_new(bf, tn, a.k_pool_w + prow, a.v_pool_w + prow);
+    }
     wd.process(bf, tok_of[slot], ok_of[slot] ? first_key : INT_MAX, L, a.scale_log2);
   };
   typename W::Buf b0, b1;
@@ -290,6 +304,8 @@ void decode_stream_kernel(StreamArgs sa) {
     Seg sg;
     int u, part, tok0;
     bool ok;
+    int tn;        // fused append: the row's new token's index in the step, or -1
+    int64_t hoff;  // pool element offset of the step's first token row
   };
   const int nsteps = (int)(u1 - u0) * W::UPP;
   auto load = [&](typename W::Buf& bf, StepInfo& si, int j) {
@@ -312,6 +328,9 @@ void decode_stream_kernel(StreamArgs sa) {
     si.tok0 = (ls.p0 + (u - ls.s0)) * PS + part * W::UT;
     const int64_t hoff =
         (int64_t)(ls.hk >> a.kv_shift) * a.head_stride + ((int64_t)phys * PS + part * W::UT) * D;
+    si.hoff = hoff;
+    const int t = ls.L - 1 - si.tok0;
+    si.tn = (a.k_new != nullptr && si.ok && t >= 0 && t < W::UT) ? t : -1;
     wd.load(bf, a.k_pool + hoff, a.v_pool + hoff);
   };
 
@@ -357,11 +376,23 @@ void decode_stream_kernel(StreamArgs sa) {
     }
   };
 
-  auto process = [&](const typename W::Buf& bf, const StepInfo& si) {
+  auto process = [&](typename W::Buf& bf, const StepInfo& si) {
     const Seg& sg = si.sg;
     if (si.part == 0 && (si.u == sg.s0 || si.u == u0)) {  // first step of the segment here
       wd.reset();
       wd.load_q(a.q + ((int64_t)sg.b * a.num_q_heads + sg.hk * g) * D, g);
+    }
+    // the row's new token: from k_new / v_new (only for a row inside its
+    // table: a length past it writes nothing)
+    if (si.tn >= 0 && a.seq_lens[sg.b] == sg.L) {
+      const int hkr = sg.hk >> a.kv_shift;
+      const int64_t nrow = ((int64_t)sg.b * (a.num_kv_heads >> a.kv_shift) + hkr) * D;
+      wd.inject(bf, si.tn, a.k_new + nrow, a.v_new + nrow);
+      // of the virtual heads sharing a KV head, the first one writes the pool
+      if ((sg.hk & ((1 << a.kv_shift) - 1)) == 0) {
+        const int64_t prow = si.hoff + (int64_t)si.tn * D;
+        wd.store_new(bf, si.tn, a.k_pool_w + prow, a.v_pool_w + prow);
+      }
     }
     wd.process(bf, si.tok0, si.ok ? sg.fk : INT_MAX, sg.L, a.scale_log2);
     if (si.part == W::UPP - 1 && (si.u == sg.s1 - 1 || si.u == u1 - 1)) finish(sg);

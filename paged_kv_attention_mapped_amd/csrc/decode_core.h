@@ -176,6 +176,46 @@ struct WaveDecoder {
     }
   }
 
+  // Fused append: token tn of a loaded step (0 <= tn < UT, wave-uniform)
+  // is the row's new token, whose K/V rows are read from knew / vnew (one
+  // KV head's D elements) instead of the pool.  The lanes whose operand
+  // slots hold that token reload them from there: four lanes for K (lane
+  // row n of tile ti is token 16ti + tok_a), one lane row for V (value i of
+  // lane row jj is token 4i + jj).
+  __device__ __forceinline__ void inject(Buf& bf, int tn, const uint16_t* knew,
+                                         const uint16_t* vnew) const {
+#pragma unroll
+    for (int ti = 0; ti < KT; ++ti)
+      if (16 * ti + tok_a == tn)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          bf.k[ti][kb] = *reinterpret_cast<const uint4*>(knew + 32 * kb + 8 * jj);
+#pragma unroll
+    for (int i = 0; i < TPR; ++i)
+      if (4 * i + jj == tn)
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch)
+          bf.v[i][ch] = *reinterpret_cast<const VChunk*>(vnew + CH * n + 16 * CH * ch);
+  }
+
+  // After inject: the same lanes write token tn's rows to its pool slot
+  // (kdst / vdst = the slot's row in the K / V pool).
+  __device__ __forceinline__ void store_new(const Buf& bf, int tn, uint16_t* kdst,
+                                            uint16_t* vdst) const {
+#pragma unroll
+    for (int ti = 0; ti < KT; ++ti)
+      if (16 * ti + tok_a == tn)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          *reinterpret_cast<uint4*>(kdst + 32 * kb + 8 * jj) = bf.k[ti][kb];
+#pragma unroll
+    for (int i = 0; i < TPR; ++i)
+      if (4 * i + jj == tn)
+#pragma unroll
+        for (int ch = 0; ch < NCH; ++ch)
+          *reinterpret_cast<VChunk*>(vdst + CH * n + 16 * CH * ch) = bf.v[i][ch];
+  }
+
   // Merge the four lane-row streams.  Afterwards every lane (jj, n) holds
   // the wave maximum M (log2 units) and sum of head n, and every lane row
   // holds the merged accumulator (relative to M).

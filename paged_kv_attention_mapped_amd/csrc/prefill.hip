@@ -231,10 +231,13 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   const int hg = bx - hk * HG;
   const int qb = nqb - 1 - bz;
 
-  const int q_start = a.cu_q[j];
-  const int Lq = a.cu_q[j + 1] - q_start;
+  // query rows of sequence j, clamped to the packed rows [0, total_q) so
+  // that no q read, out write or partial write leaves its buffer whatever
+  // cu_seq_lens_q holds
+  const int q_start = min(max(a.cu_q[j], 0), a.total_q);
+  const int Lq = min(max(a.cu_q[j + 1], q_start), a.total_q) - q_start;
   int Lk = a.cu_k[j + 1] - a.cu_k[j];
-  Lk = min(Lk, a.max_pages * PS);
+  Lk = max(0, min(Lk, a.max_pages * PS));
   if (Lq == 1) {
     if (bz == 0)
       decode_row<D, PS, HW, C::NW>(a, j, hk, hk * a.group + hg * HW, q_start, Lk, split,
@@ -637,6 +640,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, 
     b.group = a.group;
     b.window = a.window;
     b.num_splits = 1;
+    b.total_q = a.total_q;
     b.scale_log2 = a.scale_log2;
     return launch_attn512(b, num_seqs, max_seqlen_q, page_size, st);
   }

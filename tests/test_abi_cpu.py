@@ -30,14 +30,14 @@ def declared():
 
 def test_header_declares_the_entry_points():
     assert declared() == sorted([
-        "pkv_append", "pkv_append_mapped", "pkv_decode", "pkv_decode_combine",
+        "pkv_append", "pkv_append_mapped", "pkv_decode", "pkv_decode_append", "pkv_decode_combine",
         "pkv_decode_method", "pkv_decode_plan", "pkv_decode_split",
         "pkv_device_info", "pkv_graph_begin", "pkv_graph_destroy", "pkv_graph_end",
         "pkv_graph_launch", "pkv_graph_nodes", "pkv_page_alloc", "pkv_page_free",
         "pkv_decode_stream", "pkv_decode_stream_merge", "pkv_decode_stream_waves",
         "pkv_decode_stream_workspace_bytes", "pkv_decode_workspace_bytes", "pkv_prefill_varlen",
         "pkv_prefill_split_workspace_bytes", "pkv_prefill_varlen_split",
-        "pkv_slot_mapping", "pkv_status_string"])
+        "pkv_slot_mapping", "pkv_status_string", "pkv_stream_read"])
 
 
 def test_library_exports_every_declared_symbol(P):
@@ -81,6 +81,31 @@ def test_decode_validation(P):
     assert _decode(P, splits=2, ws=None) == 1
     assert _decode(P, splits=2, ws=FAKE, wsb=16) == 4
     assert _decode(P, B=0) == 0            # empty batch: nothing to do
+
+
+def _decode_append(P, **kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, k=FAKE, v=FAKE, bt=FAKE, maxp=4, lens=FAKE, B=2, hq=8,
+             hkv=2, d=128, ps=32, pages=10, maxlen=100, scale=1.0, window=0, splits=0, ws=None,
+             wsb=0, out=FAKE)
+    a.update(kw)
+    return P.lib().pkv_decode_append(a["q"], a["kn"], a["vn"], a["k"], a["v"], a["bt"], a["maxp"],
+                                     a["lens"], a["B"], a["hq"], a["hkv"], a["d"], a["ps"],
+                                     a["pages"], a["maxlen"], a["scale"], a["window"], a["splits"],
+                                     a["ws"], a["wsb"], a["out"], None)
+
+
+def test_decode_append_validation(P):
+    # the decode checks, plus the new rows
+    assert _decode_append(P, kn=None) == 1
+    assert _decode_append(P, vn=None) == 1
+    assert _decode_append(P, q=None) == 1
+    assert _decode_append(P, out=None) == 1
+    assert _decode_append(P, d=96) == 3
+    assert _decode_append(P, hq=6, hkv=4) == 2
+    assert _decode_append(P, splits=2, ws=None) == 1
+    assert _decode_append(P, splits=2, ws=FAKE, wsb=16) == 4
+    assert _decode_append(P, ps=32, pages=1 << 26) == 2     # slots past 2^31
+    assert _decode_append(P, B=0, kn=None, vn=None) == 0   # empty batch: nothing to do
 
 
 def test_prefill_and_append_validation(P):
@@ -129,6 +154,15 @@ def test_decode_plan(P):
         P.lib().pkv_decode_stream_workspace_bytes(nw, 32, 8, 128)
     assert P.decode_plan(4, 8, 32, 1000, 0, 7) == (7, 5)
     assert P.decode_plan(4, 8, 32, 1000, 0, 1)[0] == 1
+
+
+def test_stream_read_validation(P):
+    f = P.lib().pkv_stream_read
+    assert f(FAKE, 100, 4, FAKE, None) == 2          # not a multiple of 16
+    assert f(FAKE, 1024, 0, FAKE, None) == 2         # no workgroups
+    assert f(None, 1024, 4, FAKE, None) == 1
+    assert f(FAKE, 1024, 4, None, None) == 1
+    assert f(None, 0, 4, None, None) == 0            # nothing to read
 
 
 def test_device_info_rejects_null(P):

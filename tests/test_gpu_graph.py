@@ -55,6 +55,9 @@ class DecodeBuffers:
                       for b in BUCKETS}
         need = max(int(P.lib().pkv_decode_stream_workspace_bytes(n, hq, hkv, d))
                    for n in self.waves.values())
+        # the fused step's workspace (whatever decomposition pkv_decode picks)
+        need = max([need] + [P.decode_workspace_bytes(b, hq, d, hkv, ps, self.max_len, window)
+                             for b in BUCKETS])
         self.ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
     def step(self, bucket, k_pool, v_pool, out, ws=None):
@@ -69,8 +72,25 @@ class DecodeBuffers:
         P.decode_stream_merge(ws, out[:b], num_waves=self.waves[b], num_kv_heads=self.hkv)
 
 
+    def fused_step(self, bucket, k_pool, v_pool, out, ws=None):
+        """The decode step with the append fused into the decode launch."""
+        P, b = self.P, bucket
+        ws = self.ws if ws is None else ws
+        P.decode_append(self.q[:b], self.k_new[:b], self.v_new[:b], k_pool, v_pool, self.bt[:b],
+                        self.seq_lens[:b], self.max_len, page_size=self.ps, window=self.window,
+                        workspace=ws, out=out[:b])
+
+    def kernel_nodes(self, bucket, fused):
+        if not fused:
+            return 3                                  # append, stream-K decode, merge
+        m, _ = self.P.decode_method(bucket, self.hq, self.hkv, self.d, self.ps, self.max_len,
+                                    self.window)
+        return {"direct": 1, "stream": 2, "split": 2}[m]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["append_then_stream", "fused_append"])
 @pytest.mark.parametrize("name", sorted(GRAPH_SHAPES))
-def test_decode_step_graph_buckets(P, name):
+def test_decode_step_graph_buckets(P, name, fused):
     hq, hkv, d, ps, window = GRAPH_SHAPES[name]
     bmax, maxp = max(BUCKETS), 12
     rng = np.random.default_rng(zlib.crc32(name.encode()))
@@ -99,19 +119,21 @@ def test_decode_step_graph_buckets(P, name):
     e_out = torch.zeros_like(g_out)
     e_ws = torch.empty_like(buf.ws)
 
+    step = buf.fused_step if fused else buf.step
     s = torch.cuda.Stream()
     graphs = {}
     with torch.cuda.stream(s):
         for b in BUCKETS:   # warm-up launch before capture (zero-length rows, no tokens)
-            buf.step(b, gk, gv, g_out)
+            step(b, gk, gv, g_out)
         s.synchronize()
         for b in BUCKETS:
-            graphs[b] = P.capture_graph(lambda b=b: buf.step(b, gk, gv, g_out), s)
-            assert graphs[b].nodes() == (3, 0), graphs[b].nodes()   # kernels only
+            graphs[b] = P.capture_graph(lambda b=b: step(b, gk, gv, g_out), s)
+            # kernels only; with the fused append no separate append node
+            assert graphs[b].nodes() == (buf.kernel_nodes(b, fused), 0), graphs[b].nodes()
 
     for i, B in enumerate(STEP_BATCHES):
         bucket = min(b for b in BUCKETS if b >= B)
-        say(f"[graph] {name} step {i}: live batch {B} in bucket {bucket}")
+        say(f"[graph] {name} fused={fused} step {i}: live batch {B} in bucket {bucket}")
         # this step's inputs: live rows 0..B-1 get one new token; padded rows none
         q = W.bf16_bits(rng.standard_normal((bmax, hq, d), dtype=np.float32))
         kn = W.bf16_bits(rng.standard_normal((bmax, hkv, d), dtype=np.float32))
@@ -129,7 +151,7 @@ def test_decode_step_graph_buckets(P, name):
             g_out.fill_(1.0)
             e_out.fill_(1.0)
             graphs[bucket].launch(s)
-            buf.step(bucket, ek, ev, e_out, ws=e_ws)   # the same calls, eagerly
+            step(bucket, ek, ev, e_out, ws=e_ws)   # the same calls, eagerly
         s.synchronize()
 
         # graph replay == eager, bit for bit (outputs and pools)

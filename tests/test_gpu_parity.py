@@ -161,23 +161,6 @@ def test_append_mapped_edge_cases(P):
     assert np.array_equal(host_bits(gk), ok) and np.array_equal(host_bits(gv), ov)
 
 
-def test_append_large_pool(P):
-    g = state("large_decode")
-    wl = g.wl
-    say("[append] large_decode: written-row mask + sampled sequences")
-    written = (g.k != int(W.BF16_NAN)).any(dim=-1).cpu().numpy()    # [Hkv, slots]
-    cq, ck = wl.cu_lens(wl.total_lens), wl.cu_lens(wl.total_lens)
-    used = np.zeros(wl.num_slots, bool)
-    used[oracle.slot_mapping(wl.block_tables, cq, ck, wl.page_size)] = True
-    assert np.array_equal(written, np.broadcast_to(used, written.shape))
-    samp = np.random.default_rng(0).choice(wl.num_seqs, 6, replace=False)
-    o = OraclePools(wl, samp)
-    rows = np.flatnonzero((o.k[0] != W.BF16_NAN).any(-1))
-    assert rows.size == int(wl.total_lens[samp].sum())
-    assert np.array_equal(host_bits(g.k[:, rows]), o.k[:, rows])
-    assert np.array_equal(host_bits(g.v[:, rows]), o.v[:, rows])
-
-
 # ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
@@ -193,21 +176,6 @@ def test_decode_parity(P, name):
         ref = oracle.decode(qd, o.k, o.v, wl.block_tables[:wl.n_decode], wl.decode_seq_lens(),
                             wl.page_size, wl.scale, wl.window)
         check_close(got, ref, f"{name} L{layer} decode")
-
-
-def test_decode_large_sampled(P):
-    g = state("large_decode")
-    wl = g.wl
-    qd, _ = wl.queries(0)
-    say("[decode] large_decode full batch, auto split")
-    got = run_decode(P, g, qd)
-    samp = np.sort(np.random.default_rng(1).choice(wl.n_decode, 8, replace=False))
-    o = OraclePools(wl, samp)
-    ref = oracle.decode(qd[samp], o.k, o.v, wl.block_tables[samp], wl.decode_seq_lens()[samp],
-                        wl.page_size, wl.scale)
-    check_close(got[samp], ref, "large_decode sampled rows")
-    # rows the oracle did not compute: finite, and every row of the output written
-    assert np.all(np.isfinite(W.bf16_to_f32(got)))
 
 
 @pytest.mark.parametrize("splits", [1, 2, 7, 0])
@@ -445,6 +413,107 @@ def test_decode_page_permutation_bit_identical(P):
     assert np.array_equal(run_decode(P, g1, qd), run_decode(P, g2, qd))
 
 
+@pytest.mark.parametrize("name", ["mixed_step", "window_shared"])
+def test_prefill_page_permutation_bit_identical(P, name):
+    """Moving every page to another physical place (data moved, tables
+    rewritten) leaves the single mixed launch (decode rows + prompts or
+    chunks) and the split-key prefill bit-identical."""
+    wl = W.make(name)
+    g1 = state(name)
+    perm = np.random.default_rng(6).permutation(wl.num_pages).astype(np.int32)
+    wl2 = W.make(name)
+    wl2.block_tables = perm[wl.block_tables]
+    say(f"[prefill] page permutation: {name}")
+    g2 = GpuPools(wl2)
+    g2.write("prefix")
+    g2.write("new")
+    cq, ck = wl.cu_lens(wl.new_lens), wl.cu_lens(wl.total_lens)
+    for layer in range(wl.num_layers):
+        q = np.concatenate(wl.queries(layer))
+        outs = []
+        for g, w in ((g1, wl), (g2, wl2)):
+            a = (dev_bits(q), g.k, g.v, dev_i32(w.block_tables), dev_i32(cq), dev_i32(ck),
+                 int(wl.new_lens.max()), int(wl.total_lens.max()))
+            kw = dict(page_size=wl.page_size, scale=wl.scale, window=wl.window)
+            one = P.prefill_varlen(*a, **kw)
+            split = P.prefill_varlen_split(*a, num_splits=3, **kw)
+            torch.cuda.synchronize()
+            outs.append((host_bits(one), host_bits(split)))
+        assert np.array_equal(outs[0][0], outs[1][0]), f"{name} L{layer} single launch"
+        assert np.array_equal(outs[0][1], outs[1][1]), f"{name} L{layer} split-key prefill"
+
+
+CANARY = 0x5A5A
+
+
+def test_decode_writes_no_row_past_the_batch(P):
+    """Rows of `out` past the batch keep their contents, for every decomposition."""
+    g = state("qwen3_decode")
+    wl = g.wl
+    qd, _ = wl.queries(0)
+    lens = wl.decode_seq_lens()
+    B = wl.n_decode
+    for splits in (0, 1, 3):
+        full = torch.full((B + 4, wl.num_q_heads, wl.head_dim), CANARY, dtype=torch.int16,
+                          device="cuda")
+        say(f"[canary] decode num_splits={splits}")
+        P.decode(dev_bits(qd), g.k, g.v, dev_i32(wl.block_tables[:B]), dev_i32(lens),
+                 int(lens.max()), page_size=wl.page_size, scale=wl.scale, num_splits=splits,
+                 out=full[:B])
+        torch.cuda.synchronize()
+        assert torch.all(full[B:] == CANARY)
+        assert np.all(np.isfinite(W.bf16_to_f32(host_bits(full[:B]))))
+    # stream-K with an odd wave count, and its merge
+    full = torch.full((B + 4, wl.num_q_heads, wl.head_dim), CANARY, dtype=torch.int16,
+                      device="cuda")
+    say("[canary] stream-K decode, 37 waves")
+    _, ws = P.decode_stream(dev_bits(qd), g.k, g.v, dev_i32(wl.block_tables[:B]), dev_i32(lens),
+                            page_size=wl.page_size, num_waves=37, scale=wl.scale, out=full[:B])
+    P.decode_stream_merge(ws, full[:B], num_waves=37, num_kv_heads=wl.num_kv_heads)
+    torch.cuda.synchronize()
+    assert torch.all(full[B:] == CANARY)
+    assert np.all(np.isfinite(W.bf16_to_f32(host_bits(full[:B]))))
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_prefill_stays_inside_total_q(P, splits):
+    """cu_seq_lens_q running past total_q (a caller error) must not move any
+    access out of the buffers: q rows past total_q are never read (they hold
+    NaN, and every written row stays finite), out rows and workspace bytes
+    past their sizes keep their canaries."""
+    g = state("mixed_step")
+    wl = g.wl
+    cq = wl.cu_lens(wl.new_lens).copy()
+    ck = wl.cu_lens(wl.total_lens)
+    T = int(cq[-1])
+    bad = cq.copy()
+    bad[-1] += 40                       # the last sequence claims 40 rows past total_q
+    q_full = torch.full((T + 64, wl.num_q_heads, wl.head_dim), int(W.BF16_NAN), dtype=torch.int16,
+                        device="cuda")
+    q_full[:T] = dev_bits(np.concatenate(wl.queries(0)))
+    out_full = torch.full((T + 64, wl.num_q_heads, wl.head_dim), CANARY, dtype=torch.int16,
+                          device="cuda")
+    nb = P.prefill_split_workspace_bytes(T, wl.num_q_heads, wl.head_dim, splits)
+    ws_full = torch.full((nb + 4096,), 0x5A, dtype=torch.uint8, device="cuda")
+    say(f"[canary] prefill past total_q, splits={splits}")
+    P.prefill_varlen_split(q_full[:T], g.k, g.v, dev_i32(wl.block_tables), dev_i32(bad),
+                           dev_i32(ck), int(wl.new_lens.max()) + 40, int(wl.total_lens.max()),
+                           page_size=wl.page_size, num_splits=splits, scale=wl.scale,
+                           out=out_full[:T], workspace=ws_full[:nb] if nb else None)
+    torch.cuda.synchronize()
+    assert torch.all(out_full[T:] == CANARY)
+    assert torch.all(ws_full[nb:] == 0x5A)
+    got = host_bits(out_full[:T])
+    assert np.all(np.isfinite(W.bf16_to_f32(got)))
+    # the sequences before the last one are unaffected by its bad bound
+    o = OraclePools(wl)
+    n = wl.num_seqs - 1
+    q = np.concatenate(wl.queries(0))
+    ref = oracle.prefill_varlen(q[:cq[n]], o.k, o.v, wl.block_tables[:n], cq[:n + 1], ck[:n + 1],
+                                wl.page_size, wl.scale)
+    check_close(got[:cq[n]], ref, "rows before the bad sequence")
+
+
 def test_decode_edge_lengths(P):
     # L = 1 returns V exactly; L = 0 gives zeros; page-boundary lengths.
     wl = W.make("qwen3_decode", decode_ctx=("fixed", (0, 31, 32, 63, 64, 1023)), name="edges")
@@ -500,27 +569,6 @@ def test_prefill_parity(P, name):
                                     wl.cu_lens(wl.new_lens[seqs]), wl.cu_lens(wl.total_lens[seqs]),
                                     wl.page_size, wl.scale, wl.window)
         check_close(got, ref, f"{name} L{layer} prefill")
-
-
-def test_prefill_long_sampled_rows(P):
-    g = state("long_prefill")
-    wl = g.wl
-    _, qp = wl.queries(0)
-    say(f"[prefill] long_prefill Tq={qp.shape[0]}")
-    got = run_prefill(P, g, qp)
-    assert np.all(np.isfinite(W.bf16_to_f32(got)))
-    rng = np.random.default_rng(2)
-    cq = wl.prefill_cu_q()
-    for j in rng.choice(wl.n_prefill, 3, replace=False):
-        s = wl.n_decode + j
-        Lk = int(wl.total_lens[s])
-        K, V = wl.kv_seq(s)
-        rows = np.unique(np.concatenate([rng.integers(0, Lk, 24), [0, Lk - 1, 63, 64, 127]]))
-        rows = rows[rows < Lk]
-        ref = oracle.attend_rows(oracle.bf16_to_f64(qp[cq[j] + rows]),
-                                 oracle.bf16_to_f64(K).transpose(1, 0, 2),
-                                 oracle.bf16_to_f64(V).transpose(1, 0, 2), rows, wl.scale, 0)
-        check_close(got[cq[j] + rows], ref, f"long_prefill seq {j} rows")
 
 
 @pytest.mark.parametrize("shape", [(8, 2, 128, 32, 0), (4, 1, 64, 16, 0), (8, 1, 256, 32, 300)])

@@ -307,6 +307,50 @@ def test_brute_force_dense(Lq, Lk, hq, hkv, d, ps, window):
         np.testing.assert_allclose(dec, ref, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("Lq,Lk,hq,hkv,d,window,block", [
+    (1, 1, 1, 1, 8, 0, 512),
+    (5, 5, 2, 1, 8, 0, 2),
+    (7, 19, 4, 1, 16, 0, 3),
+    (9, 30, 4, 2, 8, 6, 4),
+    (3, 70, 4, 4, 32, 17, 512),
+    (40, 40, 4, 2, 16, 0, 16),
+])
+def test_matrix_form_matches_brute_force(Lq, Lk, hq, hkv, d, window, block):
+    # the matrix form of the row attention (used on long prompts) against the
+    # scalar-loop brute force on the logical arrays, with row blocks that cut
+    # the rows unevenly
+    rng = np.random.default_rng(200 + Lq * 3 + Lk)
+    K, V = _seq(rng, Lk, hkv, d)
+    q = W.bf16_bits(rng.standard_normal((Lq, hq, d)).astype(np.float32))
+    scale = 1.0 / math.sqrt(d)
+    got = oracle.attend_rows_matrix(oracle.bf16_to_f64(q), oracle.bf16_to_f64(K).transpose(1, 0, 2),
+                                    oracle.bf16_to_f64(V).transpose(1, 0, 2),
+                                    np.arange(Lk - Lq, Lk), scale, window, block=block)
+    ref = _brute(oracle.bf16_to_f64(q), oracle.bf16_to_f64(K), oracle.bf16_to_f64(V),
+                 Lq, Lk, scale, window)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_matrix_form_closed_forms():
+    rng = np.random.default_rng(21)
+    Lk, d = 33, 8
+    K, V = _seq(rng, Lk, 1, d)
+    Kf = oracle.bf16_to_f64(K).transpose(1, 0, 2)
+    Vf = oracle.bf16_to_f64(V).transpose(1, 0, 2)
+    # q = 0: row at position p averages keys 0..p (bottom-right alignment),
+    # or the last `window` of them
+    q0 = np.zeros((6, 2, d))
+    for window in (0, 5):
+        out = oracle.attend_rows_matrix(q0, Kf, Vf, np.arange(27, 33), 1.0, window, block=4)
+        for r, p in enumerate(range(27, 33)):
+            lo = 0 if window <= 0 else p - window + 1
+            np.testing.assert_allclose(out[r, 1], Vf[0, lo:p + 1].mean(0), rtol=1e-12)
+    # position 0 returns V[0] exactly; a negative position (no allowed key) is zero
+    qr = oracle.bf16_to_f64(W.bf16_bits(rng.standard_normal((2, 1, d)).astype(np.float32)))
+    out = oracle.attend_rows_matrix(qr, Kf, Vf, np.array([0, -1]), 0.3, 0)
+    assert np.array_equal(out[0, 0], Vf[0, 0]) and np.all(out[1] == 0)
+
+
 def test_brute_force_tiny_decode_config():
     wl = W.make("tiny_decode")
     kp = _pool(wl.num_kv_heads, wl.num_pages, wl.page_size, wl.head_dim)
