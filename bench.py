@@ -597,6 +597,8 @@ def main():
                     help="key splits of the single varlen launch (pkv_prefill_varlen_split); "
                          "0: the workload's default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the page-allocator timing and the copy / read ceilings")
     ap.add_argument("--no-prefill", action="store_true", help="skip the long-prefill MFMA measurement")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--scrub", choices=["auto", "on", "off"], default="auto",
@@ -835,9 +837,10 @@ def main():
     if scratch is not None:
         del scratch
         torch.cuda.empty_cache()
-    out["page_allocator"] = alloc_measure(torch, P)
-    out["hbm_copy_ceiling_gbs"] = copy_ceiling(torch)
-    out["hbm_read_ceiling"] = read_ceiling(torch, P)
+    if not args.no_extras:
+        out["page_allocator"] = alloc_measure(torch, P)
+        out["hbm_copy_ceiling_gbs"] = copy_ceiling(torch)
+        out["hbm_read_ceiling"] = read_ceiling(torch, P)
     if not args.no_cpu_baseline:
         _log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s)")
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget, 256)

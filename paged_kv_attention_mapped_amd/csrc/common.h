@@ -54,6 +54,22 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Wait for every vector memory access of this wave (vmcnt(0), other counters
+// untouched).  Placed at the end of a rarely taken branch that issues loads
+// (a block-table fetch, a query load), it keeps the compiler's per-register
+// wait bookkeeping exact on the paths that skip the branch: without it the
+// join of the two paths counts those loads as possibly pending, and every
+// later use of their registers waits for all loads in flight, including the
+// next step's prefetch.
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+// A wave-uniform 64-bit value, stated as such (kept in scalar registers).
+__device__ __forceinline__ int64_t uni64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Buffer resource over [p, p + bytes): loads through it are bounds-checked by
@@ -72,6 +88,14 @@ __device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, int byte
 }
 __device__ __forceinline__ void buffer_load(uint4& d, __amdgpu_buffer_rsrc_t r, int off) { d = buffer_load16(r, off); }
 __device__ __forceinline__ void buffer_load(uint2& d, __amdgpu_buffer_rsrc_t r, int off) { d = buffer_load8(r, off); }
+
+// Vector stores through a buffer resource (lanes past its range write nothing).
+__device__ __forceinline__ void buffer_store(__amdgpu_buffer_rsrc_t r, int byte_off, const uint4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, byte_off, 0, 0);
+}
+__device__ __forceinline__ void buffer_store(__amdgpu_buffer_rsrc_t r, int byte_off, const uint2& v) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, byte_off, 0, 0);
+}
 
 // Streaming loads (read once, not kept in cache): 16 and 8 bytes.
 __device__ __forceinline__ uint4 load_stream(const uint4* p) {

@@ -86,8 +86,10 @@ void decode_kernel(DecodeArgs a) {
   int64_t row_of[2] = {0, 0};    // pool row of the step's first token (within the head)
   auto load = [&](typename W::Buf& bf, int j, int slot) {
     const int i = j / W::UPP, part = j - i * W::UPP;
-    if ((i & 63) == 0 && part == 0)
+    if ((i & 63) == 0 && part == 0) {
       phys_lane = (i + lane < npw) ? bt_row[pa + w + NW * (i + lane)] : -1;
+      wait_vm_all();
+    }
     int phys = __builtin_amdgcn_readlane(phys_lane, i & 63);
     ok_of[slot] = phys >= 0 && phys < a.num_pages;
     phys = ok_of[slot] ? phys : 0;  // an unusable entry reads page 0 and is masked out
@@ -97,12 +99,17 @@ void decode_kernel(DecodeArgs a) {
     const int t = L - 1 - tok_of[slot];
     tn_of[slot] = (fuse && ok_of[slot] && t >= 0 && t < W::UT) ? t : -1;
     wd.load(bf, kh + row * D, vh + row * D);
+    // the row's new token: its lanes reload it from k_new / v_new (loads
+    // return in issue order, so these land after the pool's)
+    if (tn_of[slot] >= 0) {
+      const int64_t nrow = ((int64_t)b * a.num_kv_heads + hk) * D;
+      wd.inject(bf, tn_of[slot], a.k_new + nrow, a.v_new + nrow);
+      wait_vm_all();
+    }
   };
   auto process = [&](typename W::Buf& bf, int slot) {
-    if (tn_of[slot] >= 0) {  // the row's new token: from k_new / v_new, and written to the pool
+    if (tn_of[slot] >= 0) {  // ... and is written to the pool
       const int tn = tn_of[slot];
-      const int64_t nrow = ((int64_t)b * a.num_kv_heads + hk) * D;
-      wd.inject(bf, tn, a.k_new + nrow, a.v_new + nrow);
       const int64_t prow = (int64_t)hk * a.head_stride + (row_of[slot] + tn) * D;
       wd.store_new(bf, tn, a.k_pool_w + prow, a.v_pool_w + prow);
     }
@@ -218,7 +225,9 @@ void decode_stream_kernel(StreamArgs sa) {
   const int lane = threadIdx.x;
   const int Hkv = a.num_kv_heads, g = a.group;
   int* pre = smem;           // pre[b] = first unit of sequence b; pre[B] = U
-  int* lens = smem + B + 1;  // clamped lengths
+  // clamped lengths, negated when seq_lens[b] ran past the table (the fused
+  // append then writes nothing for that row)
+  int* lens = smem + B + 1;
 
   // ---- flattened unit counts: E_b pages per KV head, units = E_b * Hkv ----
   int carry = 0;
@@ -226,10 +235,11 @@ void decode_stream_kernel(StreamArgs sa) {
     const int b = b0 + lane;
     int v = 0;
     if (b < B) {
-      const int L = max(0, min(a.seq_lens[b], a.max_pages * PS));
+      const int raw = a.seq_lens[b];
+      const int L = max(0, min(raw, a.max_pages * PS));
       const int fk = a.window > 0 ? max(0, L - a.window) : 0;
       const int E = (L + PS - 1) / PS - fk / PS;
-      lens[b] = L;
+      lens[b] = raw > L ? -L : L;
       v = E * Hkv;
     }
 #pragma unroll
@@ -248,7 +258,7 @@ void decode_stream_kernel(StreamArgs sa) {
   if (lane < 2) sa.desc[(2 * w + lane) * kDescInts] = 0;
   // rows of empty sequences are zero
   for (int b = w; b < B; b += nw) {
-    if (lens[b] != 0) continue;
+    if (lens[b] != 0) continue;  // (a negated length is not 0 either)
     uint16_t* o = a.out + (int64_t)b * a.num_q_heads * D;
     for (int i = lane; i < a.num_q_heads * D; i += 64) o[i] = 0;
   }
@@ -262,6 +272,7 @@ void decode_stream_kernel(StreamArgs sa) {
   // ---- segments: (b, hk) with units [s0, s1) = its pages p0 .. ----------
   struct Seg {
     int b, hk, L, fk, p0, s0, s1;
+    bool fuse;  // the fused append may write this row's new token
   };
   // values read from LDS are per-lane registers; readfirstlane keeps the
   // (wave-uniform) segment bookkeeping in scalar registers
@@ -270,7 +281,9 @@ void decode_stream_kernel(StreamArgs sa) {
     Seg sg;
     sg.b = b;
     sg.hk = hk;
-    sg.L = uni(lens[b]);
+    const int lv = uni(lens[b]);
+    sg.L = lv < 0 ? -lv : lv;
+    sg.fuse = lv >= 0;
     sg.fk = a.window > 0 ? max(0, sg.L - a.window) : 0;
     sg.p0 = sg.fk / PS;
     const int pb0 = uni(pre[b]);
@@ -318,6 +331,7 @@ void decode_stream_kernel(StreamArgs sa) {
       tab_base = u;
       const int page = ls.p0 + (u - ls.s0) + lane;
       phys_lane = (u + lane < ls.s1) ? a.block_tables[(int64_t)ls.b * a.max_pages + page] : -1;
+      wait_vm_all();
     }
     int phys = __builtin_amdgcn_readlane(phys_lane, u - tab_base);
     si.ok = phys >= 0 && phys < a.num_pages;
@@ -332,38 +346,46 @@ void decode_stream_kernel(StreamArgs sa) {
     const int t = ls.L - 1 - si.tok0;
     si.tn = (a.k_new != nullptr && si.ok && t >= 0 && t < W::UT) ? t : -1;
     wd.load(bf, a.k_pool + hoff, a.v_pool + hoff);
+    // the row's new token (only for a row inside its table: a length past
+    // it writes nothing): its lanes reload it from k_new / v_new, after the
+    // pool loads (loads return in issue order)
+    if (si.tn >= 0 && ls.fuse) {
+      const int64_t nrow =
+          uni64(((int64_t)ls.b * (a.num_kv_heads >> a.kv_shift) + (ls.hk >> a.kv_shift)) * D);
+      wd.inject(bf, si.tn, a.k_new + nrow, a.v_new + nrow);
+      wait_vm_all();
+    } else {
+      si.tn = -1;
+    }
   };
 
+  // stores go through buffer resources with wave-uniform bases, so that no
+  // 64-bit lane address stays live across the streaming loop
   auto finish = [&](const Seg& sg) {
     float M, lsum;
     wd.merge_rows(M, lsum);
     if (sg.s0 >= u0 && sg.s1 <= u1) {  // the whole segment is here: final rows
       if (wd.jj == 0) {
-        uint16_t* o = a.out + ((int64_t)sg.b * a.num_q_heads + sg.hk * g) * D;
+        const auto orr = make_rsrc(
+            a.out + uni64(((int64_t)sg.b * a.num_q_heads + sg.hk * g) * D), g * D * 2);
         static_for<0, G>([&](auto hc) {
           constexpr int h = decltype(hc)::value;
           const float ls_h = row_bcast<h>(lsum);
-          if (h < g) {
-            const float inv = ls_h > 0.f ? 1.f / ls_h : 0.f;
-#pragma unroll
-            for (int e = 0; e < W::EPL; ++e)
-              o[h * D + wd.dim_of(e)] = (uint16_t)f32_to_bf16(wd.acc[h][e] * inv);
-          }
+          if (h < g) wd.template store_out<h>(orr, ls_h > 0.f ? 1.f / ls_h : 0.f);
         });
       }
       return;
     }
     const int slot = 2 * w + (sg.s0 <= u0 ? 0 : 1);
-    float* p = sa.part + (int64_t)slot * g * (D + 2);
+    const auto pr = make_rsrc(sa.part + (int64_t)slot * g * (D + 2), g * (D + 2) * 4);
     if (wd.jj == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-        if (h < g)
-#pragma unroll
-          for (int e = 0; e < W::EPL; ++e) p[h * D + wd.dim_of(e)] = wd.acc[h][e];
+      static_for<0, G>([&](auto hc) {
+        constexpr int h = decltype(hc)::value;
+        if (h < g) wd.template store_acc<h>(pr);
+      });
       if (wd.n < g) {
-        p[g * D + wd.n] = M;
-        p[g * D + g + wd.n] = lsum;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(M), pr, 4 * (g * D + wd.n), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lsum), pr, 4 * (g * D + g + wd.n), 0, 0);
       }
     }
     if (sg.s0 >= u0 && lane == 0) {  // first piece: describe the segment for the merge
@@ -381,18 +403,13 @@ void decode_stream_kernel(StreamArgs sa) {
     if (si.part == 0 && (si.u == sg.s0 || si.u == u0)) {  // first step of the segment here
       wd.reset();
       wd.load_q(a.q + ((int64_t)sg.b * a.num_q_heads + sg.hk * g) * D, g);
+      wait_vm_all();
     }
-    // the row's new token: from k_new / v_new (only for a row inside its
-    // table: a length past it writes nothing)
-    if (si.tn >= 0 && a.seq_lens[sg.b] == sg.L) {
-      const int hkr = sg.hk >> a.kv_shift;
-      const int64_t nrow = ((int64_t)sg.b * (a.num_kv_heads >> a.kv_shift) + hkr) * D;
-      wd.inject(bf, si.tn, a.k_new + nrow, a.v_new + nrow);
-      // of the virtual heads sharing a KV head, the first one writes the pool
-      if ((sg.hk & ((1 << a.kv_shift) - 1)) == 0) {
-        const int64_t prow = si.hoff + (int64_t)si.tn * D;
-        wd.store_new(bf, si.tn, a.k_pool_w + prow, a.v_pool_w + prow);
-      }
+    // the row's new token, injected at load time, is written to the pool by
+    // the first of the virtual heads that share its KV head
+    if (si.tn >= 0 && (sg.hk & ((1 << a.kv_shift) - 1)) == 0) {
+      const int64_t prow = uni64(si.hoff + (int64_t)si.tn * D);
+      wd.store_new(bf, si.tn, a.k_pool_w + prow, a.v_pool_w + prow);
     }
     wd.process(bf, si.tok0, si.ok ? sg.fk : INT_MAX, sg.L, a.scale_log2);
     if (si.part == W::UPP - 1 && (si.u == sg.s1 - 1 || si.u == u1 - 1)) finish(sg);

@@ -182,38 +182,41 @@ struct WaveDecoder {
   // slots hold that token reload them from there: four lanes for K (lane
   // row n of tile ti is token 16ti + tok_a), one lane row for V (value i of
   // lane row jj is token 4i + jj).
+  // Loads and stores go through buffer resources (a wave-uniform base in
+  // SGPRs, 32-bit lane offsets), so that no 64-bit lane address is kept
+  // live across the streaming loop.
   __device__ __forceinline__ void inject(Buf& bf, int tn, const uint16_t* knew,
                                          const uint16_t* vnew) const {
+    const auto kr = make_rsrc(knew, D * 2);
+    const auto vr = make_rsrc(vnew, D * 2);
 #pragma unroll
     for (int ti = 0; ti < KT; ++ti)
       if (16 * ti + tok_a == tn)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          bf.k[ti][kb] = *reinterpret_cast<const uint4*>(knew + 32 * kb + 8 * jj);
+        for (int kb = 0; kb < KB; ++kb) bf.k[ti][kb] = buffer_load16(kr, 2 * (32 * kb + 8 * jj));
 #pragma unroll
     for (int i = 0; i < TPR; ++i)
       if (4 * i + jj == tn)
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch)
-          bf.v[i][ch] = *reinterpret_cast<const VChunk*>(vnew + CH * n + 16 * CH * ch);
+        for (int ch = 0; ch < NCH; ++ch) buffer_load(bf.v[i][ch], vr, 2 * (CH * n + 16 * CH * ch));
   }
 
   // After inject: the same lanes write token tn's rows to its pool slot
   // (kdst / vdst = the slot's row in the K / V pool).
   __device__ __forceinline__ void store_new(const Buf& bf, int tn, uint16_t* kdst,
                                             uint16_t* vdst) const {
+    const auto kr = make_rsrc(kdst, D * 2);
+    const auto vr = make_rsrc(vdst, D * 2);
 #pragma unroll
     for (int ti = 0; ti < KT; ++ti)
       if (16 * ti + tok_a == tn)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          *reinterpret_cast<uint4*>(kdst + 32 * kb + 8 * jj) = bf.k[ti][kb];
+        for (int kb = 0; kb < KB; ++kb) buffer_store(kr, 2 * (32 * kb + 8 * jj), bf.k[ti][kb]);
 #pragma unroll
     for (int i = 0; i < TPR; ++i)
       if (4 * i + jj == tn)
 #pragma unroll
-        for (int ch = 0; ch < NCH; ++ch)
-          *reinterpret_cast<VChunk*>(vdst + CH * n + 16 * CH * ch) = bf.v[i][ch];
+        for (int ch = 0; ch < NCH; ++ch) buffer_store(vr, 2 * (CH * n + 16 * CH * ch), bf.v[i][ch]);
   }
 
   // Merge the four lane-row streams.  Afterwards every lane (jj, n) holds
@@ -238,6 +241,43 @@ struct WaveDecoder {
         acc[h][e] = v;
       }
     });
+  }
+
+  // Row h of the merged accumulator (lane row 0 after merge_rows), times
+  // inv, rounded to bf16 and stored at element h*D of the buffer: each lane
+  // writes its CH consecutive dims as one 16- or 8-byte store.
+  template <int H>
+  __device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t r, float inv) const {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int off = 2 * (H * D + CH * n + 16 * CH * c);
+      const float* x = acc[H] + c * CH;
+      if constexpr (CH == 8) {
+        buffer_store(r, off, make_uint4(pack_bf16x2(x[0] * inv, x[1] * inv),
+                                        pack_bf16x2(x[2] * inv, x[3] * inv),
+                                        pack_bf16x2(x[4] * inv, x[5] * inv),
+                                        pack_bf16x2(x[6] * inv, x[7] * inv)));
+      } else {
+        buffer_store(r, off, make_uint2(pack_bf16x2(x[0] * inv, x[1] * inv),
+                                        pack_bf16x2(x[2] * inv, x[3] * inv)));
+      }
+    }
+  }
+
+  // Row h of the merged accumulator as float32 at element h*D of the buffer.
+  template <int H>
+  __device__ __forceinline__ void store_acc(__amdgpu_buffer_rsrc_t r) const {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int off = 4 * (H * D + CH * n + 16 * CH * c);
+      const float* x = acc[H] + c * CH;
+#pragma unroll
+      for (int q = 0; q < CH / 4; ++q)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            u32x4{__float_as_uint(x[4 * q]), __float_as_uint(x[4 * q + 1]),
+                  __float_as_uint(x[4 * q + 2]), __float_as_uint(x[4 * q + 3])},
+            r, off + 16 * q, 0, 0);
+    }
   }
 
   // Head-dim index of accumulator element e of this lane.

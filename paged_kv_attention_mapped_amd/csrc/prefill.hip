@@ -133,8 +133,10 @@ __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, 
   bool ok_of[2] = {false, false};
   auto load = [&](typename W::Buf& bf, int i_step, int slot) {
     const int i = i_step / W::UPP, part = i_step - i * W::UPP;
-    if ((i & 63) == 0 && part == 0)
+    if ((i & 63) == 0 && part == 0) {
       phys_lane = (i + lane < npw) ? bt_row[p0 + w + NW * (i + lane)] : -1;
+      wait_vm_all();
+    }
     int phys = __builtin_amdgcn_readlane(phys_lane, i & 63);
     ok_of[slot] = phys >= 0 && phys < a.num_pages;
     phys = ok_of[slot] ? phys : 0;  // an unusable entry reads page 0 and is masked out
