@@ -303,6 +303,34 @@ pkv_status pkv_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t*
                       uint16_t* out, hipStream_t stream);
 
 /*
+ * pkv_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * caller passes inputs and outputs only; the decode partials (split-K
+ * partials, or stream-K partials and merge descriptors) live in a scratch
+ * array of 16 MiB in the library's device memory, one per GPU, held until
+ * the process ends.  The call allocates nothing and frees nothing; its
+ * first call on a device looks up that device's scratch address (make that
+ * call outside a capture).  Same arguments and results as pkv_decode,
+ * without the workspace: bit-identical to pkv_decode with a workspace of
+ * its own.  Returns PKV_ERR_WORKSPACE_TOO_SMALL, before any HIP call, when
+ * pkv_decode_workspace_bytes for these arguments exceeds 16 MiB (split-K
+ * over very large batches; stream-K of every supported shape fits on a
+ * device of up to 256 compute units).
+ *
+ * Every call on a GPU shares that GPU's scratch and rewrites what it reads,
+ * so nothing needs clearing between calls; calls that overlap in time on
+ * one GPU (several streams, or several threads) race on it and give
+ * unspecified results: keep them on one stream.
+ */
+pkv_status pkv_decode_noalloc(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                              const int32_t* block_tables, int32_t max_pages_per_seq,
+                              const int32_t* seq_lens, int32_t num_seqs,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t page_size, int32_t num_pages, int32_t max_seq_len,
+                              float scale, int32_t window, int32_t num_splits,
+                              uint16_t* out, hipStream_t stream);
+
+/*
  * Decode step with its append fused in: what pkv_append_mapped of one new
  * token per row followed by pkv_decode computes, in the decode launch.  The
  * engine writes the new token's K/V into the cache from inside its captured

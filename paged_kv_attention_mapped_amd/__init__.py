@@ -28,6 +28,7 @@ __all__ = [
     "decode_append",
     "decode_combine",
     "decode_method",
+    "decode_noalloc",
     "decode_plan",
     "decode_split",
     "decode_stream",
@@ -61,6 +62,7 @@ EXPORTS = (
     "pkv_decode_workspace_bytes",
     "pkv_decode",
     "pkv_decode_append",
+    "pkv_decode_noalloc",
     "pkv_decode_split",
     "pkv_decode_combine",
     "pkv_decode_stream_waves",
@@ -107,6 +109,8 @@ _SIGS = {
                     _F, _I32, _I32, _P, _SZ, _P, _P], _I32),
     "pkv_decode_append": ([_P, _P, _P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                            _I32, _F, _I32, _I32, _P, _SZ, _P, _P], _I32),
+    "pkv_decode_noalloc": ([_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                            _F, _I32, _I32, _P, _P], _I32),
     "pkv_decode_split": ([_P, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                           _F, _I32, _I32, _I32, _P, _P, _P, _P], _I32),
     "pkv_decode_combine": ([_P, _P, _P, _I32, _I32, _I32, _I32, _P, _P], _I32),
@@ -365,6 +369,28 @@ def decode(q, k_pool, v_pool, block_tables, seq_lens, max_seq_len, *, page_size,
         _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
         _ptr(seq_lens), B, hq, hkv, d, page_size, num_pages, max_seq_len, float(scale), window,
         num_splits, _ptr(workspace), wsb, _ptr(out), _stream(stream)))
+    return out
+
+
+def decode_noalloc(q, k_pool, v_pool, block_tables, seq_lens, max_seq_len, *, page_size,
+                   scale=None, window=0, num_splits=0, out=None, stream=None):
+    """``pkv_decode_noalloc``: decode with the library's own per-GPU scratch
+    for its partials (no workspace); returns bf16 [B, Hq, D] (``out`` may be
+    given, so that nothing is allocated)."""
+    _bf16(q, "q"); _bf16(k_pool, "k_pool"); _bf16(v_pool, "v_pool")
+    _i32(block_tables, "block_tables"); _i32(seq_lens, "seq_lens")
+    B, hq, d = q.shape
+    hkv, num_pages, d2 = _pool_shape(k_pool, page_size)
+    if d2 != d or v_pool.shape != k_pool.shape or block_tables.shape[0] < B or seq_lens.numel() < B:
+        raise ValueError("shape mismatch")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=q.device)
+    _dev(q, k_pool, v_pool, block_tables, seq_lens, out)
+    _check("pkv_decode_noalloc", lib().pkv_decode_noalloc(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), block_tables.shape[1],
+        _ptr(seq_lens), B, hq, hkv, d, page_size, num_pages, max_seq_len, float(scale), window,
+        num_splits, _ptr(out), _stream(stream)))
     return out
 
 

@@ -4,6 +4,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/pkv.h"
 #include "common.h"
@@ -458,6 +459,60 @@ pkv_status pkv_decode(const uint16_t* q, const uint16_t* k_pool, const uint16_t*
   return decode_impl(q, k_pool, v_pool, block_tables, max_pages_per_seq, seq_lens, num_seqs,
                      num_q_heads, num_kv_heads, head_dim, page_size, num_pages, max_seq_len,
                      scale, window, num_splits, workspace, workspace_bytes, out, stream, nullptr);
+}
+
+// Scratch of pkv_decode_noalloc: the decode partials (split-K partials, or
+// stream-K partials and merge descriptors) for callers that cannot allocate.
+// 16 MiB holds the stream-K workspace of every supported shape on a device
+// of up to 256 compute units (at most 15 MB, for a group of 7 at head_dim
+// 128).  Each device holds its own copy until the process ends.
+constexpr size_t kNoAllocScratchBytes = size_t{16} << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (the name is only a host-side stand-in for it).
+static pkv_status scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return PKV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return PKV_ERR_HIP;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return PKV_OK;
+}
+
+pkv_status pkv_decode_noalloc(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
+                              const int32_t* block_tables, int32_t max_pages_per_seq,
+                              const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                              int32_t num_pages, int32_t max_seq_len, float scale,
+                              int32_t window, int32_t num_splits, uint16_t* out,
+                              hipStream_t stream) {
+  pkv_status st = check_decode(q, k_pool, v_pool, block_tables, max_pages_per_seq, seq_lens,
+                               num_seqs, num_q_heads, num_kv_heads, head_dim, page_size,
+                               num_pages, max_seq_len);
+  if (st != PKV_OK) return st;
+  if (num_splits < 0) return PKV_ERR_BAD_SHAPE;
+  // sizes beyond the scratch are refused before any HIP call
+  const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, num_kv_heads,
+                                                 page_size, max_seq_len, window, num_splits);
+  if (need > kNoAllocScratchBytes) return PKV_ERR_WORKSPACE_TOO_SMALL;
+  if (num_seqs == 0) return PKV_OK;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_address(&ws);
+    if (st != PKV_OK) return st;
+  }
+  return decode_impl(q, k_pool, v_pool, block_tables, max_pages_per_seq, seq_lens, num_seqs,
+                     num_q_heads, num_kv_heads, head_dim, page_size, num_pages, max_seq_len,
+                     scale, window, num_splits, ws, need > 0 ? kNoAllocScratchBytes : 0, out,
+                     stream, nullptr);
 }
 
 pkv_status pkv_decode_append(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,

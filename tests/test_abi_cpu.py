@@ -30,7 +30,7 @@ def declared():
 
 def test_header_declares_the_entry_points():
     assert declared() == sorted([
-        "pkv_append", "pkv_append_mapped", "pkv_decode", "pkv_decode_append", "pkv_decode_combine",
+        "pkv_append", "pkv_append_mapped", "pkv_decode", "pkv_decode_append", "pkv_decode_combine", "pkv_decode_noalloc",
         "pkv_decode_method", "pkv_decode_plan", "pkv_decode_split",
         "pkv_device_info", "pkv_graph_begin", "pkv_graph_destroy", "pkv_graph_end",
         "pkv_graph_launch", "pkv_graph_nodes", "pkv_page_alloc", "pkv_page_free",
@@ -106,6 +106,27 @@ def test_decode_append_validation(P):
     assert _decode_append(P, splits=2, ws=FAKE, wsb=16) == 4
     assert _decode_append(P, ps=32, pages=1 << 26) == 2     # slots past 2^31
     assert _decode_append(P, B=0, kn=None, vn=None) == 0   # empty batch: nothing to do
+
+
+def test_decode_noalloc_validation(P):
+    L = P.lib()
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, maxp=4, lens=FAKE, B=2, hq=8, hkv=2, d=128,
+                 ps=32, pages=10, maxlen=100, scale=1.0, window=0, splits=0, out=FAKE)
+        a.update(kw)
+        return L.pkv_decode_noalloc(a["q"], a["k"], a["v"], a["bt"], a["maxp"], a["lens"], a["B"],
+                                    a["hq"], a["hkv"], a["d"], a["ps"], a["pages"], a["maxlen"],
+                                    a["scale"], a["window"], a["splits"], a["out"], None)
+    assert call(q=None) == 1
+    assert call(d=96) == 3
+    assert call(B=-1) == 2
+    assert call(splits=-1) == 2
+    assert call(B=0) == 0
+    # partials beyond the 16 MiB scratch are refused before any HIP call:
+    # 4096 rows x 32 heads x 64 splits x 130 floats
+    assert P.decode_workspace_bytes(4096, 32, 128, 8, 32, 65536, 0, 64) > 16 << 20
+    assert call(B=4096, hq=32, hkv=8, maxp=2048, maxlen=65536, splits=64) == 4
 
 
 def test_prefill_and_append_validation(P):
