@@ -32,7 +32,7 @@
  *
  * Supported shapes: head_dim in {64, 128, 256, 512} (512: the full-attention
  * layers of the dual-regime model, commit log 1847125, Gemma-4-E2B-it engine
- * entry, "Dual attention regimes"; no stream-K decode); page_size in {16, 32};
+ * entry, "Dual attention regimes"); page_size in {16, 32};
  * Hq a multiple of Hkv with Hq/Hkv <= 8.  Anything else returns
  * PKV_ERR_UNSUPPORTED before any HIP call.
  *
@@ -237,12 +237,12 @@ pkv_status pkv_decode_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t page_
  *   *method = PKV_DECODE_DIRECT  one workgroup per (sequence, KV head), one
  *                                kernel, no workspace (*count = 1);
  *             PKV_DECODE_SPLIT   split-K partials + combine (*count = splits);
- *             PKV_DECODE_STREAM  stream-K + merge (*count = persistent waves).
+ *             PKV_DECODE_STREAM  stream-K + merge (*count = persistent waves,
+ *                                or at head_dim 512 persistent workgroups).
  * With num_splits_requested = 0 a batch of at most 256 (sequence, KV head)
- * rows whose query-head group is not split in two by stream-K goes direct,
- * up to 2048 sequences go stream-K, larger batches split-K; head_dim 512
- * always takes split-K (direct when one split suffices).  Either output
- * pointer may be NULL.
+ * rows whose query-head group is not split in two by stream-K goes direct
+ * (not at head_dim 512, which always streams), up to 2048 sequences go
+ * stream-K, larger batches split-K.  Either output pointer may be NULL.
  */
 enum { PKV_DECODE_DIRECT = 0, PKV_DECODE_SPLIT = 1, PKV_DECODE_STREAM = 2 };
 pkv_status pkv_decode_method(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -425,7 +425,11 @@ pkv_status pkv_decode_combine(const float* part_m, const float* part_l, const fl
  * page again from L2), which keeps one wave's accumulators in registers.
  *
  *   num_waves   >= 1; pkv_decode_stream_waves gives the count pkv_decode
- *               uses (a few waves per compute unit of the current device)
+ *               uses (a few waves per compute unit of the current device).
+ *               At head_dim 512 the partition is over workgroups of four
+ *               waves instead (each wave owns 128 dims of every key, the
+ *               units are 32-key tiles, one workgroup per compute unit), and
+ *               num_waves counts those workgroups.
  *   workspace   pkv_decode_stream_workspace_bytes(num_waves, ...) bytes;
  *               holds partials and merge descriptors, and is fully rewritten
  *               by every call (no initialisation needed)

@@ -14,7 +14,7 @@ using namespace pkv;
 namespace {
 
 bool supported_dim(int d) { return d == 64 || d == 128 || d == 256 || d == 512; }
-bool stream_dim(int d) { return d == 64 || d == 128 || d == 256; }  // stream-K decode
+bool stream_dim(int d) { return supported_dim(d); }  // stream-K decode (512: per workgroup)
 bool supported_ps(int ps) { return ps == 16 || ps == 32; }
 
 pkv_status check_heads(int hq, int hkv) {
@@ -74,7 +74,8 @@ int device_cus() {
 // heads v*g' ..); only the pool addressing maps v back to KV head v >> 1.
 int stream_kv_shift(int num_q_heads, int num_kv_heads, int head_dim) {
   const int g = num_q_heads / num_kv_heads;
-  return (head_dim >= 128 && g > 4 && g % 2 == 0) ? 1 : 0;
+  // head_dim 512 keeps the whole group: its heads are MFMA columns
+  return (head_dim >= 128 && head_dim < 512 && g > 4 && g % 2 == 0) ? 1 : 0;
 }
 size_t stream_part_bytes(int num_waves, int group, int head_dim) {
   const size_t b = (size_t)2 * num_waves * group * (head_dim + 2) * sizeof(float);
@@ -235,7 +236,9 @@ pkv_status pkv_decode_method(int32_t num_seqs, int32_t num_q_heads, int32_t num_
   if (num_splits_requested == 0 && num_seqs > 0 && num_seqs <= kStreamMaxSeqs &&
       stream_dim(head_dim)) {
     const int shift = stream_kv_shift(num_q_heads, num_kv_heads, head_dim);
-    if (shift == 0 && (int64_t)num_seqs * num_kv_heads <= kDirectMaxRows) {
+    // (head_dim 512 always streams: its direct kernel runs one workgroup per
+    // row, too few to fill the device for the batches it serves)
+    if (shift == 0 && head_dim != 512 && (int64_t)num_seqs * num_kv_heads <= kDirectMaxRows) {
       m = PKV_DECODE_DIRECT;
       c = 1;
     } else {
@@ -538,9 +541,13 @@ pkv_status pkv_decode_stream_waves(int32_t num_seqs, int32_t num_q_heads, int32_
   if (hs != PKV_OK) return hs;
   if (!stream_dim(head_dim) || !supported_ps(page_size)) return PKV_ERR_UNSUPPORTED;
   const int64_t heads = (int64_t)num_kv_heads << stream_kv_shift(num_q_heads, num_kv_heads, head_dim);
-  const int64_t units = (int64_t)num_seqs * heads * key_pages(page_size, max_seq_len, window);
+  // units: pages (head_dim <= 256, one wave each) or 32-key tiles (head_dim
+  // 512, one workgroup of four waves per compute unit)
+  const int64_t units = (int64_t)num_seqs * heads *
+                        (head_dim == 512 ? key_pages(32, max_seq_len, window)
+                                         : key_pages(page_size, max_seq_len, window));
   const int per_simd = head_dim == 256 ? 1 : kStreamWavesPerSimd;
-  int64_t nw = (int64_t)device_cus() * 4 * per_simd;
+  int64_t nw = head_dim == 512 ? (int64_t)device_cus() : (int64_t)device_cus() * 4 * per_simd;
   const int64_t want = (units + kStreamMinUnitsPerWave - 1) / kStreamMinUnitsPerWave;
   if (want < nw) nw = want;
   if (nw < 1) nw = 1;

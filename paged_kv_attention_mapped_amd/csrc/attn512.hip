@@ -18,6 +18,13 @@
 //                 LDS and read transposed (ds_read_b64_tr_b16), and the
 //                 probabilities already sit in B-operand order because the
 //                 K rows are loaded in a permuted order.
+// For decode rows K and V are read from the pool with coalesced loads (each
+// instruction covers four rows of the wave's 256-byte slice) and staged in
+// LDS; the K operands of S^T are read back in MFMA order.  Loading K
+// straight in operand order makes every instruction touch 32 rows, 32 bytes
+// each, whose cache-line requests fill the compute unit's miss queue (twice
+// the decode time); varlen rows, with more MFMA work per tile, keep the
+// direct operand loads.
 // The 32 MFMA columns are (row, head) pairs of one KV group: R = 32/g rows
 // times the g query heads, so every K/V tile is read once for the whole
 // group.  A decode row is one row (g columns), a prefill workgroup R rows.
@@ -48,8 +55,13 @@ constexpr int kTile = 32;                    // keys per tile
 constexpr int kVStride = kSlice * 2 + 64;
 constexpr int kVBytes = kTile * kVStride;    // one wave's staged V tile
 constexpr int kSBytes = 64 * 16 * 4;         // one wave's partial score tile
-// LDS: [2 tiles][4 waves] partial scores, then [2 tiles][4 waves] V slices
-constexpr int kLds5 = 2 * kWaves5 * kSBytes + 2 * kWaves5 * kVBytes;
+// LDS bytes per staged K row: 256 + 16, so that the 16 rows one quarter of
+// an operand read touches start in 16 disjoint 4-bank groups
+constexpr int kKStride = kSlice * 2 + 16;
+constexpr int kKBytes = kTile * kKStride;    // one wave's staged K tile
+// LDS: [2 tiles][4 waves] partial scores, [2 tiles][4 waves] V slices, then
+// [4 waves] K slices (a wave reads back only its own K, in program order)
+constexpr int kLds5 = 2 * kWaves5 * kSBytes + 2 * kWaves5 * kVBytes + kWaves5 * kKBytes;
 
 // Key (relative to its tile) that lane row i of the K operand loads.  With
 // this order, score register r of lane half h holds key 16(r/8) + 8h + r%8,
@@ -59,77 +71,21 @@ __device__ __forceinline__ int key_of_row(int i) {
   return 16 * (a >> 1) + 8 * h + 4 * (a & 1) + b;
 }
 
-template <int PS>
-__global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem5[];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane >> 5;     // lane half: k-group of the operands
-  const int col = lane & 31;   // MFMA column: (row, head) pair
-  const int g = a.group;
-  const int R = 32 / g;        // rows per workgroup
-  const int nsplit = a.num_splits;
-  const int s = blockIdx.x % nsplit;
-  const int rb = blockIdx.x / nsplit;
-  const int hk = blockIdx.y;
-  const int j = blockIdx.z;
-
-  int q_start, Lq, Lk;
-  if (a.cu_q != nullptr) {
-    // clamped to the packed rows [0, total_q), so that no q read or out
-    // write leaves its buffer whatever cu_seq_lens_q holds
-    q_start = min(max(a.cu_q[j], 0), a.total_q);
-    Lq = min(max(a.cu_q[j + 1], q_start), a.total_q) - q_start;
-    Lk = a.cu_k[j + 1] - a.cu_k[j];
-  } else {
-    q_start = j;
-    Lq = 1;
-    Lk = a.seq_lens[j];
-  }
-  Lk = max(0, min(Lk, a.max_pages * PS));
-  const int row0 = rb * R;
-  if (row0 >= Lq) return;
-  const int nrows = min(R, Lq - row0);
-  const int shift = Lk - Lq;
-
-  // this lane's column
-  const int crow = col / g, chead = col - crow * g;
-  const bool col_ok = crow < nrows;
-  const int head = hk * g + chead;
-  const int pos = shift + row0 + crow;  // position of the column's row
-  const int qrow = q_start + row0 + (col_ok ? crow : 0);
-
-  // keys this workgroup may need: the rows' causal/window band, cut to the split
-  const int pmin = shift + row0, pmax = shift + row0 + nrows - 1;
-  int k_lo = a.window > 0 ? max(0, pmin - a.window + 1) : 0;
-  int k_hi = min(pmax + 1, Lk);
-  if (nsplit > 1) {
-    const int first_key = a.window > 0 ? max(0, Lk - a.window) : 0;
-    const int p0 = first_key / PS;
-    k_lo = max(k_lo, (p0 + s * a.pages_per_split) * PS);
-    k_hi = min(k_hi, (p0 + (s + 1) * a.pages_per_split) * PS);
-  }
-
-  // Q slice as the B operand: lane holds q[column][128w + 16ks + 8h .. +7]
-  bf16x8 qop[8];
-  {
-    const uint16_t* qp = a.q + ((int64_t)qrow * a.num_q_heads + head) * D5 + kSlice * w + 8 * h;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (col_ok) v = *reinterpret_cast<const uint4*>(qp + 16 * ks);
-      qop[ks] = as_bf16x8(v);
-    }
-  }
-
-  f32x16 acc[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+// The key-tile pipeline of one pass: tiles covering keys [k_lo, k_hi) of
+// the sequence whose block-table row is row j, for KV head hk, with the 32
+// MFMA columns this workgroup's lanes describe (column position pos, valid
+// when col_ok; pmin / pmax the least and greatest position of the valid
+// columns).  Folds the tiles into this lane's (acc, m_run, l_run); m_run
+// is in log2 units.  Every wave of the workgroup calls it with the same
+// tile range (the tiles exchange partial scores through LDS).
+template <int PS, bool KLDS>
+__device__ __forceinline__ void tile_loop(const Attn512Args& a, int hk, int j, int w, int lane,
+                                          int k_lo, int k_hi, int pmin, int pmax, int pos,
+                                          bool col_ok, const bf16x8 (&qop)[8],
+                                          unsigned char* smem5, f32x16 (&acc)[4], float& m_run,
+                                          float& l_run) {
+  const int h = lane >> 5;
   const float c = a.scale_log2;
-
   const uint16_t* kh = a.k_pool + (int64_t)hk * a.head_stride + kSlice * w;
   const uint16_t* vh = a.v_pool + (int64_t)hk * a.head_stride + kSlice * w;
   // block-table row read through the scalar cache (never written here), so
@@ -142,17 +98,18 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a)
   // entries, or -1 for an unusable entry.
   constexpr int NPG = kTile / PS;
   struct TileRegs {
-    uint4 k[8];       // K operand, k-steps of 16 dims
+    uint4 k[8];       // K slice rows staged to LDS before use, or (no
+                      // staging) the K operands of the 8 k-steps
     uint4 v[8];       // V slice rows, staged to LDS before use
     uint32_t usable;  // bit kr: key kb + kr is in [k_lo, k_hi) on a usable page
   };
-  // Lane-constant parts of the load addresses (elements from a page base).
-  // K: lane row i loads key key_of_row(i); V chunk i is key 4i + lane/16,
-  // dims 8 * (lane % 16) .. +7.  A tile starts on a page boundary.
-  const int k_off = (krel % PS) * D5 + 8 * h;
-  int v_off[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v_off[i] = ((4 * i + (lane >> 4)) % PS) * D5 + 8 * (lane & 15);
+  // Load addresses: K and V chunk i is key 4i + lane/16 of the tile, dims
+  // 8 * (lane % 16) .. +7 of the wave's slice: a page resource (scalar
+  // registers), one lane offset and a scalar row offset per chunk.  A tile
+  // starts on a page boundary.
+  const int lane_off = ((lane >> 4) * D5 + 8 * (lane & 15)) * 2;  // bytes
+  // without staging, lane row i loads the K operand of key key_of_row(i)
+  const int k_off = ((krel % PS) * D5 + 8 * h) * 2;                // bytes
   auto load_tile = [&](TileRegs& tr, int t) {
     const int kb = t * kTile;
     // pages of the tile (wave-uniform); an unusable entry reads page 0
@@ -174,28 +131,54 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a)
     // or page 0, which always exists) so that the compiler can count them
     // exactly and keep the next tile in flight; K rows of such keys only
     // meet masked scores, and V rows are zeroed when staged.
-    const int phk = (NPG == 1 || krel < PS) ? ph[0] : ph[NPG - 1];
-    const uint16_t* kp = kh + (int64_t)phk * PS * D5;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      tr.k[ks] = *reinterpret_cast<const uint4*>(kp + k_off + 16 * ks);
+    for (int pg = 0; pg < NPG; ++pg) {
+      const int64_t pb = (int64_t)ph[pg] * PS * D5;
+      const auto kr = make_rsrc(kh + pb, PS * D5 * 2);
+      const auto vr = make_rsrc(vh + pb, PS * D5 * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint16_t* vp = vh + (int64_t)ph[NPG == 1 ? 0 : (i * 4 >= PS ? NPG - 1 : 0)] * PS * D5;
-      tr.v[i] = *reinterpret_cast<const uint4*>(vp + v_off[i]);
+      for (int i = pg * (8 / NPG); i < (pg + 1) * (8 / NPG); ++i) {
+        const int row_off = ((4 * i) % PS) * D5 * 2;
+        if constexpr (KLDS) tr.k[i] = buffer_load16_s<KLDS>(kr, lane_off, row_off);
+        tr.v[i] = buffer_load16_s<KLDS>(vr, lane_off, row_off);
+      }
+    }
+    if constexpr (!KLDS) {
+      // the operand rows straight from the pool: lane row i holds key
+      // key_of_row(i), which lies on page ph[0] or (page 16) ph[1]
+      const int pgk = (NPG == 1 || krel < PS) ? 0 : NPG - 1;
+      const auto kr = make_rsrc(kh + (int64_t)ph[pgk] * PS * D5, PS * D5 * 2);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) tr.k[ks] = buffer_load16_s<false>(kr, k_off, 32 * ks);
     }
   };
 
   float* sbuf = reinterpret_cast<float*>(smem5);
   unsigned char* vbuf = smem5 + 2 * kWaves5 * kSBytes;
+  unsigned char* kw = smem5 + 2 * kWaves5 * kSBytes + 2 * kWaves5 * kVBytes + w * kKBytes;
+  // this lane's K operand row in the staged tile (lane row i is key key_of_row(i))
+  const unsigned char* ka = kw + krel * kKStride + 16 * h;
 
   auto process = [&](const TileRegs& tr, int t) {
     const int kb = t * kTile;
     const int par = t & 1;
     // partial scores of this wave's 128 dims
     f32x16 sp = {};
+    if constexpr (KLDS) {
+      // stage this wave's K rows, then read them back in operand order: lane
+      // (row i, half h) takes K[key_of_row(i)][16ks + 8h .. +7] for k-step ks
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) sp = mfma32(as_bf16x8(tr.k[ks]), qop[ks], sp);
+      for (int i = 0; i < 8; ++i) {
+        const int chunk = lane + 64 * i;
+        *reinterpret_cast<uint4*>(kw + (chunk >> 4) * kKStride + 16 * (chunk & 15)) = tr.k[i];
+      }
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        sp = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(ka + 32 * ks)), qop[ks], sp);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) sp = mfma32(as_bf16x8(tr.k[ks]), qop[ks], sp);
+    }
     // partial tile as [4 quads][64 lanes] float4s: each store and load
     // instruction covers 1 KB contiguous (no bank conflicts)
     float* my = sbuf + (par * kWaves5 + w) * 64 * 16;
@@ -316,15 +299,96 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a)
   // masked), so every path issues the same loads and the compiler waits for
   // exactly the tile being processed.
   const int t0 = k_lo / kTile, t1 = k_hi > k_lo ? (k_hi + kTile - 1) / kTile : t0;
+  // The scheduling barriers keep each prefetch ahead of the processing of
+  // the tile before it: without them the compiler hoists the first MFMA of
+  // process(t) above the loads of tile t+1, so that the wait for tile t
+  // finds nothing else in flight.
   TileRegs ta, tb;
   if (t0 < t1) load_tile(ta, t0);
   for (int t = t0; t < t1; t += 2) {
     load_tile(tb, t + 1);
+    __builtin_amdgcn_sched_barrier(0);
     process(ta, t);
     if (t + 1 >= t1) break;
     load_tile(ta, t + 2);
+    __builtin_amdgcn_sched_barrier(0);
     process(tb, t + 1);
   }
+
+}
+
+template <int PS, bool KLDS>
+__global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem5[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;     // lane half: k-group of the operands
+  const int col = lane & 31;   // MFMA column: (row, head) pair
+  const int g = a.group;
+  const int R = 32 / g;        // rows per workgroup
+  const int nsplit = a.num_splits;
+  const int s = blockIdx.x % nsplit;
+  const int rb = blockIdx.x / nsplit;
+  const int hk = blockIdx.y;
+  const int j = blockIdx.z;
+
+  int q_start, Lq, Lk;
+  if (a.cu_q != nullptr) {
+    // clamped to the packed rows [0, total_q), so that no q read or out
+    // write leaves its buffer whatever cu_seq_lens_q holds
+    q_start = min(max(a.cu_q[j], 0), a.total_q);
+    Lq = min(max(a.cu_q[j + 1], q_start), a.total_q) - q_start;
+    Lk = a.cu_k[j + 1] - a.cu_k[j];
+  } else {
+    q_start = j;
+    Lq = 1;
+    Lk = a.seq_lens[j];
+  }
+  Lk = max(0, min(Lk, a.max_pages * PS));
+  const int row0 = rb * R;
+  if (row0 >= Lq) return;
+  const int nrows = min(R, Lq - row0);
+  const int shift = Lk - Lq;
+
+  // this lane's column
+  const int crow = col / g, chead = col - crow * g;
+  const bool col_ok = crow < nrows;
+  const int head = hk * g + chead;
+  const int pos = shift + row0 + crow;  // position of the column's row
+  const int qrow = q_start + row0 + (col_ok ? crow : 0);
+
+  // keys this workgroup may need: the rows' causal/window band, cut to the split
+  const int pmin = shift + row0, pmax = shift + row0 + nrows - 1;
+  int k_lo = a.window > 0 ? max(0, pmin - a.window + 1) : 0;
+  int k_hi = min(pmax + 1, Lk);
+  if (nsplit > 1) {
+    const int first_key = a.window > 0 ? max(0, Lk - a.window) : 0;
+    const int p0 = first_key / PS;
+    k_lo = max(k_lo, (p0 + s * a.pages_per_split) * PS);
+    k_hi = min(k_hi, (p0 + (s + 1) * a.pages_per_split) * PS);
+  }
+
+  // Q slice as the B operand: lane holds q[column][128w + 16ks + 8h .. +7]
+  bf16x8 qop[8];
+  {
+    const uint16_t* qp = a.q + ((int64_t)qrow * a.num_q_heads + head) * D5 + kSlice * w + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (col_ok) v = *reinterpret_cast<const uint4*>(qp + 16 * ks);
+      qop[ks] = as_bf16x8(v);
+    }
+  }
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  tile_loop<PS, KLDS>(a, hk, j, w, lane, k_lo, k_hi, pmin, pmax, pos, col_ok, qop, smem5, acc,
+                      m_run, l_run);
 
   // ---- write: lane holds dims 32dt + 8(r/4) + 4h + r%4 of its column ----
   const float lt = half_sum(l_run);
@@ -358,25 +422,213 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a)
   }
 }
 
+// Decode rows as a stream-K partition over workgroups.  The units of the
+// batch -- every 32-key tile that holds an allowed key, for every KV head of
+// every row, ordered by row, then KV head, then tile -- are cut into one
+// contiguous range of equal size per workgroup (one workgroup per compute
+// unit), so that every compute unit streams the same number of tiles
+// whatever the length mix.  A (row, KV head) segment inside one range is
+// finished by its workgroup; a segment cut by range ends leaves one partial
+// per piece (unnormalised accumulator, then max in log2 units and sum, for
+// each of the g query heads) and, from the workgroup where it starts, a
+// merge descriptor, in the layout the stream-K merge kernel combines in
+// workgroup order.  The g query heads of a row are g of the 32 MFMA
+// columns, so each K/V tile is read once for the whole group.
 template <int PS>
+__global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_stream_kernel(StreamArgs sa) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem5[];
+  const DecodeArgs& d = sa.base;
+  const int B = sa.num_seqs, nw = sa.num_waves, wg = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, col = lane & 31;
+  const int Hkv = d.num_kv_heads, g = d.group;
+  int* pre = reinterpret_cast<int*>(smem5 + kLds5);  // pre[b] = first unit of row b; pre[B] = U
+  // row lengths, read through the scalar cache (never written here)
+  const __attribute__((address_space(4))) int32_t* sl =
+      (const __attribute__((address_space(4))) int32_t*)d.seq_lens;
+  auto uni = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+
+  // ---- units per row (tiles of allowed keys) x KV heads, scanned by wave 0 ----
+  if (w == 0) {
+    int carry = 0;
+    for (int b0 = 0; b0 < B; b0 += 64) {
+      const int b = b0 + lane;
+      int v = 0;
+      if (b < B) {
+        const int L = max(0, min(d.seq_lens[b], d.max_pages * PS));
+        const int fk = d.window > 0 ? max(0, L - d.window) : 0;
+        v = ((L + kTile - 1) / kTile - fk / kTile) * Hkv;
+      }
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(v, off);
+        if (lane >= off) v += t;
+      }
+      if (b < B) pre[b + 1] = carry + v;
+      carry += __shfl(v, 63);
+    }
+    if (lane == 0) pre[0] = 0;
+  }
+  if (tid < 2) sa.desc[(2 * wg + tid) * kDescInts] = 0;  // this launch's descriptors
+  __syncthreads();
+  const int U = uni(pre[B]);
+  // rows of empty sequences are zero (a row with any key has a unit)
+  for (int b = wg; b < B; b += nw) {
+    if (pre[b + 1] != pre[b]) continue;
+    uint16_t* o = d.out + (int64_t)b * d.num_q_heads * D5;
+    for (int i = tid; i < d.num_q_heads * D5; i += kWaves5 * 64) o[i] = 0;
+  }
+  if (U == 0) return;
+  const int u0 = (int)((int64_t)wg * U / nw), u1 = (int)((int64_t)(wg + 1) * U / nw);
+  if (u0 >= u1) return;
+
+  Attn512Args a = {};
+  a.k_pool = d.k_pool;
+  a.v_pool = d.v_pool;
+  a.block_tables = d.block_tables;
+  a.head_stride = d.head_stride;
+  a.max_pages = d.max_pages;
+  a.num_pages = d.num_pages;
+  a.window = d.window;
+  a.scale_log2 = d.scale_log2;
+
+  // first segment: the largest row b with pre[b] <= u0 is non-empty (u0 < U)
+  int lo = 0, hi = B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (uni(pre[mid]) <= u0) lo = mid; else hi = mid;
+  }
+  int b = lo;
+  int hk = (u0 - uni(pre[lo])) / ((uni(pre[lo + 1]) - uni(pre[lo])) / Hkv);
+  const bool col_ok = col < g;
+  const int dbase = kSlice * w + 4 * h;
+  for (int u = u0; u < u1;) {
+    const int L = max(0, min(sl[b], d.max_pages * PS));
+    const int E = (uni(pre[b + 1]) - uni(pre[b])) / Hkv;
+    const int s0 = uni(pre[b]) + hk * E, s1 = s0 + E;
+    const int first_key = a.window > 0 ? max(0, L - a.window) : 0;
+    const int tf = first_key / kTile;
+    const int ub = min(u1, s1);
+    const int k_lo = max(first_key, (tf + (u - s0)) * kTile);
+    const int k_hi = min(L, (tf + (ub - s0)) * kTile);
+    const int head = hk * g + (col_ok ? col : 0);
+    bf16x8 qop[8];
+    {
+      const uint16_t* qp = d.q + ((int64_t)b * d.num_q_heads + head) * D5 + kSlice * w + 8 * h;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (col_ok) v = *reinterpret_cast<const uint4*>(qp + 16 * ks);
+        qop[ks] = as_bf16x8(v);
+      }
+    }
+    f32x16 acc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    // the previous segment's last tiles are done with the LDS score and V
+    // slots, whatever this segment's first tile parity
+    __syncthreads();
+    tile_loop<PS, true>(a, hk, b, w, lane, k_lo, k_hi, L - 1, L - 1, L - 1, col_ok, qop, smem5,
+                        acc, m_run, l_run);
+    const float lt = half_sum(l_run);
+    if (s0 >= u0 && s1 <= u1) {  // the whole segment is here: final rows
+      if (col_ok) {
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        uint16_t* op = d.out + ((int64_t)b * d.num_q_heads + head) * D5 + dbase;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            uint2 pk;
+            pk.x = pack_bf16x2(acc[dt][4 * rq] * inv, acc[dt][4 * rq + 1] * inv);
+            pk.y = pack_bf16x2(acc[dt][4 * rq + 2] * inv, acc[dt][4 * rq + 3] * inv);
+            *reinterpret_cast<uint2*>(op + 32 * dt + 8 * rq) = pk;
+          }
+      }
+    } else {
+      // a piece of a cut segment: slot 0 holds the piece at the start of
+      // this workgroup's range, slot 1 the one at its end
+      const int slot = 2 * wg + (s0 <= u0 ? 0 : 1);
+      float* p = sa.part + (int64_t)slot * g * (D5 + 2);
+      if (col_ok) {
+        float* pa = p + col * D5 + dbase;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq)
+            *reinterpret_cast<float4*>(pa + 32 * dt + 8 * rq) = make_float4(
+                acc[dt][4 * rq], acc[dt][4 * rq + 1], acc[dt][4 * rq + 2], acc[dt][4 * rq + 3]);
+        if (w == 0 && h == 0) {
+          p[g * D5 + col] = m_run;
+          p[g * D5 + g + col] = lt;
+        }
+      }
+      if (s0 >= u0 && tid == 0) {  // the segment starts here: describe it for the merge
+        int* dsc = sa.desc + slot * kDescInts;
+        dsc[1] = b;
+        dsc[2] = hk;
+        dsc[3] = (int)(((int64_t)s1 * nw - 1) / U);  // workgroup holding the segment's last unit
+        dsc[4] = U;
+        dsc[0] = 1;
+      }
+    }
+    u = ub;
+    if (++hk == Hkv) {  // next row with any unit
+      hk = 0;
+      ++b;
+      while (b < B - 1 && uni(pre[b + 1]) == uni(pre[b])) ++b;
+    }
+  }
+}
+
+template <int PS>
+hipError_t launch_stream_ps(const StreamArgs& sa, hipStream_t st) {
+  static std::atomic<uint64_t> lds_raised{0};
+  constexpr int kMaxLds = kLds5 + (2048 + 1) * 4;  // the scan of up to 2048 rows
+  const hipError_t e = raise_lds_limit(
+      reinterpret_cast<const void*>(&attn512_stream_kernel<PS>), kMaxLds, lds_raised);
+  if (e != hipSuccess) return e;
+  const size_t smem = kLds5 + (size_t)(sa.num_seqs + 1) * sizeof(int);
+  hipLaunchKernelGGL((attn512_stream_kernel<PS>), dim3(sa.num_waves), dim3(kWaves5 * 64), smem, st,
+                     sa);
+  return hipGetLastError();
+}
+
+// K staged through LDS and loads with the streaming policy for decode rows
+// (a workgroup's columns are one row: the kernel is bound by the loads in
+// flight, and each page is read once); straight operand loads with the
+// default policy for varlen rows (the MFMA work per tile is larger, and the
+// row blocks of a sequence read the same pages, which should stay in L2)
+template <int PS, bool KLDS>
 hipError_t launch_ps(const Attn512Args& a, int num_seqs, int row_blocks, hipStream_t st) {
   static std::atomic<uint64_t> lds_raised{0};
-  const hipError_t e =
-      raise_lds_limit(reinterpret_cast<const void*>(&attn512_kernel<PS>), kLds5, lds_raised);
+  const hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&attn512_kernel<PS, KLDS>),
+                                       kLds5, lds_raised);
   if (e != hipSuccess) return e;
   const dim3 grid(row_blocks * a.num_splits, a.num_kv_heads, num_seqs);
-  hipLaunchKernelGGL((attn512_kernel<PS>), grid, dim3(kWaves5 * 64), kLds5, st, a);
+  hipLaunchKernelGGL((attn512_kernel<PS, KLDS>), grid, dim3(kWaves5 * 64), kLds5, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
+hipError_t launch_attn512_stream(const StreamArgs& sa, int page_size, hipStream_t st) {
+  return page_size == 16 ? launch_stream_ps<16>(sa, st) : launch_stream_ps<32>(sa, st);
+}
+
 hipError_t launch_attn512(const Attn512Args& a, int num_seqs, int max_rows, int page_size,
                           hipStream_t st) {
   const int R = 32 / a.group;
   const int row_blocks = (max_rows + R - 1) / R;
-  return page_size == 16 ? launch_ps<16>(a, num_seqs, row_blocks, st)
-                         : launch_ps<32>(a, num_seqs, row_blocks, st);
+  if (a.cu_q == nullptr)
+    return page_size == 16 ? launch_ps<16, true>(a, num_seqs, row_blocks, st)
+                           : launch_ps<32, true>(a, num_seqs, row_blocks, st);
+  return page_size == 16 ? launch_ps<16, false>(a, num_seqs, row_blocks, st)
+                         : launch_ps<32, false>(a, num_seqs, row_blocks, st);
 }
 
 }  // namespace pkv

@@ -82,6 +82,14 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int byt
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kNonTemporal);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
+// 16 bytes at lane offset + a wave-uniform (scalar) offset, with the
+// streaming policy (data read once) or the default one (data that other
+// workgroups read again, which should stay in L2).
+template <bool STREAM = true>
+__device__ __forceinline__ uint4 buffer_load16_s(__amdgpu_buffer_rsrc_t r, int byte_off, int soff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, soff, STREAM ? kNonTemporal : 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, int byte_off) {
   const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, kNonTemporal);
   return make_uint2(v.x, v.y);
@@ -262,5 +270,9 @@ struct Attn512Args {
 };
 hipError_t launch_attn512(const Attn512Args& a, int num_seqs, int max_rows, int page_size,
                           hipStream_t st);
+// head_dim 512 decode as a stream-K partition over workgroups (num_waves
+// counts workgroups of four waves, one per compute unit), merged by the
+// stream-K merge kernel
+hipError_t launch_attn512_stream(const StreamArgs& sa, int page_size, hipStream_t st);
 
 }  // namespace pkv

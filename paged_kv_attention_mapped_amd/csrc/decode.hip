@@ -436,6 +436,8 @@ constexpr int kMergeBatch = 4;
 template <int D, int G>
 __global__ __launch_bounds__(64) void stream_merge_kernel(StreamArgs sa) {
   constexpr int EPL = D / 64;
+  // pieces in flight per batch (two at head_dim 512, so that their values stay in registers)
+  constexpr int MB = D >= 512 ? 2 : kMergeBatch;
   const int slot = blockIdx.x, lane = threadIdx.x;
   // descriptor: [valid, sequence, KV head, last wave, total units]
   const int dv = lane < 5 ? sa.desc[slot * kDescInts + lane] : 0;
@@ -460,12 +462,12 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(StreamArgs sa) {
 #pragma unroll
     for (int i = 0; i < EPL; ++i) o[h][i] = 0.f;
   }
-  for (int wb = w0; wb <= w1; wb += kMergeBatch) {
-    float ml[kMergeBatch], pv[kMergeBatch][G][EPL];
+  for (int wb = w0; wb <= w1; wb += MB) {
+    float ml[MB], pv[MB][G][EPL];
     // loads are unconditional (a wave past w1 re-reads w1's piece) so that
     // they all leave before the first one is used
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
+    for (int k = 0; k < MB; ++k) {
       const int w = min(wb + k, w1);
       const float* p = sa.part + (int64_t)(w == w0 ? slot : 2 * w) * stride;
       ml[k] = p[g * D + min(lane, 2 * g - 1)];  // lanes h: max of head h; lanes g+h: its sum
@@ -475,7 +477,7 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(StreamArgs sa) {
         for (int i = 0; i < EPL; ++i) pv[k][h][i] = p[min(h, g - 1) * D + lane + 64 * i];
     }
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) {
+    for (int k = 0; k < MB; ++k) {
       const int w = wb + k;
       if (w > w1 || !holds(w)) continue;
 #pragma unroll
@@ -601,7 +603,8 @@ hipError_t launch_decode_stream(const StreamArgs& sa, int head_dim, int page_siz
   switch (head_dim) {
     case 64: return launch_s<64>(sa, page_size, st);
     case 128: return launch_s<128>(sa, page_size, st);
-    default: return launch_s<256>(sa, page_size, st);
+    case 256: return launch_s<256>(sa, page_size, st);
+    default: return launch_attn512_stream(sa, page_size, st);  // workgroup-level stream-K
   }
 }
 
@@ -620,7 +623,8 @@ hipError_t launch_stream_merge(const StreamArgs& sa, int head_dim, hipStream_t s
   switch (head_dim) {
     case 64: launch_merge_d<64>(sa, st); break;
     case 128: launch_merge_d<128>(sa, st); break;
-    default: launch_merge_d<256>(sa, st); break;
+    case 256: launch_merge_d<256>(sa, st); break;
+    default: launch_merge_d<512>(sa, st); break;
   }
   return hipGetLastError();
 }

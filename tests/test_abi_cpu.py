@@ -267,13 +267,16 @@ def test_page_allocator_validation(P):
 
 
 def test_head_dim_512_plans(P):
-    # head_dim 512 runs the head-dim-split kernel: direct or split-K, never stream-K
-    assert P.decode_method(4, 8, 1, 512, 32, 100) == ("direct", 1)
-    m, c = P.decode_method(256, 8, 1, 512, 32, 8192)
-    assert m == "split" and c > 1
-    assert P.lib().pkv_decode_stream_waves(4, 8, 1, 512, 32, 100, 0, None) == 3
+    # head_dim 512 streams over workgroups (one per compute unit; 256 assumed
+    # without a GPU), its units being 32-key tiles, at least 4 per workgroup
+    assert P.decode_method(4, 8, 1, 512, 32, 100) == ("stream", 4)        # 4 rows x 4 tiles
+    assert P.decode_method(256, 8, 1, 512, 32, 8192) == ("stream", 256)
+    assert P.decode_method(16, 8, 1, 512, 16, 4096, 512) == ("stream", 16 * 17 // 4)  # window: 17 tiles
+    # splits asked for: split-K with that many splits
+    assert P.decode_method(256, 8, 1, 512, 32, 8192, 0, 4) == ("split", 4)
+    parts = (2 * 256 * 8 * 514 * 4 + 255) // 256 * 256
+    assert P.decode_workspace_bytes(256, 8, 512, 1, 32, 8192) == parts + 2 * 256 * 8 * 4
     assert P.lib().pkv_decode_stream_workspace_bytes(8, 8, 1, 512) > 0
-    assert P.decode_workspace_bytes(256, 8, 512, 1, 32, 8192) == 256 * 8 * c * 514 * 4
 
 
 def test_prefill_split_validation(P):

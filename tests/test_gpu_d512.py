@@ -1,6 +1,7 @@
 """head_dim 512 (the full-attention layers of the dual-regime model) against
-the oracle: append bit-exact, decode (direct, automatic splits, explicit
-splits + combine, decode rows through the varlen entry), varlen prefill with
+the oracle: append bit-exact, decode (the automatic workgroup-level
+stream-K with any workgroup count, explicit splits + combine, one split,
+decode rows through the varlen entry), varlen prefill with
 fresh prompts, chunks after a cached prefix and mixed batches, for groups 1,
 3, 4 and 8, pages 16 and 32, with and without a window."""
 import numpy as np
@@ -51,7 +52,7 @@ def test_d512_decode(P, shape):
     lens = wl.decode_seq_lens()
     bt = dev_i32(wl.block_tables[:wl.n_decode])
     ref = oracle.decode(qd, o.k, o.v, wl.block_tables[:wl.n_decode], lens, ps, wl.scale, win)
-    assert P.decode_method(wl.n_decode, hq, hkv, 512, ps, int(lens.max()), win)[0] != "stream"
+    assert P.decode_method(wl.n_decode, hq, hkv, 512, ps, int(lens.max()), win)[0] == "stream"
     for splits in (0, 1, 3):
         say(f"[d512 decode] {name} num_splits={splits}")
         out = P.decode(dev_bits(qd), g.k, g.v, bt, dev_i32(lens), int(lens.max()), page_size=ps,
@@ -93,3 +94,32 @@ def test_d512_prefill(P, shape):
     torch.cuda.synchronize()
     ref = oracle.prefill_varlen(q, o.k, o.v, wl.block_tables, cq, ck, ps, wl.scale, win)
     check_close(host_bits(out), ref, f"d512 {name} mixed single launch")
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[s[0] for s in SHAPES])
+def test_d512_stream_any_partition(P, shape):
+    """The workgroup-level stream-K at head_dim 512 with many workgroup
+    counts, so that ranges are cut inside rows, at row and KV-head
+    boundaries and across several workgroups; an empty row and page-edge
+    lengths; each count run twice, bit-identical."""
+    name, hq, hkv, ps, win = shape
+    wl, g, o = build(name, hq, hkv, ps, win,
+                     decode_ctx=("fixed", (0, 31, 32, 33, 95, 300, 1, 1200, 64)))
+    qd, _ = wl.queries(0)
+    lens = wl.decode_seq_lens().copy()
+    lens[0] = 0                                       # an empty row
+    bt = dev_i32(wl.block_tables[:wl.n_decode])
+    ref = oracle.decode(qd, o.k, o.v, wl.block_tables[:wl.n_decode], lens, ps, wl.scale, win)
+    auto = P.decode_stream_waves(wl.n_decode, hq, hkv, 512, ps, int(lens.max()), win)
+    for nw in sorted({1, 2, 3, 5, 13, 64, auto}):
+        say(f"[d512 stream] {name} workgroups={nw}")
+        outs = []
+        for _ in range(2):
+            out, ws = P.decode_stream(dev_bits(qd), g.k, g.v, bt, dev_i32(lens), page_size=ps,
+                                      num_waves=nw, scale=wl.scale, window=win)
+            P.decode_stream_merge(ws, out, num_waves=nw, num_kv_heads=hkv)
+            torch.cuda.synchronize()
+            outs.append(host_bits(out))
+        assert np.array_equal(outs[0], outs[1]), "stream-K decode is not deterministic"
+        check_close(outs[0], ref, f"d512 {name} stream, {nw} workgroups")
+        assert np.all(outs[0][0] == 0)                # the empty row
