@@ -56,7 +56,7 @@ DESCRIPTIONS = {
 
 # key splits of the single varlen launch per workload (pkv_prefill_varlen_split);
 # workloads not listed use one (pkv_prefill_varlen)
-PREFILL_SPLITS = {}
+PREFILL_SPLITS = {"window_shared": 3}
 
 
 def _log(*a):
@@ -791,8 +791,8 @@ def main():
                               "prefill_key_splits": st.psplits}
         out["roofline"] = {
             "kernel": ("prefill_kernel (decode rows + prefill rows in one launch)" if st.psplits == 1
-                       else f"prefill_kernel with {st.psplits} key splits + combine_kernel "
-                            "(decode rows + prefill rows)"),
+                       else f"prefill_kernel with up to {st.psplits} key runs per block + "
+                            "split_merge_kernel (decode rows + prefill rows)"),
             "bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
             "avg_kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": kb,

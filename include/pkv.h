@@ -499,25 +499,31 @@ pkv_status pkv_prefill_varlen(const uint16_t* q, const uint16_t* k_pool, const u
                               uint16_t* out, hipStream_t stream);
 
 /*
- * pkv_prefill_varlen with each workgroup's keys cut into num_splits runs of
- * whole key tiles (flash-decoding's split of the key range, applied to the
- * varlen batch).  A short prefill whose workgroups are few (a handful of
- * chunks with long cached prefixes under a sliding window fill a few dozen
- * of the 256 compute units) spreads its key range over more workgroups;
- * every (query row, head, split) leaves a partial (running max in log2
- * units, sum, unnormalised accumulator) and a second launch merges them
- * with the split-K combine of pkv_decode_combine, in fixed split order.
- * A one-row sequence (a decode row) has its pages cut into num_splits runs
- * the same way.  The result equals pkv_prefill_varlen's within
- * floating-point order, and is deterministic for a given num_splits.
+ * pkv_prefill_varlen with the key range of long work cut into runs (the
+ * flash-decoding split of the keys, applied to the varlen batch).  A short
+ * prefill whose workgroups are few -- a handful of chunks with long cached
+ * prefixes under a sliding window, beside decode rows, fill a few dozen of
+ * the 256 compute units -- spreads its key tiles over more workgroups.
+ * Every query block of a prompt or chunk is cut into the same S runs of
+ * whole key tiles, S = min(num_splits, tiles of its last block / 4 at head
+ * dim 256, 2 at 128 and 64) (no cut below twice that); a one-row sequence
+ * (a decode row) has its pages cut the same way with at least four pages
+ * per wave and run.  Each run leaves a partial per (query row, head)
+ * (running max in log2 units, sum, unnormalised accumulator), and a second
+ * launch merges the rows that were cut, in fixed run order; rows that were
+ * not cut are written by the first launch.  The result equals
+ * pkv_prefill_varlen's within floating-point order and is deterministic
+ * for a given num_splits.
  *
  * Arguments are those of pkv_prefill_varlen, plus:
  *   num_splits       1..64; 1 is exactly pkv_prefill_varlen (no workspace)
  *   workspace        device memory of at least
  *                    pkv_prefill_split_workspace_bytes(total_q, num_q_heads,
- *                    head_dim, num_splits) bytes, owned by the caller,
- *                    overwritten (it needs no clearing); used only when
- *                    num_splits > 1
+ *                    head_dim, num_splits) bytes, owned by the caller:
+ *                    partials [Tq, Hq, num_splits] (max, sum) and
+ *                    [Tq, Hq, num_splits, D] (accumulator), then each row's
+ *                    run count; overwritten by every call (it needs no
+ *                    clearing); used only when num_splits > 1
  * Errors: as pkv_prefill_varlen; BAD_SHAPE for num_splits outside 1..64;
  * UNSUPPORTED for num_splits > 1 at head_dim 512; NULL_ARG or
  * WORKSPACE_TOO_SMALL for the workspace.

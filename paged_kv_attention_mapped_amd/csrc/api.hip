@@ -633,7 +633,8 @@ size_t pkv_prefill_split_workspace_bytes(int32_t total_q, int32_t num_q_heads, i
                                          int32_t num_splits) {
   if (total_q <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_splits <= 1) return 0;
   const size_t cells = (size_t)total_q * num_q_heads * num_splits;
-  return 2 * split_region(cells * sizeof(float)) + cells * (size_t)head_dim * sizeof(float);
+  return 2 * split_region(cells * sizeof(float)) +
+         split_region(cells * (size_t)head_dim * sizeof(float)) + (size_t)total_q * sizeof(int32_t);
 }
 
 static pkv_status prefill_entry(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
@@ -675,6 +676,7 @@ static pkv_status prefill_entry(const uint16_t* q, const uint16_t* k_pool, const
   a.scale_log2 = scale * kLog2e;
   a.nsplit = num_splits;
   a.part_m = a.part_l = a.part_acc = nullptr;
+  a.part_S = nullptr;
   if (num_splits > 1) {
     if (!workspace) return PKV_ERR_NULL_ARG;
     if (workspace_bytes < pkv_prefill_split_workspace_bytes(total_q, num_q_heads, head_dim, num_splits))
@@ -684,6 +686,8 @@ static pkv_status prefill_entry(const uint16_t* q, const uint16_t* k_pool, const
     a.part_m = reinterpret_cast<float*>(w);
     a.part_l = reinterpret_cast<float*>(w + split_region(cells * sizeof(float)));
     a.part_acc = reinterpret_cast<float*>(w + 2 * split_region(cells * sizeof(float)));
+    a.part_S = reinterpret_cast<int*>(w + 2 * split_region(cells * sizeof(float)) +
+                                      split_region(cells * (size_t)head_dim * sizeof(float)));
   }
   return hip_status(launch_prefill(a, num_seqs, max_seqlen_q, head_dim, page_size, stream));
 }

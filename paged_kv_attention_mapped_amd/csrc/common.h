@@ -229,14 +229,15 @@ struct PrefillArgs {
   int total_q;
   int window;
   float scale_log2;
-  // key splits (head_dim <= 256): with nsplit > 1 every (row, head, split)
-  // writes a partial (max in log2 units, sum, unnormalised accumulator) to
-  // part_m/part_l [Tq, Hq, nsplit] and part_acc [Tq, Hq, nsplit, D], and the
-  // split-K combine writes out
+  // key splits (head_dim <= 256): with nsplit > 1 a work block whose keys
+  // are cut into S > 1 runs writes one partial per (row, head, run) (max in
+  // log2 units, sum, unnormalised accumulator) to part_m/part_l [Tq, Hq,
+  // nsplit] and part_acc [Tq, Hq, nsplit, D], and a merge launch writes out
   int nsplit;
   float* part_m;
   float* part_l;
   float* part_acc;
+  int* part_S;  // [Tq] split count of each row's work block (written when nsplit > 1)
 };
 hipError_t launch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, int head_dim,
                           int page_size, hipStream_t st);

@@ -67,6 +67,10 @@ using namespace prefill_detail;
 #ifndef PKV_PREFILL_ZGROUP
 #define PKV_PREFILL_ZGROUP 8    // consecutive query blocks of one sequence dispatched together
 #endif
+// launches with at most this many sequences (and few query blocks each) walk
+// a compact work list; each workgroup scans the sequence lengths once
+constexpr int kCompactMaxSeqs = 1024;
+
 
 template <int D, int HW>
 struct PrefillCfg {
@@ -98,11 +102,17 @@ struct PrefillCfg {
 // one launch.
 template <int D, int PS, int HW, int NW>
 __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, int head0,
-                                           int q_row, int L, int split, float* sm) {
-  // with key splits (a.nsplit > 1) split s takes the s-th run of the row's
-  // pages and writes its partial (max in log2 units, sum, unnormalised
-  // accumulator); a split with no pages writes an empty partial
+                                           int q_row, int L, int split, float* sm,
+                                           bool mark) {
+  // with key splits the row's pages are cut into S runs (split_count); split
+  // s takes run s and writes its partial (max in log2 units, sum,
+  // unnormalised accumulator) for the merge, and a row that is not cut
+  // (S = 1) is written whole by split 0
   constexpr int G = HW < 2 ? 2 : HW;
+  const int2 pr = row_pages(L, a.window, PS);
+  const int S = split_count(pr.y - pr.x, a.nsplit, min_split_pages(NW));
+  if (split >= S) return;
+  if (mark && split == 0 && threadIdx.x == 0 && a.nsplit > 1) a.part_S[q_row] = S;
   using W = WaveDecoder<D, PS, G, 16>;
   float* sm_m = sm;                 // [NW][G]
   float* sm_l = sm + NW * G;        // [NW][G]
@@ -115,12 +125,10 @@ __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, 
   wd.load_q(a.q + ((int64_t)q_row * a.num_q_heads + head0) * D, HW);
 
   const int first_key = a.window > 0 ? max(0, L - a.window) : 0;
-  int p0 = first_key / PS;
-  int pend = (L + PS - 1) / PS;
-  if (a.nsplit > 1) {
-    const int per = (pend - p0 + a.nsplit - 1) / a.nsplit;
-    p0 = min(pend, p0 + split * per);
-    pend = min(pend, p0 + per);
+  int p0 = pr.x, pend = pr.y;
+  if (S > 1) {
+    p0 = pr.x + split_begin(pr.y - pr.x, S, split);
+    pend = pr.x + split_begin(pr.y - pr.x, S, split + 1);
   }
   const uint16_t* kh = a.k_pool + (int64_t)hk * a.head_stride;
   const uint16_t* vh = a.v_pool + (int64_t)hk * a.head_stride;
@@ -147,14 +155,18 @@ __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, 
   auto process = [&](const typename W::Buf& bf, int slot) {
     wd.process(bf, tok_of[slot], ok_of[slot] ? first_key : INT_MAX, L, a.scale_log2);
   };
+  // next-step loads unconditional (past the end: the last step again,
+  // unused), so that the compiler's wait counts keep the prefetch in flight
   typename W::Buf b0, b1;
-  if (nsteps > 0) load(b0, 0, 0);
-  for (int i = 0; i < nsteps; i += 2) {
-    if (i + 1 < nsteps) load(b1, i + 1, 1);
-    process(b0, 0);
-    if (i + 1 >= nsteps) break;
-    if (i + 2 < nsteps) load(b0, i + 2, 0);
-    process(b1, 1);
+  if (nsteps > 0) {
+    load(b0, 0, 0);
+    for (int i = 0; i < nsteps; i += 2) {
+      load(b1, min(i + 1, nsteps - 1), 1);
+      process(b0, 0);
+      if (i + 1 >= nsteps) break;
+      load(b0, min(i + 2, nsteps - 1), 0);
+      process(b1, 1);
+    }
   }
 
   float M, lw;
@@ -186,7 +198,7 @@ __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, 
         lsum = fmaf(wt, sm_l[ww * G + h], lsum);
       }
     }
-    if (a.nsplit > 1) {
+    if (S > 1) {
       const int64_t cell = ((int64_t)q_row * a.num_q_heads + head0 + h) * a.nsplit + split;
       a.part_acc[cell * D + d] = o;
       if (d == 0) {
@@ -200,54 +212,166 @@ __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, 
   }
 }
 
+// Rows and keys of sequence j, clamped to the packed rows [0, total_q) and
+// to the block table, so that no q read, out write or partial write leaves
+// its buffer whatever cu_seq_lens_q/k hold.
+struct SeqGeo {
+  int q_start, Lq, Lk;
+};
+template <int PS>
+__device__ __forceinline__ SeqGeo seq_geo(const PrefillArgs& a, int j) {
+  SeqGeo g;
+  g.q_start = min(max(a.cu_q[j], 0), a.total_q);
+  g.Lq = min(max(a.cu_q[j + 1], g.q_start), a.total_q) - g.q_start;
+  g.Lk = max(0, min(a.cu_k[j + 1] - a.cu_k[j], a.max_pages * PS));
+  return g;
+}
+
+// Key splits of a sequence's work under the split entry: every query block
+// of a prompt or chunk is cut into the same S runs, S set by its last block
+// (the one that sees the most keys); a one-row sequence by its pages.
+template <int BM, int BN, int PS, int NW>
+__device__ __forceinline__ int seq_splits(const PrefillArgs& a, const SeqGeo& g) {
+  if (a.nsplit <= 1 || g.Lq <= 0) return 1;
+  if (g.Lq == 1) {
+    const int2 pr = row_pages(g.Lk, a.window, PS);
+    return split_count(pr.y - pr.x, a.nsplit, min_split_pages(NW));
+  }
+  const int q0 = ((g.Lq - 1) / BM) * BM;
+  return split_count(block_tiles(block_keys(q0, g.Lq - 1, g.Lk - g.Lq, g.Lk, a.window), BN),
+                     a.nsplit, min_split_tiles(BN));
+}
+
+// Compact work list: the launch's work items are, sequence by sequence, its
+// query blocks from the last (longest) to the first, each cut into S runs,
+// each run for every (KV head, head group) -- X0 items per run; a one-row
+// sequence has one block.  Workgroup `item` scans the sequences' item
+// counts, NT at a time with a workgroup prefix sum, and finds its
+// sequence j and its index k among j's items; false past the end of the
+// list.  lds: NT/64 + 2 ints.
+template <int NT, int BM, int BN, int PS, int NW>
+__device__ bool find_item(const PrefillArgs& a, int num_seqs, int X0, int item, int* lds,
+                          int& j, int& k) {
+  constexpr int NWV = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid == 0) lds[NWV] = -1;
+  int base = 0;
+  for (int c0 = 0; c0 < num_seqs; c0 += NT) {
+    const int t = c0 + tid;
+    int cnt = 0;
+    if (t < num_seqs) {
+      const SeqGeo g = seq_geo<PS>(a, t);
+      if (g.Lq > 0)
+        cnt = (g.Lq == 1 ? 1 : (g.Lq + BM - 1) / BM) * seq_splits<BM, BN, PS, NW>(a, g) * X0;
+    }
+    int v = cnt;  // inclusive prefix within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(v, o);
+      if (lane >= o) v += u;
+    }
+    if (lane == 63) lds[wv] = v;
+    __syncthreads();
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < NWV; ++w2) {
+      const int x = lds[w2];
+      pre += w2 < wv ? x : 0;
+      tot += x;
+    }
+    const int hi = base + pre + v, lo = hi - cnt;
+    if (cnt > 0 && item >= lo && item < hi) {
+      lds[NWV] = t;
+      lds[NWV + 1] = item - lo;
+    }
+    __syncthreads();
+    if (lds[NWV] >= 0) {
+      j = lds[NWV];
+      k = lds[NWV + 1];
+      return true;
+    }
+    base += tot;
+  }
+  return false;
+}
+
 template <int D, int PS, int HW>
-__global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(PrefillArgs a, int nqb, int zg) {
+__global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(PrefillArgs a, int nqb, int zg,
+                                                                           int num_seqs) {
   using C = PrefillCfg<D, HW>;
   // [K ring: NB tiles][V ring: NB tiles]
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
-  // grid: x = (KV head, head group), y = sequence, z = query block counted
-  // from the end, so the longest (latest) blocks of every sequence go first;
-  // a one-row sequence runs in the z = 0 block, among the first dispatched
-  const int HG = a.group / HW;  // workgroups per KV head along the heads
-  int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
-  if (zg > 1) {
-    // dispatch order: groups of zg query blocks (largest first), and within
-    // a group every sequence's zg blocks back to back, so the workgroups
-    // that run together on one XCD (the same KV head when the x extent is a
-    // multiple of 8) stream the same K/V pages through its L2
-    const uint32_t X = gridDim.x, Y = gridDim.y, Z = (uint32_t)zg;
-    const uint32_t lin = blockIdx.x + X * (blockIdx.y + Y * blockIdx.z);
-    const uint32_t r = lin / X, rest = r / Z;
-    bx = (int)(lin - r * X);
-    by = (int)(rest % Y);
-    bz = (int)((rest / Y) * Z + (r - rest * Z));
-    if (bz >= nqb) return;  // padding of the last group
-  }
-  // key split (x extent = KV heads x head groups x splits)
+  const int HG = a.group / HW;       // workgroups per KV head along the heads
   const int X0 = a.num_kv_heads * HG;
-  const int split = bx / X0;
-  bx -= split * X0;
-  const int j = by;
+  int bx, j, b, split;               // (KV head, head group), sequence, block from the end, run
+  if (zg == 0) {
+    // compact work list (few query blocks per sequence): the workgroups
+    // that find nothing are all at the end of the dispatch order
+    int k;
+    if (!find_item<C::NT, C::BM, C::BN, PS, C::NW>(
+            a, num_seqs, X0, (int)blockIdx.x,
+            reinterpret_cast<int*>(reinterpret_cast<char*>(smem) + C::LDS_BYTES - 256), j, k))
+      return;
+    const int Sj = seq_splits<C::BM, C::BN, PS, C::NW>(a, seq_geo<PS>(a, j));
+    bx = k % X0;
+    k /= X0;
+    split = k % Sj;
+    b = k / Sj;
+  } else {
+    // grid: x = (KV head, head group, run), y = sequence, z = query block
+    // counted from the end, so the longest (latest) blocks of every sequence
+    // go first; a one-row sequence runs in the z = 0 block
+    bx = blockIdx.x;
+    j = blockIdx.y;
+    b = blockIdx.z;
+    if (zg > 1) {
+      // dispatch order: groups of zg query blocks (largest first), and within
+      // a group every sequence's zg blocks back to back, so the workgroups
+      // that run together on one XCD (the same KV head when the x extent is a
+      // multiple of 8) stream the same K/V pages through its L2
+      const uint32_t X = gridDim.x, Y = gridDim.y, Z = (uint32_t)zg;
+      const uint32_t lin = blockIdx.x + X * (blockIdx.y + Y * blockIdx.z);
+      const uint32_t r = lin / X, rest = r / Z;
+      bx = (int)(lin - r * X);
+      j = (int)(rest % Y);
+      b = (int)((rest / Y) * Z + (r - rest * Z));
+      if (b >= nqb) return;  // padding of the last group
+    }
+    split = bx / X0;
+    bx -= split * X0;
+  }
   const int hk = bx / HG;
   const int hg = bx - hk * HG;
-  const int qb = nqb - 1 - bz;
 
-  // query rows of sequence j, clamped to the packed rows [0, total_q) so
-  // that no q read, out write or partial write leaves its buffer whatever
-  // cu_seq_lens_q holds
-  const int q_start = min(max(a.cu_q[j], 0), a.total_q);
-  const int Lq = min(max(a.cu_q[j + 1], q_start), a.total_q) - q_start;
-  int Lk = a.cu_k[j + 1] - a.cu_k[j];
-  Lk = max(0, min(Lk, a.max_pages * PS));
+  const SeqGeo geo = seq_geo<PS>(a, j);
+  const int q_start = geo.q_start, Lq = geo.Lq, Lk = geo.Lk;
   if (Lq == 1) {
-    if (bz == 0)
+    if (b == 0)
       decode_row<D, PS, HW, C::NW>(a, j, hk, hk * a.group + hg * HW, q_start, Lk, split,
-                                   reinterpret_cast<float*>(smem));
+                                   reinterpret_cast<float*>(smem), bx == 0);
     return;
   }
+  const int qb = (zg == 0 ? (Lq + C::BM - 1) / C::BM : nqb) - 1 - b;
   const int q0 = qb * C::BM;
   if (q0 >= Lq) return;
+  const int shift = Lk - Lq;          // position of row r is shift + r
+  // keys any row of this workgroup may see, and with key splits this
+  // split's run of their tiles (split_count; a block that is not cut is
+  // written whole by split 0)
+  const int wg_last = min(q0 + C::BM, Lq) - 1;
+  int2 kr = block_keys(q0, wg_last, shift, Lk, a.window);
+  const int S = seq_splits<C::BM, C::BN, PS, C::NW>(a, geo);
+  if (split >= S) return;
+  if (S > 1) {  // this run of the block's tiles (a block with fewer tiles than runs has empty runs)
+    const int nt = block_tiles(kr, C::BN);
+    const int tf = kr.x / C::BN;
+    kr.x = max(kr.x, (tf + split_begin(nt, S, split)) * C::BN);
+    kr.y = min(kr.y, (tf + split_begin(nt, S, split + 1)) * C::BN);
+  }
+  const int kstart = kr.x, kend = kr.y;
+  if (a.nsplit > 1 && split == 0 && bx == 0)  // the rows' split count, for the merge
+    for (int r = q0 + (int)threadIdx.x; r <= wg_last; r += C::NT) a.part_S[q_start + r] = S;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -257,7 +381,6 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   const int head = hk * a.group + hg * HW + hw;
   const int r0 = q0 + 32 * (w / HW);  // first row of this wave
   const int qrow = r0 + col;
-  const int shift = Lk - Lq;          // position of row r is shift + r
   const bool grp_b = w >= C::NW / 2;  // group B: one phase behind, stages V
   const int gw = w - (grp_b ? C::NW / 2 : 0);
 
@@ -275,20 +398,6 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
     }
   }
 
-  // keys any row of this workgroup may see
-  const int wg_last = min(q0 + C::BM, Lq) - 1;
-  const int pmin = shift + q0, pmax = shift + wg_last;
-  int kstart = a.window > 0 ? max(0, pmin - a.window + 1) : 0;
-  int kend = min(pmax + 1, Lk);  // exclusive
-  if (a.nsplit > 1 && kend > kstart) {
-    // this split's share of the workgroup's key tiles: contiguous runs of
-    // whole tiles, so no tile straddles two splits (an empty share leaves
-    // an empty partial)
-    const int tf = kstart / C::BN, tl = (kend - 1) / C::BN;
-    const int per = (tl - tf + a.nsplit) / a.nsplit;
-    kstart = max(kstart, (tf + split * per) * C::BN);
-    kend = min(kend, (tf + (split + 1) * per) * C::BN);
-  }
   // this wave's rows
   const int w_last = min(r0 + 31, Lq - 1);
   const int wpmin = shift + r0, wpmax = shift + w_last;
@@ -555,7 +664,9 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
 
   // ---- normalise and write: lane holds d = 32dt + 8(r/4) + 4hh + r%4 ----
   const float lt = half_sum(l_run);
-  if (a.nsplit > 1) {  // the split's partial: max in log2 units, sum, unnormalised accumulator
+  if (S > 1) {
+    // the split's partial (max in log2 units, sum, unnormalised accumulator),
+    // merged by split_merge_kernel
     if (qrow < Lq) {
       const int64_t cell = ((int64_t)(q_start + qrow) * a.num_q_heads + head) * a.nsplit + split;
       float* pa = a.part_acc + cell * D + 4 * hh;
@@ -587,21 +698,76 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   }
 }
 
+// Merge of the key-split entry: one workgroup per packed query row.  The
+// prefill launch recorded the split count S of every row it owns
+// (part_S); a row with S > 1 gets its S partials of every head merged in
+// split order, M = max m_s, out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+// Rows outside [cu_q[0], cu_q[N]) belong to no sequence and are left alone.
+template <int D>
+__global__ __launch_bounds__(256) void split_merge_kernel(PrefillArgs a, int num_seqs) {
+  const int row = blockIdx.x;
+  const int lo = min(max(a.cu_q[0], 0), a.total_q);
+  const int hi = min(max(a.cu_q[num_seqs], lo), a.total_q);
+  const int S = min(a.part_S[row], a.nsplit);
+  if (row < lo || row >= hi || S <= 1) return;
+  constexpr int TPC = D / 4;  // threads per (row, head) cell, 4 dims each
+  const int H = a.num_q_heads;
+  for (int idx = threadIdx.x; idx < H * TPC; idx += 256) {
+    const int h = idx / TPC, d0 = 4 * (idx - h * TPC);
+    const int64_t c0 = ((int64_t)row * H + h) * a.nsplit;
+    float Mx = -INFINITY;
+    for (int sp = 0; sp < S; ++sp) Mx = fmaxf(Mx, a.part_m[c0 + sp]);
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f, lsum = 0.f;
+    if (Mx != -INFINITY) {
+      for (int sp = 0; sp < S; ++sp) {
+        const float ms = a.part_m[c0 + sp];
+        if (ms == -INFINITY) continue;
+        const float wt = fast_exp2(ms - Mx);
+        lsum = fmaf(wt, a.part_l[c0 + sp], lsum);
+        const float4 av = *reinterpret_cast<const float4*>(a.part_acc + (c0 + sp) * D + d0);
+        o0 = fmaf(wt, av.x, o0);
+        o1 = fmaf(wt, av.y, o1);
+        o2 = fmaf(wt, av.z, o2);
+        o3 = fmaf(wt, av.w, o3);
+      }
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    uint2 pk;
+    pk.x = pack_bf16x2(o0 * inv, o1 * inv);
+    pk.y = pack_bf16x2(o2 * inv, o3 * inv);
+    *reinterpret_cast<uint2*>(a.out + ((int64_t)row * H + h) * D + d0) = pk;
+  }
+}
+
 template <int D, int PS, int HW>
 hipError_t launch_p3(const PrefillArgs& a, int num_seqs, int max_q, hipStream_t st) {
   using C = PrefillCfg<D, HW>;
   const int nqb = (max_q + C::BM - 1) / C::BM;
   // grouping pays where a sequence has many query blocks; with few blocks
-  // (mixed decode/prefill steps) the first z slice, where one-row sequences
-  // run, stays first in the dispatch order
-  const int zg = nqb >= 2 * PKV_PREFILL_ZGROUP ? PKV_PREFILL_ZGROUP : 1;
-  dim3 grid(a.num_kv_heads * (a.group / HW) * a.nsplit, num_seqs, (nqb + zg - 1) / zg * zg);
+  // (mixed decode/prefill steps, chunks) the launch walks a compact list of
+  // its work items instead of a grid padded to the longest sequence
+  const int X0 = a.num_kv_heads * (a.group / HW);
+  const bool compact = nqb < 2 * PKV_PREFILL_ZGROUP && num_seqs <= kCompactMaxSeqs;
+  const int zg = compact ? 0 : nqb >= 2 * PKV_PREFILL_ZGROUP ? PKV_PREFILL_ZGROUP : 1;
+  dim3 grid;
+  if (compact) {
+    // items <= X0 * nsplit * sum_j ceil(Lq_j / BM) <= X0 * nsplit * (total_q / BM + num_seqs)
+    const int64_t items = (int64_t)X0 * a.nsplit * ((int64_t)a.total_q / C::BM + num_seqs);
+    if (items > INT32_MAX) return hipErrorInvalidConfiguration;
+    grid = dim3((unsigned)items);
+  } else {
+    grid = dim3(X0 * a.nsplit, num_seqs, (nqb + zg - 1) / zg * zg);
+  }
   const size_t smem = C::LDS_BYTES;
   static std::atomic<uint64_t> lds_raised{0};
   const hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&prefill_kernel<D, PS, HW>),
                                        (int)smem, lds_raised);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((prefill_kernel<D, PS, HW>), grid, dim3(C::NT), smem, st, a, nqb, zg);
+  hipLaunchKernelGGL((prefill_kernel<D, PS, HW>), grid, dim3(C::NT), smem, st, a, nqb, zg, num_seqs);
+  if (a.nsplit <= 1) return hipGetLastError();
+  const hipError_t e2 = hipGetLastError();
+  if (e2 != hipSuccess) return e2;
+  hipLaunchKernelGGL(split_merge_kernel<D>, dim3(a.total_q), dim3(256), 0, st, a, num_seqs);
   return hipGetLastError();
 }
 
@@ -646,16 +812,11 @@ hipError_t launch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, 
     b.scale_log2 = a.scale_log2;
     return launch_attn512(b, num_seqs, max_seqlen_q, page_size, st);
   }
-  hipError_t e;
   switch (head_dim) {
-    case 64: e = launch_p1<64>(a, num_seqs, max_seqlen_q, page_size, st); break;
-    case 128: e = launch_p1<128>(a, num_seqs, max_seqlen_q, page_size, st); break;
-    default: e = launch_p1<256>(a, num_seqs, max_seqlen_q, page_size, st); break;
+    case 64: return launch_p1<64>(a, num_seqs, max_seqlen_q, page_size, st);
+    case 128: return launch_p1<128>(a, num_seqs, max_seqlen_q, page_size, st);
+    default: return launch_p1<256>(a, num_seqs, max_seqlen_q, page_size, st);
   }
-  if (e != hipSuccess || a.nsplit <= 1) return e;
-  // key splits: merge every row's partials (the split-K combine, rows = packed query rows)
-  return launch_combine(a.part_m, a.part_l, a.part_acc, a.total_q, a.num_q_heads, head_dim, a.nsplit,
-                        a.out, st);
 }
 
 }  // namespace pkv

@@ -62,5 +62,35 @@ __device__ __forceinline__ void phase_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Key splits of the split entry.  A work block -- the key tiles a prefill
+// workgroup's rows may see, or the pages of a one-row sequence -- is cut
+// into S runs of whole units, S = min(nsplit, units / min_units) (no split
+// below 2 * min_units), run s being units [units*s/S, units*(s+1)/S).  The
+// prefill kernel and the merge both derive S from the same device values.
+__device__ __forceinline__ int split_count(int units, int nsplit, int min_units) {
+  if (nsplit <= 1 || units < 2 * min_units) return 1;
+  return min(nsplit, units / min_units);
+}
+__device__ __forceinline__ int split_begin(int units, int S, int s) {
+  return (int)(((int64_t)units * s) / S);
+}
+// Keys [kstart, kend) that rows q0..last (positions shift + r) may attend.
+__device__ __forceinline__ int2 block_keys(int q0, int last, int shift, int Lk, int window) {
+  const int pmin = shift + q0, pmax = shift + last;
+  return make_int2(window > 0 ? max(0, pmin - window + 1) : 0, min(pmax + 1, Lk));
+}
+__device__ __forceinline__ int block_tiles(int2 kr, int bn) {
+  return kr.y > kr.x ? (kr.y - 1) / bn - kr.x / bn + 1 : 0;
+}
+// Pages [p0, pend) holding the keys a one-row sequence of L keys attends.
+__device__ __forceinline__ int2 row_pages(int L, int window, int ps) {
+  const int first = window > 0 ? max(0, L - window) : 0;
+  return make_int2(first / ps, (L + ps - 1) / ps);
+}
+// minimum units per run: 128 keys of a prefill block, four pages per wave
+// of a one-row sequence
+__device__ __forceinline__ int min_split_tiles(int bn) { return bn >= 128 ? 1 : 128 / bn; }
+__device__ __forceinline__ int min_split_pages(int nw) { return 4 * nw; }
+
 }  // namespace prefill_detail
 }  // namespace pkv

@@ -281,9 +281,11 @@ def test_head_dim_512_plans(P):
 
 def test_prefill_split_validation(P):
     L = P.lib()
-    # workspace: two 256-byte aligned [Tq, Hq, S] float arrays, then [Tq, Hq, S, D] floats
+    # workspace: two 256-byte aligned [Tq, Hq, S] float arrays, [Tq, Hq, S, D] floats
+    # (256-byte aligned), then the [Tq] int32 split counts of the rows
     cells = 576 * 8 * 4
-    assert L.pkv_prefill_split_workspace_bytes(576, 8, 256, 4) == 2 * ((cells * 4 + 255) // 256 * 256) + cells * 256 * 4
+    assert L.pkv_prefill_split_workspace_bytes(576, 8, 256, 4) == (
+        2 * ((cells * 4 + 255) // 256 * 256) + cells * 256 * 4 + 576 * 4)
     assert L.pkv_prefill_split_workspace_bytes(576, 8, 256, 1) == 0
     assert L.pkv_prefill_split_workspace_bytes(0, 8, 256, 4) == 0
     need = L.pkv_prefill_split_workspace_bytes(100, 8, 128, 3)
