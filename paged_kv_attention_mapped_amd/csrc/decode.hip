@@ -434,19 +434,38 @@ void decode_stream_kernel(StreamArgs sa) {
   }
 }
 
-// Merge of cut segments: one wave per merge descriptor.  The pieces are
-// taken in wave order, kMergeBatch at a time with all their loads issued
-// together, and folded into a running (max, sum, accumulator) per query
-// head, so the result does not depend on timing and a segment cut into n
-// pieces costs about n / kMergeBatch memory round trips.
-constexpr int kMergeBatch = 4;
+// Merge of cut segments: one wave per (merge descriptor, query head).  The
+// pieces are taken in wave order, kMergeBatch at a time with all their loads
+// issued together, and folded into a running (max, sum, accumulator), so the
+// result does not depend on timing and a segment cut into n pieces costs
+// about n / kMergeBatch memory round trips.  Lane l holds D/64 consecutive
+// dims (one store of its bf16 dims).
+constexpr int kMergeBatch = 8;
 
-template <int D, int G>
+// N consecutive floats of a piece; pieces are g*(D+2) floats apart, so only
+// 8-byte alignment holds and the loads are float2
+template <int N>
+__device__ __forceinline__ void load_floats(float* d, const float* p) {
+  if constexpr (N == 1) {
+    d[0] = p[0];
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; i += 2) {
+      const float2 v = *reinterpret_cast<const float2*>(p + i);
+      d[i] = v.x;
+      d[i + 1] = v.y;
+    }
+  }
+}
+
+template <int D>
 __global__ __launch_bounds__(64) void stream_merge_kernel(StreamArgs sa) {
   constexpr int EPL = D / 64;
-  // pieces in flight per batch (two at head_dim 512, so that their values stay in registers)
-  constexpr int MB = D >= 512 ? 2 : kMergeBatch;
-  const int slot = blockIdx.x, lane = threadIdx.x;
+  constexpr int MB = kMergeBatch;
+  const int slot = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const DecodeArgs& a = sa.base;
+  const int g = a.group, nw = sa.num_waves;
+  if (h >= g) return;
   // descriptor: [valid, sequence, KV head, last wave, total units]
   const int dv = lane < 5 ? sa.desc[slot * kDescInts + lane] : 0;
   if (__builtin_amdgcn_readfirstlane(dv) == 0) return;
@@ -454,63 +473,53 @@ __global__ __launch_bounds__(64) void stream_merge_kernel(StreamArgs sa) {
   const int hk = __builtin_amdgcn_readlane(dv, 2);
   const int w1 = __builtin_amdgcn_readlane(dv, 3);
   const int64_t U = __builtin_amdgcn_readlane(dv, 4);
-  const DecodeArgs& a = sa.base;
-  const int g = a.group, nw = sa.num_waves;
   const int w0 = slot >> 1;
   const int64_t stride = (int64_t)g * (D + 2);
   // waves with an empty range (possible when there are fewer units than
   // waves) hold no piece
   auto holds = [&](int w) { return (int64_t)w * U / nw < (int64_t)(w + 1) * U / nw; };
 
-  float Mr[G], Lr[G], o[G][EPL];
+  float Mr = -INFINITY, Lr = 0.f, o[EPL];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    Mr[h] = -INFINITY;
-    Lr[h] = 0.f;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) o[h][i] = 0.f;
-  }
+  for (int i = 0; i < EPL; ++i) o[i] = 0.f;
   for (int wb = w0; wb <= w1; wb += MB) {
-    float ml[MB], pv[MB][G][EPL];
+    float mk[MB], lk[MB], pv[MB][EPL];
     // loads are unconditional (a wave past w1 re-reads w1's piece) so that
     // they all leave before the first one is used
 #pragma unroll
     for (int k = 0; k < MB; ++k) {
       const int w = min(wb + k, w1);
       const float* p = sa.part + (int64_t)(w == w0 ? slot : 2 * w) * stride;
-      ml[k] = p[g * D + min(lane, 2 * g - 1)];  // lanes h: max of head h; lanes g+h: its sum
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) pv[k][h][i] = p[min(h, g - 1) * D + lane + 64 * i];
+      mk[k] = p[g * D + h];
+      lk[k] = p[g * D + g + h];
+      load_floats<EPL>(pv[k], p + h * D + EPL * lane);
     }
 #pragma unroll
     for (int k = 0; k < MB; ++k) {
       const int w = wb + k;
-      if (w > w1 || !holds(w)) continue;
+      if (w > w1 || !holds(w) || mk[k] == -INFINITY) continue;
+      const float Mn = fmaxf(Mr, mk[k]);
+      const float al = fast_exp2(Mr - Mn);
+      const float be = fast_exp2(mk[k] - Mn);
+      Lr = fmaf(Lr, al, lk[k] * be);
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        if (h >= g) continue;
-        const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml[k]), h));
-        const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ml[k]), g + h));
-        if (m == -INFINITY) continue;
-        const float Mn = fmaxf(Mr[h], m);
-        const float al = fast_exp2(Mr[h] - Mn);
-        const float be = fast_exp2(m - Mn);
-        Lr[h] = fmaf(Lr[h], al, l * be);
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) o[h][i] = fmaf(o[h][i], al, pv[k][h][i] * be);
-        Mr[h] = Mn;
-      }
+      for (int i = 0; i < EPL; ++i) o[i] = fmaf(o[i], al, pv[k][i] * be);
+      Mr = Mn;
     }
   }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    if (h >= g) continue;
-    const float inv = Lr[h] > 0.f ? 1.f / Lr[h] : 0.f;
-    uint16_t* out = a.out + ((int64_t)b * a.num_q_heads + hk * g + h) * D;
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) out[lane + 64 * i] = (uint16_t)f32_to_bf16(o[h][i] * inv);
+  const float inv = Lr > 0.f ? 1.f / Lr : 0.f;
+  uint16_t* out = a.out + ((int64_t)b * a.num_q_heads + hk * g + h) * D + EPL * lane;
+  if constexpr (EPL == 1) {
+    *out = (uint16_t)f32_to_bf16(o[0] * inv);
+  } else if constexpr (EPL == 2) {
+    *reinterpret_cast<uint32_t*>(out) = pack_bf16x2(o[0] * inv, o[1] * inv);
+  } else if constexpr (EPL == 4) {
+    *reinterpret_cast<uint2*>(out) = make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv),
+                                                pack_bf16x2(o[2] * inv, o[3] * inv));
+  } else {
+    *reinterpret_cast<uint4*>(out) = make_uint4(
+        pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv),
+        pack_bf16x2(o[4] * inv, o[5] * inv), pack_bf16x2(o[6] * inv, o[7] * inv));
   }
 }
 
@@ -618,13 +627,8 @@ hipError_t launch_decode_stream(const StreamArgs& sa, int head_dim, int page_siz
 
 template <int D>
 void launch_merge_d(const StreamArgs& sa, hipStream_t st) {
-  const dim3 grid(2 * sa.num_waves);
-  if (sa.base.group <= 2)
-    hipLaunchKernelGGL((stream_merge_kernel<D, 2>), grid, dim3(64), 0, st, sa);
-  else if (sa.base.group <= 4)
-    hipLaunchKernelGGL((stream_merge_kernel<D, 4>), grid, dim3(64), 0, st, sa);
-  else
-    hipLaunchKernelGGL((stream_merge_kernel<D, 8>), grid, dim3(64), 0, st, sa);
+  hipLaunchKernelGGL((stream_merge_kernel<D>), dim3(2 * sa.num_waves, sa.base.group), dim3(64), 0, st,
+                     sa);
 }
 
 hipError_t launch_stream_merge(const StreamArgs& sa, int head_dim, hipStream_t st) {

@@ -698,11 +698,12 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   }
 }
 
-// Merge of the key-split entry: one workgroup per packed query row.  The
-// prefill launch recorded the split count S of every row it owns
-// (part_S); a row with S > 1 gets its S partials of every head merged in
-// split order, M = max m_s, out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
-// Rows outside [cu_q[0], cu_q[N]) belong to no sequence and are left alone.
+// Merge of the key-split entry: workgroups (packed query row, chunk of
+// its heads x dims).  The prefill launch recorded the run count S of every
+// row it owns (part_S); a row with S > 1 gets its S partials merged in run
+// order, four at a time with all their loads in flight, into a running
+// (max, sum, accumulator).  Rows outside [cu_q[0], cu_q[N]) belong to no
+// sequence and are left alone.
 template <int D>
 __global__ __launch_bounds__(256) void split_merge_kernel(PrefillArgs a, int num_seqs) {
   const int row = blockIdx.x;
@@ -710,33 +711,41 @@ __global__ __launch_bounds__(256) void split_merge_kernel(PrefillArgs a, int num
   const int hi = min(max(a.cu_q[num_seqs], lo), a.total_q);
   const int S = min(a.part_S[row], a.nsplit);
   if (row < lo || row >= hi || S <= 1) return;
-  constexpr int TPC = D / 4;  // threads per (row, head) cell, 4 dims each
+  constexpr int TPC = D / 4;  // threads per (row, head), 4 dims each
   const int H = a.num_q_heads;
-  for (int idx = threadIdx.x; idx < H * TPC; idx += 256) {
-    const int h = idx / TPC, d0 = 4 * (idx - h * TPC);
-    const int64_t c0 = ((int64_t)row * H + h) * a.nsplit;
-    float Mx = -INFINITY;
-    for (int sp = 0; sp < S; ++sp) Mx = fmaxf(Mx, a.part_m[c0 + sp]);
-    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f, lsum = 0.f;
-    if (Mx != -INFINITY) {
-      for (int sp = 0; sp < S; ++sp) {
-        const float ms = a.part_m[c0 + sp];
-        if (ms == -INFINITY) continue;
-        const float wt = fast_exp2(ms - Mx);
-        lsum = fmaf(wt, a.part_l[c0 + sp], lsum);
-        const float4 av = *reinterpret_cast<const float4*>(a.part_acc + (c0 + sp) * D + d0);
-        o0 = fmaf(wt, av.x, o0);
-        o1 = fmaf(wt, av.y, o1);
-        o2 = fmaf(wt, av.z, o2);
-        o3 = fmaf(wt, av.w, o3);
-      }
+  const int idx = blockIdx.y * 256 + threadIdx.x;
+  if (idx >= H * TPC) return;
+  const int h = idx / TPC, d0 = 4 * (idx - h * TPC);
+  const int64_t c0 = ((int64_t)row * H + h) * a.nsplit;
+  float Mr = -INFINITY, Lr = 0.f, o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    float m[4], l[4];
+    float4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {  // unconditional loads (past S: run S-1 again, unused)
+      const int64_t c = c0 + min(s0 + k, S - 1);
+      m[k] = a.part_m[c];
+      l[k] = a.part_l[c];
+      v[k] = *reinterpret_cast<const float4*>(a.part_acc + c * D + d0);
     }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    uint2 pk;
-    pk.x = pack_bf16x2(o0 * inv, o1 * inv);
-    pk.y = pack_bf16x2(o2 * inv, o3 * inv);
-    *reinterpret_cast<uint2*>(a.out + ((int64_t)row * H + h) * D + d0) = pk;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (s0 + k >= S || m[k] == -INFINITY) continue;
+      const float Mn = fmaxf(Mr, m[k]);
+      const float al = fast_exp2(Mr - Mn), be = fast_exp2(m[k] - Mn);
+      Lr = fmaf(Lr, al, l[k] * be);
+      o0 = fmaf(o0, al, v[k].x * be);
+      o1 = fmaf(o1, al, v[k].y * be);
+      o2 = fmaf(o2, al, v[k].z * be);
+      o3 = fmaf(o3, al, v[k].w * be);
+      Mr = Mn;
+    }
   }
+  const float inv = Lr > 0.f ? 1.f / Lr : 0.f;
+  uint2 pk;
+  pk.x = pack_bf16x2(o0 * inv, o1 * inv);
+  pk.y = pack_bf16x2(o2 * inv, o3 * inv);
+  *reinterpret_cast<uint2*>(a.out + ((int64_t)row * H + h) * D + d0) = pk;
 }
 
 template <int D, int PS, int HW>
@@ -767,7 +776,8 @@ hipError_t launch_p3(const PrefillArgs& a, int num_seqs, int max_q, hipStream_t 
   if (a.nsplit <= 1) return hipGetLastError();
   const hipError_t e2 = hipGetLastError();
   if (e2 != hipSuccess) return e2;
-  hipLaunchKernelGGL(split_merge_kernel<D>, dim3(a.total_q), dim3(256), 0, st, a, num_seqs);
+  const unsigned chunks = (unsigned)((a.num_q_heads * (D / 4) + 255) / 256);
+  hipLaunchKernelGGL(split_merge_kernel<D>, dim3(a.total_q, chunks), dim3(256), 0, st, a, num_seqs);
   return hipGetLastError();
 }
 
