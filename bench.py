@@ -494,11 +494,13 @@ def recorded_traffic(config: str, src_hash: str, fused: bool = False):
 
 
 # ---------------------------------------------------------------------------
-def prefill_measure(torch, P, iters=20, warmup=5):
+def prefill_measure(torch, P, iters=20, warmup=40):
     """The long prefill's MFMA fraction: each launch timed by its own event
     pair, back to back on resident K/V, and the same kernel inside the
     long-prefill step (its prompts' rows appended just before it); medians
-    over the launches."""
+    over the launches.  The warm-up is long enough for the clock to settle:
+    the first few dozen launches of a burst run up to ~10% faster than the
+    steady state that follows, with or without an append between them."""
     import workloads as W
     wl = W.make("long_prefill")
     st = Step(wl, torch, P)
@@ -530,7 +532,8 @@ def prefill_measure(torch, P, iters=20, warmup=5):
             "min_ms": round(float(ms.min()), 4), "tflops": round(tf, 2),
             "peak_tflops": BF16_PEAK_TFLOPS, "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
             "flops_per_call": fl,
-            "timing": f"median of {iters} launches back to back, each between its own events",
+            "timing": f"median of {iters} launches back to back, each between its own events, "
+                      f"after {warmup} untimed launches (steady clock)",
             "in_step": {"ms_per_call": round(smed, 4), "tflops": round(stf, 2),
                         "mfma_frac": round(stf / BF16_PEAK_TFLOPS, 4),
                         "timing": "median of the prefill launch inside the long-prefill step "

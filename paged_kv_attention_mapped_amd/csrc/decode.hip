@@ -115,20 +115,14 @@ void decode_kernel(DecodeArgs a) {
     }
     wd.process(bf, tok_of[slot], ok_of[slot] ? first_key : INT_MAX, L, a.scale_log2);
   };
-  // The next step's loads are issued unconditionally (past the end they
-  // reload the last step, unused): with a conditional load the compiler
-  // cannot count the loads in flight and waits for all of them before every
-  // step, prefetch included.
   typename W::Buf b0, b1;
-  if (nsteps > 0) {
-    load(b0, 0, 0);
-    for (int j = 0; j < nsteps; j += 2) {
-      load(b1, min(j + 1, nsteps - 1), 1);
-      process(b0, 0);
-      if (j + 1 >= nsteps) break;
-      load(b0, min(j + 2, nsteps - 1), 0);
-      process(b1, 1);
-    }
+  if (nsteps > 0) load(b0, 0, 0);
+  for (int j = 0; j < nsteps; j += 2) {
+    if (j + 1 < nsteps) load(b1, j + 1, 1);
+    process(b0, 0);
+    if (j + 1 >= nsteps) break;
+    if (j + 2 < nsteps) load(b0, j + 2, 0);
+    process(b1, 1);
   }
 
   float M, lw;
@@ -420,16 +414,14 @@ void decode_stream_kernel(StreamArgs sa) {
     wd.process(bf, si.tok0, si.ok ? sg.fk : INT_MAX, sg.L, a.scale_log2);
     if (si.part == W::UPP - 1 && (si.u == sg.s1 - 1 || si.u == u1 - 1)) finish(sg);
   };
-  // next-step loads unconditional (past the end: the last step again,
-  // unused), so that the compiler's wait counts keep the prefetch in flight
   StepInfo i0, i1;
   typename W::Buf b0, b1;
   load(b0, i0, 0);
   for (int j = 0; j < nsteps; j += 2) {
-    load(b1, i1, min(j + 1, nsteps - 1));
+    if (j + 1 < nsteps) load(b1, i1, j + 1);
     process(b0, i0);
     if (j + 1 >= nsteps) break;
-    load(b0, i0, min(j + 2, nsteps - 1));
+    if (j + 2 < nsteps) load(b0, i0, j + 2);
     process(b1, i1);
   }
 }

@@ -155,18 +155,14 @@ __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, 
   auto process = [&](const typename W::Buf& bf, int slot) {
     wd.process(bf, tok_of[slot], ok_of[slot] ? first_key : INT_MAX, L, a.scale_log2);
   };
-  // next-step loads unconditional (past the end: the last step again,
-  // unused), so that the compiler's wait counts keep the prefetch in flight
   typename W::Buf b0, b1;
-  if (nsteps > 0) {
-    load(b0, 0, 0);
-    for (int i = 0; i < nsteps; i += 2) {
-      load(b1, min(i + 1, nsteps - 1), 1);
-      process(b0, 0);
-      if (i + 1 >= nsteps) break;
-      load(b0, min(i + 2, nsteps - 1), 0);
-      process(b1, 1);
-    }
+  if (nsteps > 0) load(b0, 0, 0);
+  for (int i = 0; i < nsteps; i += 2) {
+    if (i + 1 < nsteps) load(b1, i + 1, 1);
+    process(b0, 0);
+    if (i + 1 >= nsteps) break;
+    if (i + 2 < nsteps) load(b0, i + 2, 0);
+    process(b1, 1);
   }
 
   float M, lw;
