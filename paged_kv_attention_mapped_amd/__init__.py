@@ -534,8 +534,9 @@ def prefill_split_workspace_bytes(total_q, num_q_heads, head_dim, num_splits):
 def prefill_varlen_split(q, k_pool, v_pool, block_tables, cu_seq_lens_q, cu_seq_lens_k,
                          max_seqlen_q, max_seqlen_k, *, page_size, num_splits, scale=None, window=0,
                          out=None, workspace=None, stream=None):
-    """``pkv_prefill_varlen_split``: varlen prefill with each workgroup's keys cut into
-    ``num_splits`` runs and merged by the split-K combine; returns bf16 [Tq, Hq, D]."""
+    """``pkv_prefill_varlen_split``: varlen prefill with the key tiles of long work cut
+    into at most ``num_splits`` runs, the cut rows merged by a second launch; returns
+    bf16 [Tq, Hq, D]."""
     _bf16(q, "q"); _bf16(k_pool, "k_pool"); _bf16(v_pool, "v_pool")
     _i32(block_tables, "block_tables"); _i32(cu_seq_lens_q, "cu_q"); _i32(cu_seq_lens_k, "cu_k")
     Tq, hq, d = q.shape

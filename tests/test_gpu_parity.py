@@ -602,6 +602,34 @@ def test_prefill_many_blocks_every_row(P, shape):
     check_close(host_bits(out), ref, f"many blocks {shape}")
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+def test_varlen_over_1024_sequences(P, splits):
+    """More sequences than the compact work list takes (1 024), so the launch
+    uses the padded grid: 1 030 decode rows and three prompts of few query
+    blocks, with and without key runs; the output starts as NaN and every
+    row is compared."""
+    cfg = W.Config("many_seqs", 20260102, 8, 2, 128, 16,
+                   decode_ctx=("uniform", 1030, 1, 200), prefill_new=("fixed", (70, 1, 129)))
+    wl = W.build(cfg)
+    g = GpuPools(wl)
+    g.write("prefix")
+    g.write("new")
+    o = OraclePools(wl)
+    cq, ck = wl.cu_lens(wl.new_lens), wl.cu_lens(wl.total_lens)
+    qd, qp = wl.queries(0)
+    q = np.concatenate([qd, qp])
+    say(f"[prefill] {wl.num_seqs} sequences, {q.shape[0]} rows, {splits} runs")
+    out = torch.full(q.shape, int(W.BF16_NAN), dtype=torch.int16, device="cuda")
+    P.prefill_varlen_split(dev_bits(q), g.k, g.v, dev_i32(wl.block_tables), dev_i32(cq),
+                           dev_i32(ck), int(wl.new_lens.max()), int(wl.total_lens.max()),
+                           page_size=wl.page_size, num_splits=splits, scale=wl.scale,
+                           window=wl.window, out=out)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_varlen(q, o.k, o.v, wl.block_tables, cq, ck, wl.page_size, wl.scale,
+                                wl.window)
+    check_close(host_bits(out), ref, f"{wl.num_seqs} sequences, {splits} runs")
+
+
 def test_prefill_edge_cases(P):
     # ragged lengths around tile sizes, an empty sequence, a chunk after a prefix
     wl = W.make("mixed_step", decode_ctx=("fixed", ()), prefill_new=("fixed", (1, 31, 32, 0, 33, 127, 129)),
