@@ -859,7 +859,9 @@ def main():
         pk_ms = float(np.mean([a.elapsed_time(b) for a, b in pevs]))
         fl = prefill_flops(wl)
         tf = fl / (pk_ms * 1e-3) / 1e12
-        pre = {"kernel": "attn512_kernel" if wl.head_dim == 512 else "prefill_kernel",
+        pre = {"kernel": ("prefill_kernel (head_dim 512: one MFMA stream per key tile) + "
+                          "attn512_kernel for the one-row sequences (none here)"
+                          if wl.head_dim == 512 else "prefill_kernel"),
                "bound": "mfma", "achieved": round(tf, 3),
                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                "traffic": None, "avg_kernel_ms": round(pk_ms, 5), "algorithmic_flops_per_launch": fl}

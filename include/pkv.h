@@ -486,7 +486,10 @@ pkv_status pkv_decode_stream_merge(const void* workspace, size_t workspace_bytes
  * decode machinery (its pages split over the workgroup's waves) rather than
  * with 32-row MFMA tiles, so a step mixing decode rows and prompts is one
  * launch per layer (the CB paged kernel likewise takes the whole mixed
- * batch through cu_seq_lens_q on every forward).
+ * batch through cu_seq_lens_q on every forward).  At head_dim 512 the
+ * one-row sequences take a second launch (the head-dim-split kernel, whose
+ * MFMA columns are the group's heads) after the prompts' launch, both on
+ * `stream`.
  */
 pkv_status pkv_prefill_varlen(const uint16_t* q, const uint16_t* k_pool, const uint16_t* v_pool,
                               const int32_t* block_tables, int32_t max_pages_per_seq,

@@ -345,6 +345,7 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a)
     Lk = a.seq_lens[j];
   }
   Lk = max(0, min(Lk, a.max_pages * PS));
+  if (a.one_row_only && Lq != 1) return;
   const int row0 = rb * R;
   if (row0 >= Lq) return;
   const int nrows = min(R, Lq - row0);

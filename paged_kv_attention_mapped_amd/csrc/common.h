@@ -266,6 +266,7 @@ struct Attn512Args {
   int window;
   int num_splits;
   int pages_per_split;
+  int one_row_only;         // varlen rows: attend only the one-row sequences
   int total_q;              // varlen rows: packed query rows (cu_q is clamped to it)
   float scale_log2;
 };

@@ -42,6 +42,13 @@
 // conflict-free block with a compile-time offset.  Tile t+3 is requested
 // in V(t) and waited for at the end of V(t+2); block-table entries are
 // read through the scalar cache one tile before their tile.
+//
+// Head dim 512.  Four waves of 32 rows, one per SIMD: O^T of 32 rows takes
+// all 256 AGPRs and the Q operands half the VGPRs, so the score tile is
+// accumulated in VGPRs by inline-assembly MFMAs and the rare rescale of O
+// is written out per AGPR.  Tiles are staged in whole 128-byte lines into
+// two K and three V ring slots (160 KB of LDS), and a key tile is one MFMA
+// stream that carries the next tile's softmax and loads (co_loop).
 #include <math.h>
 
 #include "common.h"
@@ -74,7 +81,7 @@ constexpr int kCompactMaxSeqs = 1024;
 
 template <int D, int HW>
 struct PrefillCfg {
-  static constexpr int NW = D == 256 ? 4 : PKV_PREFILL_WAVES;  // waves per workgroup
+  static constexpr int NW = D >= 256 ? 4 : PKV_PREFILL_WAVES;  // waves per workgroup
   static constexpr int NT = NW * 64;           // threads
   static constexpr int G = NW / 2;             // waves per group
   static constexpr int QB = NW / HW;           // waves along the rows
@@ -84,9 +91,13 @@ struct PrefillCfg {
   static constexpr int NU = BN / 16;           // 16-key steps of O^T
   static constexpr int KS = D / 16;            // k-steps of S^T
   static constexpr int DT = D / 32;            // 32-row tiles of O^T
-  static constexpr int NB = 4;                 // ring depth (tiles) per tensor
+  // ring depth (tiles) of K (NB) and V (NBV); at head_dim 512 a tile is
+  // 32 KB: two K and three V tiles (160 KB), all waves in one phase (LOCK)
+  static constexpr int NB = D == 512 ? 2 : 4;
+  static constexpr int NBV = D == 512 ? 3 : NB;
+  static constexpr bool LOCK = NB == 2;
   static constexpr int TILE = BN * D * 2;      // bytes of one K (or V) tile
-  static constexpr int LDS_BYTES = 2 * NB * TILE;
+  static constexpr int LDS_BYTES = (NB + NBV) * TILE;
   // each wave moves DT 1 KB blocks per tile: K blocks gw*DT .. +DT-1 (one
   // 32-key row tile), or V step u = gw for all DT column tiles
   static_assert(NW % 2 == 0 && NU == G && KS % DT == 0, "staging split");
@@ -244,8 +255,9 @@ __device__ __forceinline__ int seq_splits(const PrefillArgs& a, const SeqGeo& g)
 // sequence has one block.  Workgroup `item` scans the sequences' item
 // counts, NT at a time with a workgroup prefix sum, and finds its
 // sequence j and its index k among j's items; false past the end of the
-// list.  lds: NT/64 + 2 ints.
-template <int NT, int BM, int BN, int PS, int NW>
+// list.  Without ONE_ROW one-row sequences have no items (another launch
+// takes them).  lds: NT/64 + 2 ints.
+template <int NT, int BM, int BN, int PS, int NW, bool ONE_ROW>
 __device__ bool find_item(const PrefillArgs& a, int num_seqs, int X0, int item, int* lds,
                           int& j, int& k) {
   constexpr int NWV = NT / 64;
@@ -257,7 +269,7 @@ __device__ bool find_item(const PrefillArgs& a, int num_seqs, int X0, int item, 
     int cnt = 0;
     if (t < num_seqs) {
       const SeqGeo g = seq_geo<PS>(a, t);
-      if (g.Lq > 0)
+      if (g.Lq > (ONE_ROW ? 0 : 1))
         cnt = (g.Lq == 1 ? 1 : (g.Lq + BM - 1) / BM) * seq_splits<BM, BN, PS, NW>(a, g) * X0;
     }
     int v = cnt;  // inclusive prefix within the wave
@@ -295,6 +307,10 @@ template <int D, int PS, int HW>
 __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(PrefillArgs a, int nqb, int zg,
                                                                            int num_seqs) {
   using C = PrefillCfg<D, HW>;
+  // one-row sequences run decode_row here, except at head_dim 512, where a
+  // wave-level decoder does not fit the registers (launch_prefill sends
+  // them to the head-dim-split kernel)
+  constexpr bool kOneRow = D != 512;
   // [K ring: NB tiles][V ring: NB tiles]
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
@@ -305,7 +321,7 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
     // compact work list (few query blocks per sequence): the workgroups
     // that find nothing are all at the end of the dispatch order
     int k;
-    if (!find_item<C::NT, C::BM, C::BN, PS, C::NW>(
+    if (!find_item<C::NT, C::BM, C::BN, PS, C::NW, kOneRow>(
             a, num_seqs, X0, (int)blockIdx.x,
             reinterpret_cast<int*>(reinterpret_cast<char*>(smem) + C::LDS_BYTES - 256), j, k))
       return;
@@ -342,10 +358,12 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
 
   const SeqGeo geo = seq_geo<PS>(a, j);
   const int q_start = geo.q_start, Lq = geo.Lq, Lk = geo.Lk;
-  if (Lq == 1) {
-    if (b == 0)
-      decode_row<D, PS, HW, C::NW>(a, j, hk, hk * a.group + hg * HW, q_start, Lk, split,
-                                   reinterpret_cast<float*>(smem), bx == 0);
+  if (Lq <= 1) {
+    if constexpr (kOneRow) {
+      if (Lq == 1 && b == 0)
+        decode_row<D, PS, HW, C::NW>(a, j, hk, hk * a.group + hg * HW, q_start, Lk, split,
+                                     reinterpret_cast<float*>(smem), bx == 0);
+    }
     return;
   }
   const int qb = (zg == 0 ? (Lq + C::BM - 1) / C::BM : nqb) - 1 - b;
@@ -414,12 +432,27 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   // when pages hold 16 keys).  Each run is one scalar buffer resource
   // bounded to its keys below kend: the hardware writes zeros for lanes past
   // the bound, so keys past kend and unusable pages read as zeros.
-  constexpr int NR = PS >= 32 ? 1 : 2;           // page runs per wave and tile
+  //
+  // At head_dim 512 (CO) every load reads whole 128-byte lines: 8 rows x
+  // 128 bytes per instruction instead of 32 rows x 32 bytes (K) or 16 rows x
+  // 64 bytes (V), which cuts the time the vector memory path spends on a
+  // tile's loads fourfold.  Wave w stages rows 8w..8w+7 of both tensors (one
+  // page run, one table entry), with the loads spread through the MFMA
+  // stream (co_loop below).
+  //   K: block (rg, cg) (rows 8rg.., 16-byte chunks 8cg..) at (4cg + rg) KB,
+  //      lane 8i+x's 16 bytes = row 8rg+i, chunk 8cg + (x ^ i ^ (rg&1)); the
+  //      XOR keeps the MFMA operand reads free of bank conflicts.
+  //   V: block (u, p, h) (keys 16u+8h.., dims 64p..) at ((u*DT/2 + p)*2 + h)
+  //      KB; its halves are the lo/hi 512-byte pieces of the transposed-read
+  //      layout below for dt = 2p and 2p+1.
+  constexpr bool CO = D == 512;
+  constexpr int NR = (CO || PS >= 32) ? 1 : 2;   // page runs per wave and tile
   constexpr int NDMA = C::DT * NR;               // LDS-destination loads per wave and tile
   constexpr int VM_AHEAD = 2 * NDMA;             // loads of the two tiles requested after
+  static_assert(CO == C::LOCK && (!CO || C::KT == 1), "whole-line staging layout");
   const uint16_t* src = (grp_b ? a.v_pool : a.k_pool) + (int64_t)hk * a.head_stride;
-  const int w0 = grp_b ? 16 * gw : 32 * ((gw * C::DT) / C::KS);
-  const int rr_all = grp_b ? 16 : 32;            // rows of this wave
+  const int w0 = CO ? 8 * w : grp_b ? 16 * gw : 32 * ((gw * C::DT) / C::KS);
+  const int rr_all = CO ? 8 : grp_b ? 16 : 32;   // rows of this wave
   const int RR = NR == 2 ? 16 : rr_all;          // rows per run
   const int roff = (NR == 2 && !grp_b) ? 16 : 0; // first row of run 1
   const int sstride = grp_b ? 64 : 32;           // global bytes between the wave's blocks
@@ -437,6 +470,23 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   // both runs are the same page run, so both groups issue the same loads)
   const bool run1 = NR == 2 && (lane & 16) != 0;
   const int loff = ((run1 && !grp_b ? lrow - 16 : lrow) * D + 8 * lchunk) * 2;  // bytes from the run base
+  // CO: lane offsets from the run base of the wave's K and V loads, and the
+  // K operand reads' lane offsets for k-steps ks = 4cg + m
+  int coff_k = 0, coff_v = 0, kaddr[4] = {0, 0, 0, 0};
+  if constexpr (CO) {
+    {
+      const int i = lane >> 3, x = lane & 7;
+      coff_k = (i * D + 8 * (x ^ i ^ (w & 1))) * 2;
+    }
+    {
+      const int s5 = lane & 31;
+      const int kk = 4 * (s5 >> 4) + ((s5 >> 1) & 3), cc = 2 * ((s5 >> 3) & 1) + (s5 & 1);
+      coff_v = (kk * D + 32 * (lane >> 5) + 8 * cc) * 2;
+    }
+    const int r = lane & 31, rg = r >> 3, i = r & 7, h = lane >> 5;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) kaddr[m] = rg * 1024 + 16 * (8 * i + ((2 * m + h) ^ i ^ (rg & 1)));
+  }
   // block-table row, read through the scalar cache (it is never written here)
   const __attribute__((address_space(4))) int32_t* bt_row =
       (const __attribute__((address_space(4))) int32_t*)(a.block_tables + (int64_t)j * a.max_pages);
@@ -478,6 +528,27 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
     }
   };
 
+  // CO staging: the run of wave w in tile s of a pool, and its loads
+  constexpr int NCG = C::DT / 2;  // 128-byte column groups of a row
+  auto co_rsrc = [&](int s, int phys, const uint16_t* pool) {
+    const int kb = s * C::BN + w0;
+    const bool ok = kb < kend && phys >= 0 && phys < a.num_pages;
+    const int valid = ok ? min(kend - kb, 8) : 0;
+    return sgpr_rsrc(pool + (int64_t)hk * a.head_stride + (ok ? ((int64_t)phys * PS + kb % PS) * D : 0),
+                     valid * D * 2);
+  };
+  auto co_dma_k = [&](int s, int phys) {  // K blocks (w, cg) of tile s
+    const i32x4 rs = co_rsrc(s, phys, a.k_pool);
+    const uint32_t m0 = lds0 + (s & (C::NB - 1)) * C::TILE + w * 1024;
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) load_lds16(rs, m0 + cg * 4096, coff_k, 128 * cg);
+  };
+  // V block (w/2, p, w%2) of a tile into V ring slot vslot
+  auto co_dma_v = [&](const i32x4& rs, int vslot, int p) {
+    const uint32_t m0 = lds0 + (C::NB + vslot) * C::TILE + ((w >> 1) * C::DT + (w & 1)) * 1024;
+    load_lds16(rs, m0 + p * 2048, coff_v, 128 * p);
+  };
+
   // Matrix phase M(t): O^T += V(t)^T P(t)^T, then S(t+1)^T = K(t+1) Q^T, as
   // one stream of MFMA jobs whose LDS operands are requested LA jobs ahead
   // (the scheduling barriers keep that order).  A V job (u, dt) takes the
@@ -494,7 +565,7 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
     bf16x8 opnd[LA + 1];
     f32x16 s[C::KT];
     auto fetch = [&](auto J) {
-      constexpr int jj = decltype(J)::value;
+      constexpr int jj = decltype(J)::value, slot = jj % (LA + 1);
       if constexpr (jj < NPV) {
         constexpr int u = jj / C::DT, dt = jj % C::DT;
         const char* v0 = vl + (u * C::DT + dt) * 1024;
@@ -504,23 +575,23 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
             (lds_s16x4*)(__attribute__((address_space(3))) char*)(v0 + 512));
         const uint2 l2 = __builtin_bit_cast(uint2, lo);
         const uint2 h2 = __builtin_bit_cast(uint2, hi);
-        opnd[jj % (LA + 1)] = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
+        opnd[slot] = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
       } else {
         constexpr int q = jj - NPV, kt = q % C::KT, ks = q / C::KT;
-        opnd[jj % (LA + 1)] = as_bf16x8(*reinterpret_cast<const uint4*>(kl + (kt * C::KS + ks) * 1024));
+        opnd[slot] = as_bf16x8(*reinterpret_cast<const uint4*>(kl + (kt * C::KS + ks) * 1024));
       }
     };
     static_for<0, LA>(fetch);
     static_for<0, NJ>([&](auto J) {
-      constexpr int jj = decltype(J)::value;
+      constexpr int jj = decltype(J)::value, slot = jj % (LA + 1);
       if constexpr (jj + LA < NJ) fetch(std::integral_constant<int, jj + LA>{});
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (jj < NPV) {
         constexpr int u = jj / C::DT, dt = jj % C::DT;
-        acc[dt] = mfma32(opnd[jj % (LA + 1)], pop[u], acc[dt]);
+        acc[dt] = mfma32(opnd[slot], pop[u], acc[dt]);
       } else {
         constexpr int q = jj - NPV, kt = q % C::KT, ks = q / C::KT;
-        s[kt] = mfma32(opnd[jj % (LA + 1)], qop[ks], ks == 0 ? f32x16{} : s[kt]);
+        s[kt] = mfma32(opnd[slot], qop[ks], ks == 0 ? f32x16{} : s[kt]);
       }
     });
 #pragma unroll
@@ -528,23 +599,200 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   };
   // S^T of key tile t_first (prologue), same block layout
   auto qk_first = [&](f32x16 (&st)[C::KT], int t) {
-    const char* kl = (const char*)smem + (t & (C::NB - 1)) * C::TILE + 16 * lane;
+    const char* kl = (const char*)smem + (t & (C::NB - 1)) * C::TILE + (CO ? 0 : 16 * lane);
 #pragma unroll
     for (int kt = 0; kt < C::KT; ++kt) {
       f32x16 sacc = {};
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
-        sacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(kl + (kt * C::KS + ks) * 1024)),
-                      qop[ks], sacc);
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const char* ka = CO ? kl + (ks >> 2) * 4096 + kaddr[ks & 3] : kl + (kt * C::KS + ks) * 1024;
+        const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4*>(ka));
+        if constexpr (!CO)
+          sacc = mfma32(kop, qop[ks], sacc);
+        else if (ks == 0)
+          sacc = mfma32_v_first(kop, qop[ks]);
+        else
+          mfma32_v_acc(sacc, kop, qop[ks]);
+      }
+      if constexpr (CO) mfma_settle(sacc);
       st[kt] = sacc;
     }
   };
 
-  // Every wave executes the same number of barriers: group B one extra
-  // before its first phase, group A one extra after its last.  Tile loads
-  // are issued unconditionally (tiles past the end read zeros), so every
-  // wave issues the same sequence and each wait count below is exact.
-  if (kend > kstart) {
+  // ---- head_dim 512: one phase per key tile ----
+  // Step t runs one MFMA stream: S(t+1) = K(t+1) Q^T (32 jobs, with the
+  // loads of K(t+2) among them), then O += V(t) P(t) (32 jobs, with the
+  // loads of V(t+2) and the softmax of S(t+1) among them), so that the
+  // vector work and the loads run under the MFMAs.  P(t) was formed with
+  // the maximum before S(t+1); a rescale that S(t+1) asks for is applied
+  // to O at the start of step t+1.  One barrier closes the step: K(t+2) (needed
+  // first thing in step t+1) and V(t+1) have landed by then, V(t+2) may
+  // still be in flight.  K ring: slot t%2; V ring: slot t%3.
+  auto co_loop = [&]() {
+    if (kend <= kstart) return;
+    constexpr int LA = PKV_PREFILL_LOOKAHEAD, NK = C::KS, NJ = NK + C::NU * C::DT;
+    static_assert(!CO || (C::NBV == 3 && C::NB == 2 && NK == 32 && NJ == 64), "head_dim 512 stream");
+    const int t_first = kstart / C::BN, t_last = (kend - 1) / C::BN;
+    auto bt1 = [&](int s) { return bt_row[min((s * C::BN + w0) / PS, a.max_pages - 1)]; };
+    // softmax of one 32-key tile in stages (fed a score tile whose MFMAs
+    // have settled); `live` = false computes without committing anything
+    f32x16 sc;  // the scores, then (from stage 3) their probabilities
+    float mx = -INFINITY, alpha = 1.f, mc = 0.f;
+    bool any_raise = false;
+    auto soft = [&](auto Q, int k0, bool live, bf16x8 (&pn)[C::NU]) {
+      constexpr int q = decltype(Q)::value;
+      if constexpr (q == 0) {
+        const bool need_mask = (k0 + C::BN - 1 > wpmin) ||
+                               (a.window > 0 && wpmax - k0 >= a.window) || (k0 + C::BN > Lk);
+        if (need_mask) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kp = k0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+            const bool ok = kp <= mypos && kp < Lk && (a.window <= 0 || mypos - kp < a.window);
+            sc[r] = ok ? sc[r] : -INFINITY;
+          }
+        }
+      } else if constexpr (q == 1) {
+        mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+        mx = half_max(mx);
+      } else if constexpr (q == 2) {
+        const bool raise = live && (mx - m_run) * c > kRescaleSlack;
+        any_raise = __builtin_amdgcn_ballot_w64(raise) != 0;
+        const float m_new = raise ? mx : m_run;
+        alpha = raise ? fast_exp2((m_run - m_new) * c) : 1.f;  // 0 from -inf
+        l_run *= alpha;
+        m_run = m_new;
+        mc = (m_run == -INFINITY) ? 0.f : m_run * c;
+      } else if constexpr (q >= 3 && q < 11) {
+        constexpr int e = 2 * (q - 3);
+        sc[e] = fast_exp2(fmaf(sc[e], c, -mc));
+        sc[e + 1] = fast_exp2(fmaf(sc[e + 1], c, -mc));
+      } else if constexpr (q == 11) {
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) psum += sc[e];
+        if (live) l_run += psum;
+#pragma unroll
+        for (int u = 0; u < C::NU; ++u) {
+          uint4 pp;
+          pp.x = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)sc[8 * u], (__bf16)sc[8 * u + 1]});
+          pp.y = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)sc[8 * u + 2], (__bf16)sc[8 * u + 3]});
+          pp.z = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)sc[8 * u + 4], (__bf16)sc[8 * u + 5]});
+          pp.w = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)sc[8 * u + 6], (__bf16)sc[8 * u + 7]});
+          pn[u] = as_bf16x8(pp);
+        }
+      }
+    };
+    auto rescale = [&]() {  // O *= alpha, once the last MFMA on O has settled
+      if (!any_raise) return;
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) scale_agpr(acc[dt], alpha);
+    };
+
+    // prologue: K and V of tiles t_first and t_first+1 with the Q loads,
+    // then S(t_first) and P(t_first)
+    int vslot = t_first % C::NBV;
+    int pe = bt1(t_first + 2);
+    {
+      const int p0 = bt1(t_first), p1 = bt1(t_first + 1);
+      co_dma_k(t_first, p0);
+      co_dma_k(t_first + 1, p1);
+      const i32x4 r0 = co_rsrc(t_first, p0, a.v_pool), r1 = co_rsrc(t_first + 1, p1, a.v_pool);
+      const int vs1 = vslot == C::NBV - 1 ? 0 : vslot + 1;
+#pragma unroll
+      for (int q = 0; q < NCG; ++q) co_dma_v(r0, vslot, q);
+#pragma unroll
+      for (int q = 0; q < NCG; ++q) co_dma_v(r1, vs1, q);
+    }
+    phase_barrier<0>();
+    bf16x8 pop[C::NU];
+    {
+      f32x16 st0[C::KT];
+      qk_first(st0, t_first);
+      sc = st0[0];
+      static_for<0, 12>([&](auto Q) { soft(Q, t_first * C::BN, true, pop); });
+      // O is still zero: nothing to rescale
+    }
+    phase_barrier<63>();  // every wave has read K(t_first) before K(t_first+2) lands there
+
+    for (int t = t_first; t <= t_last; ++t) {
+      // the rescale the previous step's softmax asked for, before O += V(t) P(t)
+      if (t > t_first) rescale();
+      const bool live = t < t_last;
+      const int pnext = bt1(t + 3);
+      const i32x4 rk = co_rsrc(t + 2, pe, a.k_pool), rv = co_rsrc(t + 2, pe, a.v_pool);
+      const uint32_t kdst = lds0 + (t & 1) * C::TILE + w * 1024;        // K(t+2): slot t%2
+      const int vs2 = vslot == 0 ? C::NBV - 1 : vslot - 1;             // V(t+2): slot (t+2)%3
+      const char* kl = (const char*)smem + ((t + 1) & 1) * C::TILE;
+      const char* vl = (const char*)smem + (C::NB + vslot) * C::TILE + 8 * lane;
+      const int k1 = (t + 1) * C::BN;
+      bf16x8 opnd[LA + 1], pn[C::NU];
+      f32x16 s;
+      auto fetch = [&](auto J) {
+        constexpr int jj = decltype(J)::value, slot = jj % (LA + 1);
+        if constexpr (jj < NK) {
+          opnd[slot] = as_bf16x8(*reinterpret_cast<const uint4*>(kl + (jj >> 2) * 4096 + kaddr[jj & 3]));
+        } else {
+          constexpr int q = jj - NK, u = q / C::DT, dt = q % C::DT;
+          const char* v0 = vl + u * C::DT * 1024 + (dt >> 1) * 2048 + (dt & 1) * 512;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(__attribute__((address_space(3))) char*)v0);
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_s16x4*)(__attribute__((address_space(3))) char*)(v0 + 1024));
+          const uint2 l2 = __builtin_bit_cast(uint2, lo);
+          const uint2 h2 = __builtin_bit_cast(uint2, hi);
+          opnd[slot] = as_bf16x8(make_uint4(l2.x, l2.y, h2.x, h2.y));
+        }
+      };
+      static_for<0, LA>(fetch);
+      static_for<0, NJ>([&](auto J) {
+        constexpr int jj = decltype(J)::value, slot = jj % (LA + 1);
+        if constexpr (jj + LA < NJ) fetch(std::integral_constant<int, jj + LA>{});
+        // K(t+2): one block per odd job of the first 16; V(t+2): one block
+        // every fourth job of the second half
+        if constexpr (jj < 2 * NCG && (jj & 1))
+          load_lds16(rk, kdst + (jj >> 1) * 4096, coff_k, 128 * (jj >> 1));
+        if constexpr (jj >= NK && (jj - NK) % 4 == 1 && (jj - NK) / 4 < NCG)
+          co_dma_v(rv, vs2, (jj - NK) / 4);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (jj < NK) {
+          if constexpr (jj == 0)
+            s = mfma32_v_first(opnd[slot], qop[jj]);
+          else
+            mfma32_v_acc(s, opnd[slot], qop[jj]);
+        } else {
+          constexpr int q = jj - NK, u = q / C::DT, dt = q % C::DT;
+          acc[dt] = mfma32(opnd[slot], pop[u], acc[dt]);
+          // softmax of S(t+1) under the O MFMAs (the score chain ended
+          // before the first of them; mfma_settle covers its latency)
+          if constexpr (q == 0) {
+            mfma_settle(s);
+            sc = s;
+          }
+          if constexpr (q < 12) soft(std::integral_constant<int, q>{}, k1, live, pn);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+#pragma unroll
+      for (int u = 0; u < C::NU; ++u) pop[u] = pn[u];
+      pe = pnext;
+      vslot = vslot == C::NBV - 1 ? 0 : vslot + 1;
+      phase_barrier<NCG>();  // K(t+2) and V(t+1) landed; V(t+2)'s loads may still fly
+    }
+    // drain the loads of tiles past the end before the workgroup exits
+    __builtin_amdgcn_s_waitcnt(0x0070);
+  };
+
+  if constexpr (CO) {
+    co_loop();
+  } else if (kend > kstart) {
+    // Every wave executes the same number of barriers: group B one extra
+    // before its first phase, group A one extra after its last.  Tile loads
+    // are issued unconditionally (tiles past the end read zeros), so every
+    // wave issues the same sequence and each wait count below is exact.
     const int t_first = kstart / C::BN, t_last = (kend - 1) / C::BN;
     int pg[2][NR];  // table entries of tile t+3 (slot (t+3-t_first)&1) and t+4
     {
@@ -797,7 +1045,14 @@ hipError_t launch_p1(const PrefillArgs& a, int num_seqs, int max_q, int ps, hipS
 
 hipError_t launch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, int head_dim,
                           int page_size, hipStream_t st) {
-  if (head_dim == 512) {  // the head-dim-split kernel, varlen rows
+  if (head_dim == 512) {
+    // prompts and chunks on the MFMA prefill kernel; one-row sequences (it
+    // skips them) on the head-dim-split kernel, whose group of heads forms
+    // the MFMA columns of one row
+    if (max_seqlen_q > 1) {
+      const hipError_t e = launch_p1<512>(a, num_seqs, max_seqlen_q, page_size, st);
+      if (e != hipSuccess) return e;
+    }
     Attn512Args b = {};
     b.q = a.q;
     b.k_pool = a.k_pool;
@@ -814,9 +1069,10 @@ hipError_t launch_prefill(const PrefillArgs& a, int num_seqs, int max_seqlen_q, 
     b.group = a.group;
     b.window = a.window;
     b.num_splits = 1;
+    b.one_row_only = 1;
     b.total_q = a.total_q;
     b.scale_log2 = a.scale_log2;
-    return launch_attn512(b, num_seqs, max_seqlen_q, page_size, st);
+    return launch_attn512(b, num_seqs, 1, page_size, st);
   }
   switch (head_dim) {
     case 64: return launch_p1<64>(a, num_seqs, max_seqlen_q, page_size, st);

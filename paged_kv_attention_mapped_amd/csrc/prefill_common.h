@@ -49,6 +49,38 @@ __device__ __forceinline__ void load_lds16(i32x4 rs, uint32_t m0, int voff, int 
                   "s"(__builtin_amdgcn_readfirstlane(soff))
                : "memory", "m0");
 }
+
+// S^T = K Q^T with the accumulator in VGPRs.  The compiler gives every MFMA
+// of a kernel the AGPR-accumulator form; at head_dim 512 the O accumulators
+// of 32 rows take all 256 AGPRs, so the score tile is accumulated through
+// these instead.  An MFMA may take the previous one's result as its
+// accumulator input directly (the hardware forwards it); vector
+// instructions may read the result only after mfma_settle, which covers
+// the longest latency of a 32x32 MFMA.
+__device__ __forceinline__ f32x16 mfma32_v_first(bf16x8 a, bf16x8 b) {
+  f32x16 d;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ void mfma32_v_acc(f32x16& d, bf16x8 a, bf16x8 b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_settle(f32x16& d) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d));
+}
+// t *= alpha for an accumulator tile held in AGPRs, element by element in
+// place (written out so that the compiler cannot move copies of the tile
+// into VGPRs out of the rare rescale branch).  The tile's last MFMA must
+// have been issued at least mfma_settle's wait earlier.
+__device__ __forceinline__ void scale_agpr(f32x16& t, float alpha) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float x = t[r], tmp;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(x), "=&v"(tmp) : "v"(alpha));
+    t[r] = x;
+  }
+}
 #pragma clang diagnostic pop
 
 // barrier that first waits for LDS reads and for all but VM of this wave's
