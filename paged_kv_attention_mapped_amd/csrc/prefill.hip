@@ -639,52 +639,99 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
     f32x16 sc;  // the scores, then (from stage 3) their probabilities
     float mx = -INFINITY, alpha = 1.f, mc = 0.f;
     bool any_raise = false;
+    // Stage q of NSOFT, one per O job: a few independent vector operations
+    // per stage, each consuming what an earlier stage produced, so that the
+    // stage issues under its MFMA without waiting on its own results.
+    bool need_mask = false, raise = false;
+    int mlo = 0, mhi = 0;
+    float x0 = 0.f, x1 = 0.f, x2 = 0.f, x3 = 0.f, m_new = 0.f, rarg = 0.f, psum = 0.f;
     auto soft = [&](auto Q, int k0, bool live, bf16x8 (&pn)[C::NU]) {
       constexpr int q = decltype(Q)::value;
+      // register r holds key k0 + 8(r/4) + 4hh + r%4
       if constexpr (q == 0) {
-        const bool need_mask = (k0 + C::BN - 1 > wpmin) ||
-                               (a.window > 0 && wpmax - k0 >= a.window) || (k0 + C::BN > Lk);
+        need_mask = (k0 + C::BN - 1 > wpmin) || (a.window > 0 && wpmax - k0 >= a.window) ||
+                    (k0 + C::BN > Lk);
+        // usable keys of this lane's row: mlo <= key - k0 - 4hh <= mhi
+        mhi = min(mypos, Lk - 1) - k0 - 4 * hh;
+        mlo = (a.window > 0 ? mypos - a.window + 1 : INT_MIN / 2) - k0 - 4 * hh;
+      } else if constexpr (q == 1 || q == 2) {
         if (need_mask) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kp = k0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool ok = kp <= mypos && kp < Lk && (a.window <= 0 || mypos - kp < a.window);
-            sc[r] = ok ? sc[r] : -INFINITY;
+          for (int r = 8 * (q - 1); r < 8 * q; ++r) {
+            const int kr = 8 * (r >> 2) + (r & 3);
+            sc[r] = (kr <= mhi) & (kr >= mlo) ? sc[r] : -INFINITY;
           }
         }
-      } else if constexpr (q == 1) {
-        mx = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+      } else if constexpr (q == 3) {
+        x0 = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+        x1 = fmaxf(fmaxf(sc[3], sc[4]), sc[5]);
+        x2 = fmaxf(fmaxf(sc[6], sc[7]), sc[8]);
+        x3 = fmaxf(fmaxf(sc[9], sc[10]), sc[11]);
+      } else if constexpr (q == 4) {
+        x0 = fmaxf(fmaxf(x0, x1), sc[15]);
+        x1 = fmaxf(fmaxf(sc[12], sc[13]), sc[14]);
+        x2 = fmaxf(x2, x3);
+      } else if constexpr (q == 5) {
+        mx = fmaxf(fmaxf(x0, x1), x2);
+      } else if constexpr (q == 6) {
         mx = half_max(mx);
-      } else if constexpr (q == 2) {
-        const bool raise = live && (mx - m_run) * c > kRescaleSlack;
+      } else if constexpr (q == 7) {
+        raise = live && (mx - m_run) * c > kRescaleSlack;
         any_raise = __builtin_amdgcn_ballot_w64(raise) != 0;
-        const float m_new = raise ? mx : m_run;
-        alpha = raise ? fast_exp2((m_run - m_new) * c) : 1.f;  // 0 from -inf
-        l_run *= alpha;
+      } else if constexpr (q == 8) {
+        m_new = raise ? mx : m_run;
+      } else if constexpr (q == 9) {
+        rarg = (m_run - m_new) * c;
+        mc = (m_new == -INFINITY) ? 0.f : m_new * c;
+      } else if constexpr (q == 10) {
+        alpha = raise ? fast_exp2(rarg) : 1.f;  // 0 from -inf
         m_run = m_new;
-        mc = (m_run == -INFINITY) ? 0.f : m_run * c;
-      } else if constexpr (q >= 3 && q < 11) {
-        constexpr int e = 2 * (q - 3);
-        sc[e] = fast_exp2(fmaf(sc[e], c, -mc));
-        sc[e + 1] = fast_exp2(fmaf(sc[e + 1], c, -mc));
-      } else if constexpr (q == 11) {
-        float psum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) psum += sc[e];
-        if (live) l_run += psum;
-#pragma unroll
-        for (int u = 0; u < C::NU; ++u) {
-          uint4 pp;
-          pp.x = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)sc[8 * u], (__bf16)sc[8 * u + 1]});
-          pp.y = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)sc[8 * u + 2], (__bf16)sc[8 * u + 3]});
-          pp.z = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)sc[8 * u + 4], (__bf16)sc[8 * u + 5]});
-          pp.w = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)sc[8 * u + 6], (__bf16)sc[8 * u + 7]});
-          pn[u] = as_bf16x8(pp);
+        sc[0] = fmaf(sc[0], c, -mc);
+        sc[1] = fmaf(sc[1], c, -mc);
+      } else if constexpr (q >= 11 && q < 19) {
+        // exponentials of pair q-11, arguments of pair q-10
+        constexpr int e = 2 * (q - 11);
+        if constexpr (q == 11) l_run *= alpha;
+        sc[e] = fast_exp2(sc[e]);
+        sc[e + 1] = fast_exp2(sc[e + 1]);
+        if constexpr (e + 2 < 16) {
+          sc[e + 2] = fmaf(sc[e + 2], c, -mc);
+          sc[e + 3] = fmaf(sc[e + 3], c, -mc);
         }
+      } else if constexpr (q == 19) {
+        x0 = sc[0] + sc[1];
+        x1 = sc[2] + sc[3];
+        x2 = sc[4] + sc[5];
+        x3 = sc[6] + sc[7];
+      } else if constexpr (q == 20) {
+        x0 += x1;
+        x2 += x3;
+        x1 = sc[8] + sc[9];
+        x3 = sc[10] + sc[11];
+      } else if constexpr (q == 21) {
+        x0 += x2;
+        x1 += x3;
+        x2 = sc[12] + sc[13];
+        x3 = sc[14] + sc[15];
+      } else if constexpr (q == 22 || q == 23) {
+        constexpr int u = q - 22;
+        uint4 pp;
+        pp.x = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)sc[8 * u], (__bf16)sc[8 * u + 1]});
+        pp.y = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)sc[8 * u + 2], (__bf16)sc[8 * u + 3]});
+        pp.z = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)sc[8 * u + 4], (__bf16)sc[8 * u + 5]});
+        pp.w = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)sc[8 * u + 6], (__bf16)sc[8 * u + 7]});
+        pn[u] = as_bf16x8(pp);
+        if constexpr (q == 22) {
+          x0 += x1;
+          x2 += x3;
+        } else {
+          psum = x0 + x2;
+        }
+      } else if constexpr (q == 24) {
+        if (live) l_run += psum;
       }
     };
+    constexpr int NSOFT = 25;
     auto rescale = [&]() {  // O *= alpha, once the last MFMA on O has settled
       if (!any_raise) return;
       asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -713,7 +760,7 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
       f32x16 st0[C::KT];
       qk_first(st0, t_first);
       sc = st0[0];
-      static_for<0, 12>([&](auto Q) { soft(Q, t_first * C::BN, true, pop); });
+      static_for<0, NSOFT>([&](auto Q) { soft(Q, t_first * C::BN, true, pop); });
       // O is still zero: nothing to rescale
     }
     phase_barrier<63>();  // every wave has read K(t_first) before K(t_first+2) lands there
@@ -763,16 +810,15 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
             s = mfma32_v_first(opnd[slot], qop[jj]);
           else
             mfma32_v_acc(s, opnd[slot], qop[jj]);
-        } else {
-          constexpr int q = jj - NK, u = q / C::DT, dt = q % C::DT;
-          acc[dt] = mfma32(opnd[slot], pop[u], acc[dt]);
-          // softmax of S(t+1) under the O MFMAs (the score chain ended
-          // before the first of them; mfma_settle covers its latency)
-          if constexpr (q == 0) {
+          if constexpr (jj == NK - 1) {  // the score chain's latency, under its last MFMA
             mfma_settle(s);
             sc = s;
           }
-          if constexpr (q < 12) soft(std::integral_constant<int, q>{}, k1, live, pn);
+        } else {
+          constexpr int q = jj - NK, u = q / C::DT, dt = q % C::DT;
+          acc[dt] = mfma32(opnd[slot], pop[u], acc[dt]);
+          // softmax of S(t+1) under the O MFMAs, one stage per job
+          if constexpr (q < NSOFT) soft(std::integral_constant<int, q>{}, k1, live, pn);
         }
         __builtin_amdgcn_sched_barrier(0);
       });
