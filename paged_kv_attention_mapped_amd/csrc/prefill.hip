@@ -400,7 +400,7 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
 
   // Q rows as the B operand of S^T: lane holds q[qrow][16ks + 8hh .. +7].
   bf16x8 qop[C::KS];
-  {
+  if constexpr (D != 512) {  // (head_dim 512 stages Q through LDS: co_loop)
     const bool ok = qrow < Lq;
     const uint16_t* qp =
         a.q + ((int64_t)(q_start + (ok ? qrow : 0)) * a.num_q_heads + head) * D + 8 * hh;
@@ -537,9 +537,10 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
     return sgpr_rsrc(pool + (int64_t)hk * a.head_stride + (ok ? ((int64_t)phys * PS + kb % PS) * D : 0),
                      valid * D * 2);
   };
-  auto co_dma_k = [&](int s, int phys) {  // K blocks (w, cg) of tile s
+  // K blocks (w, cg) of tile s into the 32 KB slot at lds byte `slot`
+  auto co_dma_k = [&](uint32_t slot, int s, int phys) {
     const i32x4 rs = co_rsrc(s, phys, a.k_pool);
-    const uint32_t m0 = lds0 + (s & (C::NB - 1)) * C::TILE + w * 1024;
+    const uint32_t m0 = slot + w * 1024;
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) load_lds16(rs, m0 + cg * 4096, coff_k, 128 * cg);
   };
@@ -627,7 +628,7 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   // the maximum before S(t+1); a rescale that S(t+1) asks for is applied
   // to O at the start of step t+1.  One barrier closes the step: K(t+2) (needed
   // first thing in step t+1) and V(t+1) have landed by then, V(t+2) may
-  // still be in flight.  K ring: slot t%2; V ring: slot t%3.
+  // still be in flight.  K ring: slot (t-t_first)%2; V ring: (t-t_first)%3.
   auto co_loop = [&]() {
     if (kend <= kstart) return;
     constexpr int LA = PKV_PREFILL_LOOKAHEAD, NK = C::KS, NJ = NK + C::NU * C::DT;
@@ -739,31 +740,65 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
       for (int dt = 0; dt < C::DT; ++dt) scale_agpr(acc[dt], alpha);
     };
 
-    // prologue: K and V of tiles t_first and t_first+1 with the Q loads,
-    // then S(t_first) and P(t_first)
-    int vslot = t_first % C::NBV;
+    // Prologue.  Q is staged like a K tile, each wave's 32 rows of its head
+    // in whole lines into its own 32 KB of the rings (the B-operand layout
+    // read back as the K operands are), beside K(t_first) in the fifth slot;
+    // once Q is in registers, the rings take K(t_first+1), V(t_first) and
+    // V(t_first+1) while S(t_first) and P(t_first) are computed.  Ring slots
+    // count from t_first.
+    {
+      const int nvalid = min(32, Lq - r0);
+      const int rstride = a.num_q_heads * D * 2;  // bytes between packed rows
+      const i32x4 rq = sgpr_rsrc(a.q + ((int64_t)(q_start + r0) * a.num_q_heads + head) * D,
+                                 nvalid > 0 ? (nvalid - 1) * rstride + D * 2 : 0);
+      const int i = lane >> 3, x = lane & 7;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int vo = (8 * rg + i) * rstride + 16 * (x ^ i ^ (rg & 1));
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg)
+          load_lds16(rq, lds0 + w * C::TILE + (cg * 4 + rg) * 1024, vo, 128 * cg);
+      }
+    }
+    const uint32_t slot5 = lds0 + (C::NB + 2) * C::TILE;
+    co_dma_k(slot5, t_first, bt1(t_first));
+    phase_barrier<0>();  // Q and K(t_first) in LDS
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      qop[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(
+          (const char*)smem + w * C::TILE + (ks >> 2) * 4096 + kaddr[ks & 3]));
+    phase_barrier<63>();  // every wave holds its Q: the rings are free
+    int vslot = 0;
     int pe = bt1(t_first + 2);
     {
-      const int p0 = bt1(t_first), p1 = bt1(t_first + 1);
-      co_dma_k(t_first, p0);
-      co_dma_k(t_first + 1, p1);
-      const i32x4 r0 = co_rsrc(t_first, p0, a.v_pool), r1 = co_rsrc(t_first + 1, p1, a.v_pool);
-      const int vs1 = vslot == C::NBV - 1 ? 0 : vslot + 1;
+      const int p1 = bt1(t_first + 1);
+      co_dma_k(lds0 + C::TILE, t_first + 1, p1);
+      const i32x4 r0 = co_rsrc(t_first, bt1(t_first), a.v_pool), r1 = co_rsrc(t_first + 1, p1, a.v_pool);
 #pragma unroll
-      for (int q = 0; q < NCG; ++q) co_dma_v(r0, vslot, q);
+      for (int q = 0; q < NCG; ++q) co_dma_v(r0, 0, q);
 #pragma unroll
-      for (int q = 0; q < NCG; ++q) co_dma_v(r1, vs1, q);
+      for (int q = 0; q < NCG; ++q) co_dma_v(r1, 1, q);
     }
-    phase_barrier<0>();
     bf16x8 pop[C::NU];
     {
-      f32x16 st0[C::KT];
-      qk_first(st0, t_first);
-      sc = st0[0];
+      const char* k5 = (const char*)smem + (C::NB + 2) * C::TILE;
+      f32x16 sacc;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4*>(k5 + (ks >> 2) * 4096 + kaddr[ks & 3]));
+        if (ks == 0)
+          sacc = mfma32_v_first(kop, qop[ks]);
+        else
+          mfma32_v_acc(sacc, kop, qop[ks]);
+      }
+      mfma_settle(sacc);
+      sc = sacc;
       static_for<0, NSOFT>([&](auto Q) { soft(Q, t_first * C::BN, true, pop); });
       // O is still zero: nothing to rescale
     }
-    phase_barrier<63>();  // every wave has read K(t_first) before K(t_first+2) lands there
+    // K(t_first+1) and V(t_first) have landed (V(t_first+1) may still fly),
+    // and every wave has read the fifth slot before V(t_first+2) lands there
+    phase_barrier<NCG>();
 
     for (int t = t_first; t <= t_last; ++t) {
       // the rescale the previous step's softmax asked for, before O += V(t) P(t)
@@ -771,9 +806,10 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
       const bool live = t < t_last;
       const int pnext = bt1(t + 3);
       const i32x4 rk = co_rsrc(t + 2, pe, a.k_pool), rv = co_rsrc(t + 2, pe, a.v_pool);
-      const uint32_t kdst = lds0 + (t & 1) * C::TILE + w * 1024;        // K(t+2): slot t%2
-      const int vs2 = vslot == 0 ? C::NBV - 1 : vslot - 1;             // V(t+2): slot (t+2)%3
-      const char* kl = (const char*)smem + ((t + 1) & 1) * C::TILE;
+      const int rt = t - t_first;                                       // ring position
+      const uint32_t kdst = lds0 + (rt & 1) * C::TILE + w * 1024;      // K(t+2)
+      const int vs2 = vslot == 0 ? C::NBV - 1 : vslot - 1;             // V(t+2)
+      const char* kl = (const char*)smem + ((rt + 1) & 1) * C::TILE;   // K(t+1)
       const char* vl = (const char*)smem + (C::NB + vslot) * C::TILE + 8 * lane;
       const int k1 = (t + 1) * C::BN;
       bf16x8 opnd[LA + 1], pn[C::NU];
