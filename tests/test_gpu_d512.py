@@ -3,7 +3,8 @@ the oracle: append bit-exact, decode (the automatic workgroup-level
 stream-K with any workgroup count, explicit splits + combine, one split,
 decode rows through the varlen entry), varlen prefill with
 fresh prompts, chunks after a cached prefix and mixed batches, for groups 1,
-3, 4 and 8, pages 16 and 32, with and without a window."""
+2, 3, 4 and 8, pages 16 and 32, with and without a window; prompts long
+enough for the grouped dense grid of the prefill launch."""
 import numpy as np
 import pytest
 
@@ -21,6 +22,7 @@ SHAPES = [  # name, Hq, Hkv, page, window
     ("g4_p16_win", 8, 2, 16, 300),
     ("g3_p32", 3, 1, 32, 0),
     ("g1_p16", 2, 2, 16, 0),
+    ("g2_p32", 4, 2, 32, 0),
 ]
 
 
@@ -123,3 +125,35 @@ def test_d512_stream_any_partition(P, shape):
         assert np.array_equal(outs[0], outs[1]), "stream-K decode is not deterministic"
         check_close(outs[0], ref, f"d512 {name} stream, {nw} workgroups")
         assert np.all(outs[0][0] == 0)                # the empty row
+
+
+DENSE = [  # name, Hq, Hkv, page, window: four, two and one head per workgroup
+    ("g8_p32", 8, 1, 32, 0),
+    ("g4_p16_win", 8, 2, 16, 300),
+    ("g2_p32", 4, 2, 32, 0),
+    ("g3_p16", 3, 1, 16, 0),
+]
+
+
+@pytest.mark.parametrize("shape", DENSE, ids=[s[0] for s in DENSE])
+def test_d512_prefill_grouped_grid(P, shape):
+    """Prompts of 520-1030 rows and 600-row chunks after a cached prefix: at
+    least 16 query blocks, so the launch takes the grouped dense grid (the
+    shorter cases above walk the compact work list); every row against the
+    oracle, rows of short and long sequences in one launch."""
+    name, hq, hkv, ps, win = shape
+    wl, g, o = build(name, hq, hkv, ps, win, decode_ctx=("fixed", (40,)),
+                     prefill_new=("fixed", (520, 1030, 777)),
+                     chunk=("uniform", 2, 300, 900, 600))
+    qd, qp = wl.queries(0)
+    seqs = wl.prefill_ids()
+    say(f"[d512 grouped grid] {name}: N={len(seqs)} Tq={qp.shape[0]} max_q={int(wl.new_lens[seqs].max())}")
+    assert int(wl.new_lens[seqs].max()) >= 16 * 32
+    out = P.prefill_varlen(dev_bits(qp), g.k, g.v, dev_i32(wl.block_tables[seqs]),
+                           dev_i32(wl.prefill_cu_q()), dev_i32(wl.prefill_cu_k()),
+                           int(wl.new_lens[seqs].max()), int(wl.total_lens[seqs].max()),
+                           page_size=ps, scale=wl.scale, window=win)
+    torch.cuda.synchronize()
+    ref = oracle.prefill_varlen(qp, o.k, o.v, wl.block_tables[seqs], wl.prefill_cu_q(),
+                                wl.prefill_cu_k(), ps, wl.scale, win)
+    check_close(host_bits(out), ref, f"d512 {name} grouped-grid prefill")

@@ -1,4 +1,4 @@
-"""Every row of the two full-size workloads against the oracle.
+"""Every row of the three full-size workloads against the oracle.
 
 * The 256-sequence decode (context U[1024, 8192], 32/8/128, page 32): the
   step's append fused into the decode launch (what the benchmark runs), the
@@ -9,6 +9,8 @@
 * The 16-prompt long prefill (U[1024, 4096] rows each, 32/8/128): every
   sequence's pages bit for bit, and every one of its ~42 000 query rows
   against the oracle's attention over the keys it gathers from its pool.
+* The 8-prompt head_dim-512 prefill (U[1024, 4096], 8/1/512), the same
+  way: the launch the full512_prefill benchmark times (grouped dense grid).
 
 The parity bar (max-abs 2e-2, mean-abs 2e-3) applies to all elements of a
 workload.  Oracle work runs in host threads, one BLAS thread each."""
@@ -125,3 +127,41 @@ def test_long_prefill_every_row(P):
     bad = [j for j, r in enumerate(res) if not r[0]]
     assert not bad, f"pool pages differ from the oracle's for prompts {bad}"
     summarize([r[1] for r in res], "long_prefill every row")
+
+
+
+def test_full512_prefill_every_row(P):
+    wl = W.make("full512_prefill")
+    ps = wl.page_size
+    say(f"[full] full512_prefill: {wl.n_prefill} prompts, {wl.total_q()} rows")
+    g = GpuPools(wl)
+    g.write("prefix", chunk=16)
+    g.write("new", chunk=16)
+    _, qp = wl.queries(0)
+    seqs = wl.prefill_ids()
+    cq, ck = wl.prefill_cu_q(), wl.prefill_cu_k()
+    out = P.prefill_varlen(dev_bits(qp), g.k, g.v, dev_i32(wl.block_tables[seqs]), dev_i32(cq),
+                           dev_i32(ck), int(wl.new_lens[seqs].max()),
+                           int(wl.total_lens[seqs].max()), page_size=ps, scale=wl.scale)
+    torch.cuda.synchronize()
+    got = host_bits(out)
+    _poison_outside(wl, g)
+    hk, hv = host_bits(g.k), host_bits(g.v)
+
+    def check(j):
+        s = int(seqs[j])
+        k, v, bt, phys = compact_oracle_pools(wl, [s])
+        rows = page_rows(phys, ps)
+        same = np.array_equal(hk[:, rows], k) and np.array_equal(hv[:, rows], v)
+        Lq, Lk = int(wl.new_lens[s]), int(wl.total_lens[s])
+        K = oracle.gather(k, bt[0], Lk, ps)
+        V = oracle.gather(v, bt[0], Lk, ps)
+        ref = oracle.attend_rows_matrix(oracle.bf16_to_f64(qp[cq[j]:cq[j + 1]]), K, V,
+                                        np.arange(Lk - Lq, Lk), wl.scale, 0)
+        return same, err_stats(got[cq[j]:cq[j + 1]], ref)
+
+    say("[full] full512_prefill: oracle attention of every row")
+    res = thread_map(check, range(wl.n_prefill))
+    bad = [j for j, r in enumerate(res) if not r[0]]
+    assert not bad, f"pool pages differ from the oracle's for prompts {bad}"
+    summarize([r[1] for r in res], "full512_prefill every row")
