@@ -92,10 +92,9 @@ struct PrefillCfg {
   static constexpr int KS = D / 16;            // k-steps of S^T
   static constexpr int DT = D / 32;            // 32-row tiles of O^T
   // ring depth (tiles) of K (NB) and V (NBV); at head_dim 512 a tile is
-  // 32 KB: two K and three V tiles (160 KB), all waves in one phase (LOCK)
+  // 32 KB: two K and three V tiles (160 KB, the whole LDS)
   static constexpr int NB = D == 512 ? 2 : 4;
   static constexpr int NBV = D == 512 ? 3 : NB;
-  static constexpr bool LOCK = NB == 2;
   static constexpr int TILE = BN * D * 2;      // bytes of one K (or V) tile
   static constexpr int LDS_BYTES = (NB + NBV) * TILE;
   // each wave moves DT 1 KB blocks per tile: K blocks gw*DT .. +DT-1 (one
@@ -449,7 +448,7 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   constexpr int NR = (CO || PS >= 32) ? 1 : 2;   // page runs per wave and tile
   constexpr int NDMA = C::DT * NR;               // LDS-destination loads per wave and tile
   constexpr int VM_AHEAD = 2 * NDMA;             // loads of the two tiles requested after
-  static_assert(CO == C::LOCK && (!CO || C::KT == 1), "whole-line staging layout");
+  static_assert(!CO || C::KT == 1, "whole-line staging layout");
   const uint16_t* src = (grp_b ? a.v_pool : a.k_pool) + (int64_t)hk * a.head_stride;
   const int w0 = CO ? 8 * w : grp_b ? 16 * gw : 32 * ((gw * C::DT) / C::KS);
   const int rr_all = CO ? 8 : grp_b ? 16 : 32;   // rows of this wave
@@ -600,22 +599,14 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   };
   // S^T of key tile t_first (prologue), same block layout
   auto qk_first = [&](f32x16 (&st)[C::KT], int t) {
-    const char* kl = (const char*)smem + (t & (C::NB - 1)) * C::TILE + (CO ? 0 : 16 * lane);
+    const char* kl = (const char*)smem + (t & (C::NB - 1)) * C::TILE + 16 * lane;
 #pragma unroll
     for (int kt = 0; kt < C::KT; ++kt) {
       f32x16 sacc = {};
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const char* ka = CO ? kl + (ks >> 2) * 4096 + kaddr[ks & 3] : kl + (kt * C::KS + ks) * 1024;
-        const bf16x8 kop = as_bf16x8(*reinterpret_cast<const uint4*>(ka));
-        if constexpr (!CO)
-          sacc = mfma32(kop, qop[ks], sacc);
-        else if (ks == 0)
-          sacc = mfma32_v_first(kop, qop[ks]);
-        else
-          mfma32_v_acc(sacc, kop, qop[ks]);
-      }
-      if constexpr (CO) mfma_settle(sacc);
+      for (int ks = 0; ks < C::KS; ++ks)
+        sacc = mfma32(as_bf16x8(*reinterpret_cast<const uint4*>(kl + (kt * C::KS + ks) * 1024)),
+                      qop[ks], sacc);
       st[kt] = sacc;
     }
   };
