@@ -157,3 +157,35 @@ def test_d512_prefill_grouped_grid(P, shape):
     ref = oracle.prefill_varlen(qp, o.k, o.v, wl.block_tables[seqs], wl.prefill_cu_q(),
                                 wl.prefill_cu_k(), ps, wl.scale, win)
     check_close(host_bits(out), ref, f"d512 {name} grouped-grid prefill")
+
+
+def test_d512_prefill_stays_inside_total_q(P):
+    """cu_seq_lens_q running past total_q (a caller error) at head_dim 512:
+    q rows past total_q (NaN) are never read, out rows past it keep their
+    canaries, and the sequences before the bad one match the oracle.  A
+    mixed batch, so both launches (prompts, one-row sequences) see it."""
+    canary = 0x5A5A
+    wl, g, o = build("g8_p32", 8, 1, 32, 0, decode_ctx=("fixed", (40, 500, 77)),
+                     prefill_new=("fixed", (33, 130)), chunk=("uniform", 1, 100, 300, 60))
+    qd, qp = wl.queries(0)
+    q = np.concatenate([qd, qp])
+    cq, ck = wl.cu_lens(wl.new_lens).copy(), wl.cu_lens(wl.total_lens)
+    T = int(cq[-1])
+    bad = cq.copy()
+    bad[-1] += 40                       # the last sequence claims 40 rows past total_q
+    q_full = torch.full((T + 64, wl.num_q_heads, 512), int(W.BF16_NAN), dtype=torch.int16,
+                        device="cuda")
+    q_full[:T] = dev_bits(q)
+    out_full = torch.full((T + 64, wl.num_q_heads, 512), canary, dtype=torch.int16, device="cuda")
+    say(f"[d512 canary] prefill past total_q: T={T}")
+    P.prefill_varlen(q_full[:T], g.k, g.v, dev_i32(wl.block_tables), dev_i32(bad), dev_i32(ck),
+                     int(wl.new_lens.max()) + 40, int(wl.total_lens.max()), page_size=32,
+                     scale=wl.scale, out=out_full[:T])
+    torch.cuda.synchronize()
+    assert torch.all(out_full[T:] == canary)
+    got = host_bits(out_full[:T])
+    assert np.all(np.isfinite(W.bf16_to_f32(got)))
+    n = wl.num_seqs - 1
+    ref = oracle.prefill_varlen(q[:cq[n]], o.k, o.v, wl.block_tables[:n], cq[:n + 1], ck[:n + 1],
+                                32, wl.scale, 0)
+    check_close(got[:cq[n]], ref, "d512 rows before the bad sequence")
