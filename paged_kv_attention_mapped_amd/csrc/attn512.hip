@@ -45,6 +45,10 @@ using prefill_detail::kRescaleSlack;
 using prefill_detail::half_sum;
 using prefill_detail::lds_s16x4;
 using prefill_detail::s16x4;
+using prefill_detail::i32x4;
+using prefill_detail::lds_void;
+using prefill_detail::load_lds16_nt;
+using prefill_detail::sgpr_rsrc;
 
 constexpr int D5 = 512;
 constexpr int kWaves5 = 4;                  // waves per workgroup, 128 dims each
@@ -317,6 +321,290 @@ __device__ __forceinline__ void tile_loop(const Attn512Args& a, int hk, int j, i
 
 }
 
+// ---------------------------------------------------------------------------
+// Key tiles of a decode row in the stream-K kernel.  A decode row fills at
+// most 8 MFMA columns (its query-head group), so the matrix steps here use
+// v_mfma_f32_16x16x32_bf16 (16 columns) instead of the 32-column tiles of
+// tile_loop, which halves the MFMA issue and the softmax work per tile.
+// Lane (q, n) = (lane / 16, lane % 16):
+//   S^T = K Q^T     this wave's 128 dims, two 16-key blocks; A row n of
+//                   block b is key 8(n/4) + 4b + n%4, so score register
+//                   4b + j of lane (q, n) is key 8q + 4b + j of head n: the
+//                   lane holds keys 8q .. 8q+7, the B-operand order of PV;
+//   O^T += V^T P^T  eight 16-dim tiles, V^T read transposed from LDS.
+// K and V go to LDS with LDS-destination buffer loads, without passing
+// through registers: one instruction moves the wave's 256-byte slices of 4
+// key rows into 1 KB of LDS, lane l's 16 bytes at 16 l, and lane l loads
+// chunk (l % 16) ^ swz(row) of its row, which makes the MFMA-order reads of
+// K and the transposed reads of V free of bank conflicts.  Each wave owns
+// two K/V slots (the tile it processes and the next one, whose loads are in
+// flight meanwhile); only the partial scores cross waves.  A page's buffer
+// resource ends at the tile's last allowed key, and an unusable page has an
+// empty one, so those rows arrive as zeros.
+constexpr int kScBytes = 2 * kWaves5 * 2048;                  // [2 tiles][4 waves] partial scores
+constexpr int kKVSlot = 2 * kTile * kSlice * 2;               // a wave's K and V slices of a tile
+constexpr int kLdsStream = kScBytes + kWaves5 * 2 * kKVSlot;  // 144 KB
+
+// staged row r holds, at 16-byte position p, chunk p ^ swz(r) of its slice
+__device__ __forceinline__ int swz_k(int r) { return (r & 3) | ((r >> 1) & 12); }
+__device__ __forceinline__ int swz_v(int r) { return 2 * ((r & 3) | ((r >> 1) & 4)); }
+
+// wait until at most N of this wave's vector memory loads are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x0f70 | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+
+// max / sum over lanes l, l^16, l^32 and l^48 (the four k-groups of a column)
+__device__ __forceinline__ float quad_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return half_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return half_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
+// Folds the tiles of keys [k_lo, k_hi) of the row at position pos (block
+// table row j, KV head hk) into this lane's (acc, m_run, l_run); m_run is
+// in log2 units and l_run this lane's share of the sum (summed over the
+// four k-groups by the caller).  qp points at this lane's query slice (head
+// n of the group, dims 128w + 8q ..), read when col_ok.  Every wave calls
+// it with the same range.
+template <int PS>
+__device__ __forceinline__ void stream_tiles(const Attn512Args& a, int hk, int j, int w, int lane,
+                                             int k_lo, int k_hi, int pos, bool col_ok,
+                                             const uint16_t* qp, unsigned char* smem,
+                                             f32x4 (&acc)[8], float& m_run, float& l_run) {
+  constexpr int NPG = kTile / PS;  // pages per tile
+  constexpr int LPP = 8 / NPG;     // loads per page and tensor
+  const int t0 = k_lo / kTile, t1 = k_hi > k_lo ? (k_hi + kTile - 1) / kTile : t0;
+  if (t0 >= t1) return;
+  const int q = lane >> 4, n = lane & 15;
+  const float c = a.scale_log2;
+  const uint16_t* kh = a.k_pool + (int64_t)hk * a.head_stride + kSlice * w;
+  const uint16_t* vh = a.v_pool + (int64_t)hk * a.head_stride + kSlice * w;
+  const int32_t* bt_row = a.block_tables + (int64_t)j * a.max_pages;
+  const int last_page = (k_hi - 1) / PS;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void*)smem;
+  const int kv0 = kScBytes + w * 2 * kKVSlot;  // this wave's slots (byte offsets in LDS)
+
+  // load i of a tensor: tile row 4i + q, source chunk n ^ swz(row)
+  int vo_k[8], vo_v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * i + q;
+    vo_k[i] = (r % PS) * D5 * 2 + 16 * (n ^ swz_k(r));
+    vo_v[i] = (r % PS) * D5 * 2 + 16 * (n ^ swz_v(r));
+  }
+  // K operand of k-step ks, block b: key 8(n/4) + 4b + n%4 (whose swizzle is
+  // n), chunk 4ks + q
+  int ka[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) ka[ks] = (8 * (n >> 2) + (n & 3)) * 256 + 16 * ((4 * ks + q) ^ n);
+  // transposed V reads: lane (q, n) points at key 8q + 4hh + n/4, dims
+  // 16dt + 4(n%4) .. +3, i.e. 16-byte pair dt ^ s2 of the row
+  const int s2 = (n >> 2) + 4 * (q & 1);
+  int va[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) va[dt] = (8 * q + (n >> 2)) * 256 + 8 * (n & 3) + 32 * (dt ^ s2);
+
+  // Table entries 64 pages at a time, lane l holding page pbase + l: a
+  // scalar load per tile would be waited for by every LDS wait of the tile
+  // (one counter covers both), a full memory round trip per tile.
+  int pbase = t0 * NPG, ent = 0;
+  auto fetch_entries = [&]() {
+    ent = bt_row[min(pbase + lane, last_page)];
+  };
+  auto entries = [&](int t, int (&e)[NPG]) {
+#pragma unroll
+    for (int pg = 0; pg < NPG; ++pg)
+      e[pg] = __builtin_amdgcn_readlane(ent, min(t * NPG + pg, last_page) - pbase);
+  };
+  // makes the pages of tile t readable from ent (a refill drains the loads
+  // in flight: once per 64 pages)
+  auto cover = [&](int t) {
+    if (min(t * NPG + NPG - 1, last_page) - pbase >= 64) {
+      pbase = t * NPG;
+      fetch_entries();
+      wait_vm<0>();
+    }
+  };
+  // keys of tile t inside [k_lo, k_hi) on a usable page
+  auto usable_of = [&](int t, const int (&e)[NPG]) {
+    uint32_t u = 0;
+#pragma unroll
+    for (int pg = 0; pg < NPG; ++pg) {
+      const int kb = t * kTile + pg * PS;
+      const bool ok = e[pg] >= 0 && e[pg] < a.num_pages;
+      const int lo = max(k_lo - kb, 0), hi = min(k_hi - kb, PS);
+      if (ok && hi > lo)
+        u |= (hi - lo >= 32 ? 0xffffffffu : ((1u << (hi - lo)) - 1u)) << (pg * PS + lo);
+    }
+    return u;
+  };
+  // page pg of tile t, cut at k_hi (an unusable page or one past k_hi is empty)
+  auto rsrc = [&](const uint16_t* base, int t, int pg, int e) {
+    const int kb = t * kTile + pg * PS;
+    const bool ok = e >= 0 && e < a.num_pages && kb < k_hi;
+    const int hi = ok ? min(k_hi - kb, PS) : 0;
+    return sgpr_rsrc(base + (ok ? (int64_t)e * PS * D5 : 0), hi * D5 * 2);
+  };
+  auto issue_k = [&](int t, const int (&e)[NPG], int slot) {
+#pragma unroll
+    for (int pg = 0; pg < NPG; ++pg) {
+      const i32x4 rs = rsrc(kh, t, pg, e[pg]);
+#pragma unroll
+      for (int i = pg * LPP; i < (pg + 1) * LPP; ++i) load_lds16_nt(rs, lds0 + slot + i * 1024, vo_k[i], 0);
+    }
+  };
+
+  // Q^T as the B operand: lane (q, n) holds q[head n][128w + 32ks + 8q .. +7];
+  // read with the table entries and waited for here, so that no wait in the
+  // tile loop has to cover these loads
+  fetch_entries();
+  bf16x8 qop[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (col_ok) v = *reinterpret_cast<const uint4*>(qp + 32 * ks);
+    qop[ks] = as_bf16x8(v);
+  }
+  wait_vm<0>();
+
+  int e_cur[NPG], e_nxt[NPG];
+  entries(t0, e_cur);
+  uint32_t use_cur = usable_of(t0, e_cur);
+  issue_k(t0, e_cur, kv0);
+#pragma unroll
+  for (int pg = 0; pg < NPG; ++pg) {
+    const i32x4 rs = rsrc(vh, t0, pg, e_cur[pg]);
+#pragma unroll
+    for (int i = pg * LPP; i < (pg + 1) * LPP; ++i)
+      load_lds16_nt(rs, lds0 + kv0 + kTile * kSlice * 2 + i * 1024, vo_v[i], 0);
+  }
+
+  for (int t = t0; t < t1; ++t) {
+    const int par = (t - t0) & 1;
+    const int cur = kv0 + par * kKVSlot, nxt = kv0 + (par ^ 1) * kKVSlot;
+    // the next tile's K goes to the free slot first (a tile past the range
+    // has empty resources: it moves zeros and reads no memory)
+    cover(t + 1);
+    entries(t + 1, e_nxt);
+    issue_k(t + 1, e_nxt, nxt);
+    const uint32_t use_nxt = usable_of(t + 1, e_nxt);
+    i32x4 rv[NPG];
+#pragma unroll
+    for (int pg = 0; pg < NPG; ++pg) rv[pg] = rsrc(vh, t + 1, pg, e_nxt[pg]);
+    wait_vm<8>();  // this tile's K and V are in LDS
+
+    // partial S^T of this wave's dims (all K operands requested first), the
+    // next tile's V loads in between
+    uint4 kop[8];
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb)
+      kop[jb] = *reinterpret_cast<const uint4*>(smem + cur + ka[jb >> 1] + (jb & 1) * 1024);
+    f32x4 sp[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) sp[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) {
+      sp[jb & 1] = mfma16(as_bf16x8(kop[jb]), qop[jb >> 1], sp[jb & 1]);
+      load_lds16_nt(rv[jb / LPP], lds0 + nxt + kTile * kSlice * 2 + jb * 1024, vo_v[jb], 0);
+    }
+    float* my = reinterpret_cast<float*>(smem) + (par * kWaves5 + w) * 512;
+    *reinterpret_cast<f32x4*>(my + 4 * lane) = sp[0];
+    *reinterpret_cast<f32x4*>(my + 256 + 4 * lane) = sp[1];
+    // LDS writes done, then the barrier; the loads in flight stay in flight
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+
+    // full scores of this lane's column: register r is key 8q + r
+    float x[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) x[r] = 0.f;
+    if (col_ok) {
+#pragma unroll
+      for (int ww = 0; ww < kWaves5; ++ww) {
+        const float* src = reinterpret_cast<const float*>(smem) + (par * kWaves5 + ww) * 512;
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(src + 4 * lane);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 256 + 4 * lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[r] += v0[r];
+          x[4 + r] += v1[r];
+        }
+      }
+    }
+    const int kb = t * kTile;
+    const bool full = use_cur == 0xffffffffu && kb + kTile - 1 <= pos &&
+                      (a.window <= 0 || pos - kb < a.window);
+    float mt = -INFINITY;
+    if (full) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        x[r] *= c;
+        mt = fmaxf(mt, x[r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int kr = 8 * q + r, k = kb + kr;
+        bool ok = col_ok && k <= pos && ((use_cur >> kr) & 1u);
+        if (a.window > 0) ok = ok && pos - k < a.window;
+        x[r] = ok ? x[r] * c : -INFINITY;
+        mt = fmaxf(mt, x[r]);
+      }
+    }
+    mt = quad_max(mt);
+    const bool raise = mt > m_run + kRescaleSlack;
+    float alpha = 1.f;
+    if (raise) {
+      alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - mt);
+      m_run = mt;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      x[r] = fast_exp2(x[r] - m_use);
+      psum += x[r];
+    }
+    l_run = l_run * alpha + psum;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[dt][r] *= alpha;
+    }
+    // P^T as the B operand (p <= 2^slack: the hardware conversion suffices)
+    uint4 pk;
+    pk.x = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)x[0], (__bf16)x[1]});
+    pk.y = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)x[2], (__bf16)x[3]});
+    pk.z = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)x[4], (__bf16)x[5]});
+    pk.w = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)x[6], (__bf16)x[7]});
+    const bf16x8 pop = as_bf16x8(pk);
+    const unsigned char* vs = smem + cur + kTile * kSlice * 2;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      uint2 part[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(__attribute__((address_space(3))) unsigned char*)(vs + va[dt] + hh * 1024));
+        part[hh] = __builtin_bit_cast(uint2, v4);
+      }
+      acc[dt] = mfma16(as_bf16x8(make_uint4(part[0].x, part[0].y, part[1].x, part[1].y)), pop, acc[dt]);
+    }
+    use_cur = use_nxt;
+  }
+  // the loads past the range are done before the slots are reused
+  wait_vm<0>();
+}
+
 template <int PS, bool KLDS>
 __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_kernel(Attn512Args a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem5[];
@@ -442,9 +730,9 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_stream_kernel(StreamA
   const int B = sa.num_seqs, nw = sa.num_waves, wg = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = lane >> 5, col = lane & 31;
+  const int q = lane >> 4, col = lane & 15;
   const int Hkv = d.num_kv_heads, g = d.group;
-  int* pre = reinterpret_cast<int*>(smem5 + kLds5);  // pre[b] = first unit of row b; pre[B] = U
+  int* pre = reinterpret_cast<int*>(smem5 + kLdsStream);  // pre[b] = first unit of row b; pre[B] = U
   // row lengths, read through the scalar cache (never written here)
   const __attribute__((address_space(4))) int32_t* sl =
       (const __attribute__((address_space(4))) int32_t*)d.seq_lens;
@@ -503,7 +791,7 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_stream_kernel(StreamA
   int b = lo;
   int hk = (u0 - uni(pre[lo])) / ((uni(pre[lo + 1]) - uni(pre[lo])) / Hkv);
   const bool col_ok = col < g;
-  const int dbase = kSlice * w + 4 * h;
+  const int dbase = kSlice * w + 4 * q;  // lane (q, col) holds dims 16dt + 4q .. +3 of head col
   for (int u = u0; u < u1;) {
     const int L = max(0, min(sl[b], d.max_pages * PS));
     const int E = (uni(pre[b + 1]) - uni(pre[b])) / Hkv;
@@ -514,41 +802,27 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_stream_kernel(StreamA
     const int k_lo = max(first_key, (tf + (u - s0)) * kTile);
     const int k_hi = min(L, (tf + (ub - s0)) * kTile);
     const int head = hk * g + (col_ok ? col : 0);
-    bf16x8 qop[8];
-    {
-      const uint16_t* qp = d.q + ((int64_t)b * d.num_q_heads + head) * D5 + kSlice * w + 8 * h;
+    const uint16_t* qp = d.q + ((int64_t)b * d.num_q_heads + head) * D5 + kSlice * w + 8 * q;
+    f32x4 acc[8];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (col_ok) v = *reinterpret_cast<const uint4*>(qp + 16 * ks);
-        qop[ks] = as_bf16x8(v);
-      }
-    }
-    f32x16 acc[4];
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+    for (int dt = 0; dt < 8; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
-    // the previous segment's last tiles are done with the LDS score and V
-    // slots, whatever this segment's first tile parity
+    // the previous segment's last tile is done with the LDS score slots,
+    // whatever this segment's first tile parity
     __syncthreads();
-    tile_loop<PS, true>(a, hk, b, w, lane, k_lo, k_hi, L - 1, L - 1, L - 1, col_ok, qop, smem5,
-                        acc, m_run, l_run);
-    const float lt = half_sum(l_run);
+    stream_tiles<PS>(a, hk, b, w, lane, k_lo, k_hi, L - 1, col_ok, qp, smem5, acc, m_run, l_run);
+    const float lt = quad_sum(l_run);
     if (s0 >= u0 && s1 <= u1) {  // the whole segment is here: final rows
       if (col_ok) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
         uint16_t* op = d.out + ((int64_t)b * d.num_q_heads + head) * D5 + dbase;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            uint2 pk;
-            pk.x = pack_bf16x2(acc[dt][4 * rq] * inv, acc[dt][4 * rq + 1] * inv);
-            pk.y = pack_bf16x2(acc[dt][4 * rq + 2] * inv, acc[dt][4 * rq + 3] * inv);
-            *reinterpret_cast<uint2*>(op + 32 * dt + 8 * rq) = pk;
-          }
+        for (int dt = 0; dt < 8; ++dt) {
+          uint2 pk;
+          pk.x = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
+          pk.y = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
+          *reinterpret_cast<uint2*>(op + 16 * dt) = pk;
+        }
       }
     } else {
       // a piece of a cut segment: slot 0 holds the piece at the start of
@@ -558,12 +832,8 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_stream_kernel(StreamA
       if (col_ok) {
         float* pa = p + col * D5 + dbase;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq)
-            *reinterpret_cast<float4*>(pa + 32 * dt + 8 * rq) = make_float4(
-                acc[dt][4 * rq], acc[dt][4 * rq + 1], acc[dt][4 * rq + 2], acc[dt][4 * rq + 3]);
-        if (w == 0 && h == 0) {
+        for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(pa + 16 * dt) = acc[dt];
+        if (w == 0 && q == 0) {
           p[g * D5 + col] = m_run;
           p[g * D5 + g + col] = lt;
         }
@@ -589,11 +859,11 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_stream_kernel(StreamA
 template <int PS>
 hipError_t launch_stream_ps(const StreamArgs& sa, hipStream_t st) {
   static std::atomic<uint64_t> lds_raised{0};
-  constexpr int kMaxLds = kLds5 + (2048 + 1) * 4;  // the scan of up to 2048 rows
+  constexpr int kMaxLds = kLdsStream + (2048 + 1) * 4;  // the scan of up to 2048 rows
   const hipError_t e = raise_lds_limit(
       reinterpret_cast<const void*>(&attn512_stream_kernel<PS>), kMaxLds, lds_raised);
   if (e != hipSuccess) return e;
-  const size_t smem = kLds5 + (size_t)(sa.num_seqs + 1) * sizeof(int);
+  const size_t smem = kLdsStream + (size_t)(sa.num_seqs + 1) * sizeof(int);
   hipLaunchKernelGGL((attn512_stream_kernel<PS>), dim3(sa.num_waves), dim3(kWaves5 * 64), smem, st,
                      sa);
   return hipGetLastError();

@@ -49,6 +49,15 @@ __device__ __forceinline__ void load_lds16(i32x4 rs, uint32_t m0, int voff, int 
                   "s"(__builtin_amdgcn_readfirstlane(soff))
                : "memory", "m0");
 }
+// the same with the streaming policy (nt): data read once
+__device__ __forceinline__ void load_lds16_nt(i32x4 rs, uint32_t m0, int voff, int soff) {
+  const i32x4 r = {__builtin_amdgcn_readfirstlane(rs[0]), __builtin_amdgcn_readfirstlane(rs[1]),
+                   __builtin_amdgcn_readfirstlane(rs[2]), __builtin_amdgcn_readfirstlane(rs[3])};
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(r),
+                  "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory", "m0");
+}
 
 // S^T = K Q^T with the accumulator in VGPRs.  The compiler gives every MFMA
 // of a kernel the AGPR-accumulator form; at head_dim 512 the O accumulators
