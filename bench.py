@@ -548,7 +548,7 @@ def read_ceiling(torch, P, nbytes=4 << 30, reps=5):
     buf.fill_(3)
     cus, _ = P.device_info()
     best = None
-    for per_cu in (4, 8, 16):
+    for per_cu in (1, 2, 4, 8, 16):
         wg = cus * per_cu
         sink = torch.empty(4 * wg, dtype=torch.int32, device="cuda")
         for _ in range(2):
