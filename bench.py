@@ -822,11 +822,10 @@ def main():
                      "attn512_kernel (head-dim split, " +
                      ("split-K partials)" if st.S > 1 else "direct)"))
         if st.fused:
-            kname = ("pkv_decode_append: " +
-                     ("append_last_kernel + " if wl.head_dim == 512 else "") + kname +
+            own = wl.head_dim == 512 and not st.nw  # head_dim 512 splits: append launch first
+            kname = ("pkv_decode_append: " + ("append_last_kernel + " if own else "") + kname +
                      (" + stream_merge_kernel" if st.nw else " + combine_kernel" if st.S > 1 else "") +
-                     (", the step's new rows appended by their own launch first"
-                      if wl.head_dim == 512 else
+                     (", the step's new rows appended by their own launch first" if own else
                       ", the step's new rows appended inside the decode launch"))
         out["roofline"] = {
             "kernel": kname,

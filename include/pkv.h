@@ -354,9 +354,11 @@ pkv_status pkv_decode_noalloc(const uint16_t* q, const uint16_t* k_pool, const u
  * seq_lens places it.  A row with seq_lens[b] == 0 (a padded graph-bucket
  * row) appends nothing and is written as zeros; a row whose table entry for
  * that page is unusable, or whose length exceeds its table, writes nothing
- * to the pool.  At head_dim 512 the rows are appended by a launch of their
- * own before the decode (same result).  num_pages*page_size must stay below
- * 2^31.
+ * to the pool.  At head_dim 512 the stream-K decode has the workgroup that
+ * reads a row's last tile write the new token to the pool before it
+ * requests that tile (no other workgroup reads it); with explicit splits the
+ * rows are appended by a launch of their own before the decode (same
+ * result).  num_pages*page_size must stay below 2^31.
  */
 pkv_status pkv_decode_append(const uint16_t* q, const uint16_t* k_new, const uint16_t* v_new,
                              uint16_t* k_pool, uint16_t* v_pool, const int32_t* block_tables,

@@ -416,9 +416,9 @@ static pkv_status decode_impl(const uint16_t* q, const uint16_t* k_pool, const u
     if (!workspace) return PKV_ERR_NULL_ARG;
     if (workspace_bytes < need) return PKV_ERR_WORKSPACE_TOO_SMALL;
   }
-  // head_dim 512 has no fused decode kernel: the step's rows are appended by
-  // a launch of their own first (same result)
-  if (fused != nullptr && head_dim == 512) {
+  // head_dim 512: the stream-K kernel appends the rows itself; explicit
+  // splits append them by a launch of their own first (same result)
+  if (fused != nullptr && head_dim == 512 && method != PKV_DECODE_STREAM) {
     const pkv_status ast = hip_status(launch_append_last(
         fused->k_new, fused->v_new, block_tables, max_pages_per_seq, seq_lens, num_seqs, page_size,
         num_pages, num_kv_heads, head_dim, fused->k_pool, fused->v_pool, stream));

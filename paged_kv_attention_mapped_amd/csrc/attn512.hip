@@ -372,13 +372,20 @@ __device__ __forceinline__ float quad_sum(float v) {
 // table row j, KV head hk) into this lane's (acc, m_run, l_run); m_run is
 // in log2 units and l_run this lane's share of the sum (summed over the
 // four k-groups by the caller).  qp points at this lane's query slice (head
-// n of the group, dims 128w + 8q ..), read when col_ok.  Every wave calls
-// it with the same range.
+// n of the group, dims 128w + 8q ..), read when col_ok.  When kn is set,
+// key pos is the step's new token: its K/V rows (kn, vn: this KV head's new
+// rows) are written to the pool (kw, vw: this KV head's pools), and into
+// the staged tile that holds the key once that tile has landed in LDS (no
+// other workgroup reads that pool row).  Every wave calls it with the same
+// range.
 template <int PS>
 __device__ __forceinline__ void stream_tiles(const Attn512Args& a, int hk, int j, int w, int lane,
                                              int k_lo, int k_hi, int pos, bool col_ok,
                                              const uint16_t* qp, unsigned char* smem,
-                                             f32x4 (&acc)[8], float& m_run, float& l_run) {
+                                             f32x4 (&acc)[8], float& m_run, float& l_run,
+                                             const uint16_t* kn = nullptr,
+                                             const uint16_t* vn = nullptr, uint16_t* kw = nullptr,
+                                             uint16_t* vw = nullptr) {
   constexpr int NPG = kTile / PS;  // pages per tile
   constexpr int LPP = 8 / NPG;     // loads per page and tensor
   const int t0 = k_lo / kTile, t1 = k_hi > k_lo ? (k_hi + kTile - 1) / kTile : t0;
@@ -473,7 +480,29 @@ __device__ __forceinline__ void stream_tiles(const Attn512Args& a, int hk, int j
     if (col_ok) v = *reinterpret_cast<const uint4*>(qp + 32 * ks);
     qop[ks] = as_bf16x8(v);
   }
+  // the new token: this wave's 256-byte slices of its K and V rows, one
+  // dword per lane, and its page's table entry
+  uint32_t nk = 0, nv = 0;
+  int e_new = -1;
+  if (kn != nullptr) {
+    nk = reinterpret_cast<const uint32_t*>(kn + kSlice * w)[lane];
+    nv = reinterpret_cast<const uint32_t*>(vn + kSlice * w)[lane];
+    e_new = bt_row[pos / PS];
+  }
   wait_vm<0>();
+  // staged position of the new token's dword of this lane: row pos % 32 of
+  // the last tile, chunk lane / 4 at its swizzled position
+  const int r_new = pos % kTile;
+  const int lk_new = r_new * 256 + 16 * ((lane >> 2) ^ swz_k(r_new)) + 4 * (lane & 3);
+  const int lv_new = kTile * kSlice * 2 + r_new * 256 + 16 * ((lane >> 2) ^ swz_v(r_new)) + 4 * (lane & 3);
+  if (kn != nullptr) {
+    e_new = __builtin_amdgcn_readfirstlane(e_new);
+    if (e_new >= 0 && e_new < a.num_pages) {  // an unusable entry takes no write
+      const int64_t off = ((int64_t)e_new * PS + pos % PS) * D5 + kSlice * w;
+      reinterpret_cast<uint32_t*>(kw + off)[lane] = nk;
+      reinterpret_cast<uint32_t*>(vw + off)[lane] = nv;
+    }
+  }
 
   int e_cur[NPG], e_nxt[NPG];
   entries(t0, e_cur);
@@ -500,6 +529,12 @@ __device__ __forceinline__ void stream_tiles(const Attn512Args& a, int hk, int j
 #pragma unroll
     for (int pg = 0; pg < NPG; ++pg) rv[pg] = rsrc(vh, t + 1, pg, e_nxt[pg]);
     wait_vm<8>();  // this tile's K and V are in LDS
+    if (kn != nullptr && t == t1 - 1) {
+      // the new token over the row the tile read from the pool (the pool
+      // write above may not have landed when the tile was requested)
+      *reinterpret_cast<uint32_t*>(smem + cur + lk_new) = nk;
+      *reinterpret_cast<uint32_t*>(smem + cur + lv_new) = nv;
+    }
 
     // partial S^T of this wave's dims (all K operands requested first), the
     // next tile's V loads in between
@@ -810,7 +845,14 @@ __global__ __launch_bounds__(kWaves5 * 64, 1) void attn512_stream_kernel(StreamA
     // the previous segment's last tile is done with the LDS score slots,
     // whatever this segment's first tile parity
     __syncthreads();
-    stream_tiles<PS>(a, hk, b, w, lane, k_lo, k_hi, L - 1, col_ok, qp, smem5, acc, m_run, l_run);
+    // the piece holding the row's last key appends the step's new token
+    // (a row longer than its table appends nothing)
+    const bool app = d.k_new != nullptr && k_hi == L && L >= 1 && sl[b] == L;
+    const int64_t nrow = ((int64_t)b * Hkv + hk) * D5;
+    const int64_t hoff = (int64_t)hk * d.head_stride;
+    stream_tiles<PS>(a, hk, b, w, lane, k_lo, k_hi, L - 1, col_ok, qp, smem5, acc, m_run, l_run,
+                     app ? d.k_new + nrow : nullptr, app ? d.v_new + nrow : nullptr,
+                     d.k_pool_w + hoff, d.v_pool_w + hoff);
     const float lt = quad_sum(l_run);
     if (s0 >= u0 && s1 <= u1) {  // the whole segment is here: final rows
       if (col_ok) {

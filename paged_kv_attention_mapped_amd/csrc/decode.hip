@@ -426,7 +426,8 @@ void decode_stream_kernel(StreamArgs sa) {
   }
 }
 
-// Merge of cut segments: one wave per (merge descriptor, query head).  The
+// Merge of cut segments: one workgroup per merge descriptor, one wave per
+// query head (fewer, larger workgroups: most descriptors are empty).  The
 // pieces are taken in wave order, kMergeBatch at a time with all their loads
 // issued together, and folded into a running (max, sum, accumulator), so the
 // result does not depend on timing and a segment cut into n pieces costs
@@ -451,13 +452,12 @@ __device__ __forceinline__ void load_floats(float* d, const float* p) {
 }
 
 template <int D>
-__global__ __launch_bounds__(64) void stream_merge_kernel(StreamArgs sa) {
+__global__ __launch_bounds__(512) void stream_merge_kernel(StreamArgs sa) {
   constexpr int EPL = D / 64;
   constexpr int MB = kMergeBatch;
-  const int slot = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const int slot = blockIdx.x, h = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const DecodeArgs& a = sa.base;
   const int g = a.group, nw = sa.num_waves;
-  if (h >= g) return;
   // descriptor: [valid, sequence, KV head, last wave, total units]
   const int dv = lane < 5 ? sa.desc[slot * kDescInts + lane] : 0;
   if (__builtin_amdgcn_readfirstlane(dv) == 0) return;
@@ -619,8 +619,9 @@ hipError_t launch_decode_stream(const StreamArgs& sa, int head_dim, int page_siz
 
 template <int D>
 void launch_merge_d(const StreamArgs& sa, hipStream_t st) {
-  hipLaunchKernelGGL((stream_merge_kernel<D>), dim3(2 * sa.num_waves, sa.base.group), dim3(64), 0, st,
-                     sa);
+  // one wave per query head of the (virtual) group, at most 8
+  hipLaunchKernelGGL((stream_merge_kernel<D>), dim3(2 * sa.num_waves), dim3(64 * sa.base.group), 0,
+                     st, sa);
 }
 
 hipError_t launch_stream_merge(const StreamArgs& sa, int head_dim, hipStream_t st) {
