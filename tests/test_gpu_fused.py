@@ -103,11 +103,15 @@ def test_fused_append_decode(P, case):
         assert np.all(got[zero] == 0)
 
 
-def test_fused_padded_rows_and_unusable_entries(P):
+@pytest.mark.parametrize("heads", [(32, 8, 128), (16, 2, 512)], ids=["d128", "d512"])
+def test_fused_padded_rows_and_unusable_entries(P, heads):
     """Rows of length 0 (graph-bucket padding) write nothing and give zeros;
     a row whose last table entry is unusable (-1, or past the pool) writes
-    nothing; results equal the two-launch step's bit for bit."""
-    cfg = W.Config("pad", 20261209, 32, 8, 128, 32,
+    nothing; results equal the two-launch step's bit for bit.  At head_dim
+    512 the stream-K kernel appends (no splits), a launch of its own appends
+    before the direct and split kernels."""
+    hq, hkv, d = heads
+    cfg = W.Config("pad", 20261209, hq, hkv, d, 32,
                    decode_ctx=("fixed", (40, 0, 95, 31, 200, 63, 7, 500)))
     wl = W.build(cfg)
     dec = wl.decode_ids()
@@ -119,7 +123,7 @@ def test_fused_padded_rows_and_unusable_entries(P):
     bt[5, (int(lens[5]) - 1) // wl.page_size] = wl.num_pages  # past the pool
     q, _ = wl.queries(0)
     for splits in (0, 1, 2):
-        say(f"[fused] padded rows and unusable entries, splits={splits}")
+        say(f"[fused] padded rows and unusable entries, head_dim {d}, splits={splits}")
         ga, gb = GpuPools(wl), GpuPools(wl)
         ga.write("prefix")
         gb.write("prefix")
