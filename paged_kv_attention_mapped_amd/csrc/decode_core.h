@@ -95,10 +95,15 @@ struct WaveDecoder {
     }
   }
 
-  // Issue the loads of one step; krow/vrow point at the step's first token row.
-  __device__ __forceinline__ void load(Buf& bf, const uint16_t* krow, const uint16_t* vrow) const {
-    const auto kr = make_rsrc(krow, UT * D * 2);
-    const auto vr = make_rsrc(vrow, UT * D * 2);
+  // Issue the loads of one step; krow/vrow point at the step's first token
+  // row.  A step past the end (live false) issues the same loads through an
+  // empty range: they return zeros and read no memory, so that a loop can
+  // request its next step unconditionally and the compiler's wait before a
+  // step covers that step's loads only, not the next step's.
+  __device__ __forceinline__ void load(Buf& bf, const uint16_t* krow, const uint16_t* vrow,
+                                       bool live = true) const {
+    const auto kr = make_rsrc(krow, live ? UT * D * 2 : 0);
+    const auto vr = make_rsrc(vrow, live ? UT * D * 2 : 0);
 #pragma unroll
     for (int ti = 0; ti < KT; ++ti)
 #pragma unroll

@@ -150,28 +150,31 @@ __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, 
   int tok_of[2] = {0, 0};
   bool ok_of[2] = {false, false};
   auto load = [&](typename W::Buf& bf, int i_step, int slot) {
+    const bool live = i_step < nsteps;  // a step past the end loads nothing
     const int i = i_step / W::UPP, part = i_step - i * W::UPP;
-    if ((i & 63) == 0 && part == 0) {
+    if (live && (i & 63) == 0 && part == 0) {
       phys_lane = (i + lane < npw) ? bt_row[p0 + w + NW * (i + lane)] : -1;
       wait_vm_all();
     }
     int phys = __builtin_amdgcn_readlane(phys_lane, i & 63);
-    ok_of[slot] = phys >= 0 && phys < a.num_pages;
+    ok_of[slot] = live && phys >= 0 && phys < a.num_pages;
     phys = ok_of[slot] ? phys : 0;  // an unusable entry reads page 0 and is masked out
     tok_of[slot] = (p0 + w + NW * i) * PS + part * W::UT;
     const int64_t row = (int64_t)phys * PS + part * W::UT;
-    wd.load(bf, kh + row * D, vh + row * D);
+    wd.load(bf, kh + row * D, vh + row * D, live);
   };
   auto process = [&](const typename W::Buf& bf, int slot) {
     wd.process(bf, tok_of[slot], ok_of[slot] ? first_key : INT_MAX, L, a.scale_log2);
   };
+  // the next step is requested unconditionally (past the end it loads
+  // nothing), so the wait before a step leaves the next one in flight
   typename W::Buf b0, b1;
   if (nsteps > 0) load(b0, 0, 0);
   for (int i = 0; i < nsteps; i += 2) {
-    if (i + 1 < nsteps) load(b1, i + 1, 1);
+    load(b1, i + 1, 1);
     process(b0, 0);
     if (i + 1 >= nsteps) break;
-    if (i + 2 < nsteps) load(b0, i + 2, 0);
+    load(b0, i + 2, 0);
     process(b1, 1);
   }
 
