@@ -56,7 +56,7 @@ DESCRIPTIONS = {
 
 # key splits of the single varlen launch per workload (pkv_prefill_varlen_split);
 # workloads not listed use one (pkv_prefill_varlen)
-PREFILL_SPLITS = {"window_shared": 3}
+PREFILL_SPLITS = {"window_shared": 4}
 
 
 def _log(*a):

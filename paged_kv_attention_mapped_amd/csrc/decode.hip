@@ -47,17 +47,20 @@ constexpr int occ(int o) { return D == 256 ? 1 : o; }
 template <int D, int PS, int G, bool SPLIT>
 __global__ __launch_bounds__(PKV_DECODE_WAVES * 64, occ<D>(PKV_DECODE_OCCUPANCY))
 void decode_kernel(DecodeArgs a) {
-  using W = WaveDecoder<D, PS, G, PKV_DECODE_UNIT>;
+  using W = WaveDecoder<D, PS, G, PKV_DECODE_UNIT, true>;
   constexpr int NW = PKV_DECODE_WAVES;
   __shared__ float sm_m[NW][G];
   __shared__ float sm_l[NW][G];
   __shared__ float sm_acc[NW][G][D];
+  // each wave's K rows pass through LDS into MFMA operand order
+  __shared__ __attribute__((aligned(16))) unsigned char sm_k[NW][W::UT * D * 2];
 
   const int s = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = a.group;
   W wd;
   wd.init(lane);
+  wd.set_kstage(sm_k[w]);
   wd.reset();
   wd.load_q(a.q + ((int64_t)b * a.num_q_heads + hk * g) * D, g);
 

@@ -113,7 +113,7 @@ struct PrefillCfg {
 template <int D, int PS, int HW, int NW>
 __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, int head0,
                                            int q_row, int L, int split, float* sm,
-                                           bool mark) {
+                                           bool mark, unsigned char* kstage) {
   // with key splits the row's pages are cut into S runs (split_count); split
   // s takes run s and writes its partial (max in log2 units, sum,
   // unnormalised accumulator) for the merge, and a row that is not cut
@@ -123,7 +123,7 @@ __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, 
   const int S = split_count(pr.y - pr.x, a.nsplit, min_split_pages(NW));
   if (split >= S) return;
   if (mark && split == 0 && threadIdx.x == 0 && a.nsplit > 1) a.part_S[q_row] = S;
-  using W = WaveDecoder<D, PS, G, 16>;
+  using W = WaveDecoder<D, PS, G, 16, true>;
   float* sm_m = sm;                 // [NW][G]
   float* sm_l = sm + NW * G;        // [NW][G]
   float* sm_acc = sm + 2 * NW * G;  // [NW][G][D]
@@ -131,6 +131,7 @@ __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   W wd;
   wd.init(lane);
+  wd.set_kstage(kstage + w * W::UT * D * 2);  // K rows go to operand order through LDS
   wd.reset();
   wd.load_q(a.q + ((int64_t)q_row * a.num_q_heads + head0) * D, HW);
 
@@ -364,7 +365,8 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
     if constexpr (kOneRow) {
       if (Lq == 1 && b == 0)
         decode_row<D, PS, HW, C::NW>(a, j, hk, hk * a.group + hg * HW, q_start, Lk, split,
-                                     reinterpret_cast<float*>(smem), bx == 0);
+                                     reinterpret_cast<float*>(smem), bx == 0,
+                                     reinterpret_cast<unsigned char*>(smem) + C::LDS_BYTES / 2);
     }
     return;
   }
