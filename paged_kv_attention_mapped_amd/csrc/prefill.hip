@@ -985,38 +985,64 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   }
 
   // ---- normalise and write: lane holds d = 32dt + 8(r/4) + 4hh + r%4 ----
+  // The rows go out through LDS: each wave stages its 32 rows x D (16-byte
+  // chunks XOR-swizzled by row, so the column-order writes spread over the
+  // banks) and stores whole consecutive chunks of a row per lane group, in
+  // place of 8- or 16-byte pieces of 32 different rows per instruction.
   const float lt = half_sum(l_run);
-  if (S > 1) {
+  // every wave is past its last read of the K/V rings
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  const int rows = min(32, Lq - r0);  // this wave's rows that exist
+  // (key runs are not offered at head_dim 512, whose fp32 rows would not
+  // fit the staging area)
+  if (D <= 256 && S > 1) {
     // the split's partial (max in log2 units, sum, unnormalised accumulator),
     // merged by split_merge_kernel
-    if (qrow < Lq) {
-      const int64_t cell = ((int64_t)(q_start + qrow) * a.num_q_heads + head) * a.nsplit + split;
-      float* pa = a.part_acc + cell * D + 4 * hh;
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-          *reinterpret_cast<float4*>(pa + 32 * dt + 8 * rb) =
-              make_float4(acc[dt][4 * rb], acc[dt][4 * rb + 1], acc[dt][4 * rb + 2], acc[dt][4 * rb + 3]);
-      if (hh == 0) {
-        a.part_m[cell] = m_run == -INFINITY ? -INFINITY : m_run * c;
-        a.part_l[cell] = lt;
-      }
-    }
-    return;
-  }
-  if (qrow < Lq) {
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    uint16_t* op = a.out + ((int64_t)(q_start + qrow) * a.num_q_heads + head) * D + 4 * hh;
+    constexpr int CPR = D / 4;                      // 16-byte chunks per fp32 row
+    constexpr int SW = CPR < 16 ? CPR - 1 : 15;
+    unsigned char* stg = reinterpret_cast<unsigned char*>(smem) + w * 32 * D * 4;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        uint2 pk;
-        pk.x = pack_bf16x2(acc[dt][4 * rb] * inv, acc[dt][4 * rb + 1] * inv);
-        pk.y = pack_bf16x2(acc[dt][4 * rb + 2] * inv, acc[dt][4 * rb + 3] * inv);
-        *reinterpret_cast<uint2*>(op + 32 * dt + 8 * rb) = pk;
+      for (int rb = 0; rb < 4; ++rb)
+        *reinterpret_cast<float4*>(stg + col * D * 4 + 16 * ((8 * dt + 2 * rb + hh) ^ (col & SW))) =
+            make_float4(acc[dt][4 * rb], acc[dt][4 * rb + 1], acc[dt][4 * rb + 2], acc[dt][4 * rb + 3]);
+#pragma unroll
+    for (int i = 0; i < 32 * CPR / 64; ++i) {
+      const int cr = (64 * i + lane) / CPR, k = (64 * i + lane) % CPR;
+      const float4 v = *reinterpret_cast<const float4*>(stg + cr * D * 4 + 16 * (k ^ (cr & SW)));
+      if (cr < rows) {
+        const int64_t cell = ((int64_t)(q_start + r0 + cr) * a.num_q_heads + head) * a.nsplit + split;
+        *reinterpret_cast<float4*>(a.part_acc + cell * D + 4 * k) = v;
       }
+    }
+    if (qrow < Lq && hh == 0) {
+      const int64_t cell = ((int64_t)(q_start + qrow) * a.num_q_heads + head) * a.nsplit + split;
+      a.part_m[cell] = m_run == -INFINITY ? -INFINITY : m_run * c;
+      a.part_l[cell] = lt;
+    }
+    return;
+  }
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  constexpr int CPR = D / 8;                        // 16-byte chunks per bf16 row
+  constexpr int SW = CPR < 16 ? CPR - 1 : 15;
+  unsigned char* stg = reinterpret_cast<unsigned char*>(smem) + w * 32 * D * 2;
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      uint2 pk;
+      pk.x = pack_bf16x2(acc[dt][4 * rb] * inv, acc[dt][4 * rb + 1] * inv);
+      pk.y = pack_bf16x2(acc[dt][4 * rb + 2] * inv, acc[dt][4 * rb + 3] * inv);
+      *reinterpret_cast<uint2*>(stg + col * D * 2 + 16 * ((4 * dt + rb) ^ (col & SW)) + 8 * hh) = pk;
+    }
+#pragma unroll
+  for (int i = 0; i < 32 * CPR / 64; ++i) {
+    const int cr = (64 * i + lane) / CPR, k = (64 * i + lane) % CPR;
+    const uint4 v = *reinterpret_cast<const uint4*>(stg + cr * D * 2 + 16 * (k ^ (cr & SW)));
+    if (cr < rows)
+      *reinterpret_cast<uint4*>(a.out + ((int64_t)(q_start + r0 + cr) * a.num_q_heads + head) * D + 8 * k) = v;
   }
 }
 
