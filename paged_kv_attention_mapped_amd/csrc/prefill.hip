@@ -103,14 +103,172 @@ struct PrefillCfg {
   static_assert(QB >= 1, "more heads than waves");
 };
 
+// The wave decoder of a one-row sequence.  A step is 16 tokens of a page:
+//   S = K Q^T     v_mfma_f32_16x16x32_bf16 with K rows as A (read back from
+//                 LDS in operand order, row n of the tile being token
+//                 4(n%4) + n/4, so that score register r of lane row jj is
+//                 token 4r + jj) and the NH heads as columns;
+//   softmax       one running max and sum per head, the max taken over the
+//                 four lane rows (two exchanges per step);
+//   O^T += V^T P  v_mfma_f32_16x16x16_bf16 per 16 dims: lane (jj, n) holds
+//                 the probabilities of tokens jj, 4+jj, 8+jj, 12+jj for head
+//                 n, which is the B operand when k = 4jj + r stands for
+//                 token 4r + jj; V is staged row-major with token 4r + jj at
+//                 row 4jj + r, so one transposed read (ds_read_b64_tr_b16)
+//                 per 16 dims yields the matching A operand.
+// K and V arrive with whole-line loads (RPI rows per instruction) and go
+// through a per-wave LDS area, 16-byte chunks XOR-swizzled by row.  The
+// matrix cores take the PV products that would otherwise cost NH fused
+// multiply-adds per token and dim on the vector ALUs.
+template <int D, int PS, int NH>
+struct RowDecoder {
+  static constexpr int UT = 16;               // tokens per step
+  static constexpr int UPP = PS / UT;         // steps per page
+  static constexpr int KB = D / 32;           // k-steps of S
+  static constexpr int DB = D / 16;           // 16-dim blocks of O^T
+  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;        // rows per load instruction
+  static constexpr int NL = UT / RPI;         // load instructions per tensor per step
+  static constexpr int SWZ = CPR < 16 ? CPR - 1 : 15;
+  static constexpr int STAGE = 2 * UT * D * 2;  // LDS bytes per wave (K rows, V rows)
+  static_assert(NH <= 16 && PS % UT == 0 && UT % RPI == 0, "decoder shape");
+  struct Buf {
+    uint4 k[NL];
+    uint4 v[NL];
+  };
+
+  int jj, n, tok_a;
+  unsigned char* kst;
+  unsigned char* vst;
+  float m_run, l_run;
+  f32x4 oacc[DB];  // O^T: dims 16b + 4jj + r of head n
+  bf16x8 qop[KB];
+
+  __device__ __forceinline__ void init(int lane, unsigned char* stage) {
+    jj = lane >> 4;
+    n = lane & 15;
+    tok_a = 4 * (n & 3) + (n >> 2);
+    kst = stage;
+    vst = stage + UT * D * 2;
+    m_run = -INFINITY;
+    l_run = 0.f;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) oacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Q^T as the B operand of S: lane (jj, n) holds q[head n][32kb + 8jj ..
+  // +7]; columns n >= NH are zero.
+  __device__ __forceinline__ void load_q(const uint16_t* qg) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (n < NH) v = *reinterpret_cast<const uint4*>(qg + n * D + 32 * kb + 8 * jj);
+      qop[kb] = as_bf16x8(v);
+    }
+  }
+
+  // The loads of one step (krow / vrow: its first token row).  With live
+  // false they go through an empty range: zeros, no memory read.
+  __device__ __forceinline__ void load(Buf& bf, const uint16_t* krow, const uint16_t* vrow,
+                                       bool live) const {
+    const auto kr = make_rsrc(krow, live ? UT * D * 2 : 0);
+    const auto vr = make_rsrc(vrow, live ? UT * D * 2 : 0);
+    const int lane = 16 * jj + n;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int off = 2 * ((RPI * i + lane / CPR) * D + 8 * (lane % CPR));
+      bf.k[i] = buffer_load16(kr, off);
+      bf.v[i] = buffer_load16(vr, off);
+    }
+  }
+
+  // Fold one step (tokens tok0 .. tok0+15; those outside [lo, hi) masked).
+  __device__ __forceinline__ void process(const Buf& bf, int tok0, int lo, int hi,
+                                          float scale_log2) {
+    const int lane = 16 * jj + n, c = lane % CPR;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int r = RPI * i + lane / CPR;
+      *reinterpret_cast<uint4*>(kst + r * (2 * D) + 16 * (c ^ (r & SWZ))) = bf.k[i];
+      const int pr = 4 * (r & 3) + (r >> 2);
+      *reinterpret_cast<uint4*>(vst + pr * (2 * D) + 16 * (c ^ (pr & SWZ))) = bf.v[i];
+    }
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const uint4 kop =
+          *reinterpret_cast<const uint4*>(kst + tok_a * (2 * D) + 16 * ((4 * kb + jj) ^ (tok_a & SWZ)));
+      sc = mfma16(as_bf16x8(kop), qop[kb], sc);
+    }
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = sc[r] * scale_log2;
+    const bool partial = (tok0 < lo) || (tok0 + UT > hi);
+    uint32_t keep = 0xfu;
+    if (partial) {
+      keep = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = tok0 + 4 * r + jj;
+        const bool ok = t >= lo && t < hi;
+        keep |= (ok ? 1u : 0u) << r;
+        x[r] = ok ? x[r] : -INFINITY;
+      }
+    }
+    float pmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    pmax = fmaxf(pmax, __shfl_xor(pmax, 16));
+    pmax = fmaxf(pmax, __shfl_xor(pmax, 32));
+    const float m_new = fmaxf(m_run, pmax);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      x[r] = fast_exp2(x[r] - m_use);
+      psum += x[r];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    // p in [0, 1]: the hardware round-to-nearest conversion suffices
+    const bf16x2 p01 = {(__bf16)x[0], (__bf16)x[1]};
+    const bf16x2 p23 = {(__bf16)x[2], (__bf16)x[3]};
+    const s16x4 pop = __builtin_bit_cast(s16x4, make_uint2(__builtin_bit_cast(uint32_t, p01),
+                                                            __builtin_bit_cast(uint32_t, p23)));
+    // transposed reads: source lane n of lane row jj points at row
+    // 4jj + n/4, dims 16b + 4(n%4); lane n receives rows 4jj .. 4jj+3
+    // (tokens jj, 4+jj, 8+jj, 12+jj) of dim 16b + n
+    const int prow = 4 * jj + (n >> 2), a4 = n & 3;
+    unsigned char* vrow = vst + prow * (2 * D) + 8 * (a4 & 1);
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4*)(__attribute__((address_space(3))) unsigned char*)(
+              vrow + 16 * ((2 * b + (a4 >> 1)) ^ (prow & SWZ))));
+      if (partial) {  // masked tokens' V rows may hold anything (NaN)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v4[r] = ((keep >> r) & 1u) ? v4[r] : (short)0;
+      }
+      oacc[b] *= alpha;
+      oacc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v4, pop, oacc[b], 0, 0, 0);
+    }
+  }
+
+  // The step state after the last step: M (log2 units) and the sum of head
+  // n, the same in every lane row.
+  __device__ __forceinline__ void finish(float& M, float& lsum) const {
+    M = m_run;
+    lsum = l_run + __shfl_xor(l_run, 16);
+    lsum += __shfl_xor(lsum, 32);
+  }
+};
+
 // A sequence with a single query row (a decode row packed into the varlen
 // batch, or a one-token prompt): the workgroup's NW waves take the allowed
-// pages round-robin with the decode machinery of decode_core.h (K on MFMA
-// as the A operand, the HW heads as columns, PV on the vector ALUs) and
-// merge their softmax states through LDS, instead of running 32-row MFMA
-// tiles for one row.  A mixed batch of decode rows and prompts is thereby
-// one launch.
-template <int D, int PS, int HW, int NW>
+// pages round-robin with RowDecoder (NH heads of one KV head) and merge
+// their softmax states through LDS, instead of running 32-row MFMA tiles
+// for one row.  A mixed batch of decode rows and prompts is thereby one
+// launch.
+template <int D, int PS, int NH, int NW>
 __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, int head0,
                                            int q_row, int L, int split, float* sm,
                                            bool mark, unsigned char* kstage) {
@@ -118,23 +276,20 @@ __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, 
   // s takes run s and writes its partial (max in log2 units, sum,
   // unnormalised accumulator) for the merge, and a row that is not cut
   // (S = 1) is written whole by split 0
-  constexpr int G = HW < 2 ? 2 : HW;
+  constexpr int G = NH;
   const int2 pr = row_pages(L, a.window, PS);
   const int S = split_count(pr.y - pr.x, a.nsplit, min_split_pages(NW));
   if (split >= S) return;
   if (mark && split == 0 && threadIdx.x == 0 && a.nsplit > 1) a.part_S[q_row] = S;
-  using W = WaveDecoder<D, PS, G, 16, true>;
+  using W = RowDecoder<D, PS, NH>;
   float* sm_m = sm;                 // [NW][G]
   float* sm_l = sm + NW * G;        // [NW][G]
   float* sm_acc = sm + 2 * NW * G;  // [NW][G][D]
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   W wd;
-  wd.init(lane);
-  wd.set_kstage(kstage + w * W::UT * D * 2);  // K rows go to operand order through LDS
-  wd.reset();
-  wd.load_q(a.q + ((int64_t)q_row * a.num_q_heads + head0) * D, HW);
-
+  wd.init(lane, kstage + w * W::STAGE);
+  wd.load_q(a.q + ((int64_t)q_row * a.num_q_heads + head0) * D);
   const int first_key = a.window > 0 ? max(0, L - a.window) : 0;
   int p0 = pr.x, pend = pr.y;
   if (S > 1) {
@@ -180,19 +335,18 @@ __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, 
   }
 
   float M, lw;
-  wd.merge_rows(M, lw);
-  if (wd.jj == 0) {
-    if (wd.n < G) {
+  wd.finish(M, lw);
+  if (wd.n < G) {
+    if (wd.jj == 0) {
       sm_m[w * G + wd.n] = M;
       sm_l[w * G + wd.n] = lw;
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < W::EPL; ++e) sm_acc[(w * G + h) * D + wd.dim_of(e)] = wd.acc[h][e];
+    for (int b = 0; b < W::DB; ++b)
+      *reinterpret_cast<f32x4*>(sm_acc + (w * G + wd.n) * D + 16 * b + 4 * wd.jj) = wd.oacc[b];
   }
   __syncthreads();
-  for (int idx = tid; idx < HW * D; idx += 64 * NW) {
+  for (int idx = tid; idx < NH * D; idx += 64 * NW) {
     const int h = idx / D, d = idx - h * D;
     float Mx = -INFINITY;
 #pragma unroll
@@ -255,13 +409,14 @@ __device__ __forceinline__ int seq_splits(const PrefillArgs& a, const SeqGeo& g)
 // Compact work list: the launch's work items are, sequence by sequence, its
 // query blocks from the last (longest) to the first, each cut into S runs,
 // each run for every (KV head, head group) -- X0 items per run; a one-row
-// sequence has one block.  Workgroup `item` scans the sequences' item
+// sequence has one block and X1 items per run (X1 = the KV heads when one
+// workgroup takes a KV head's whole group of heads).  Workgroup `item` scans the sequences' item
 // counts, NT at a time with a workgroup prefix sum, and finds its
 // sequence j and its index k among j's items; false past the end of the
 // list.  Without ONE_ROW one-row sequences have no items (another launch
 // takes them).  lds: NT/64 + 2 ints.
 template <int NT, int BM, int BN, int PS, int NW, bool ONE_ROW>
-__device__ bool find_item(const PrefillArgs& a, int num_seqs, int X0, int item, int* lds,
+__device__ bool find_item(const PrefillArgs& a, int num_seqs, int X0, int X1, int item, int* lds,
                           int& j, int& k) {
   constexpr int NWV = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -273,7 +428,7 @@ __device__ bool find_item(const PrefillArgs& a, int num_seqs, int X0, int item, 
     if (t < num_seqs) {
       const SeqGeo g = seq_geo<PS>(a, t);
       if (g.Lq > (ONE_ROW ? 0 : 1))
-        cnt = (g.Lq == 1 ? 1 : (g.Lq + BM - 1) / BM) * seq_splits<BM, BN, PS, NW>(a, g) * X0;
+        cnt = (g.Lq == 1 ? X1 : (g.Lq + BM - 1) / BM * X0) * seq_splits<BM, BN, PS, NW>(a, g);
     }
     int v = cnt;  // inclusive prefix within the wave
 #pragma unroll
@@ -319,18 +474,28 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
 
   const int HG = a.group / HW;       // workgroups per KV head along the heads
   const int X0 = a.num_kv_heads * HG;
+  // at head_dim 256 (four waves, HW = 4) a group of 8 heads takes two
+  // workgroups per prompt block; a one-row sequence then runs its whole group
+  // in one workgroup (the 8 heads are 8 of the decoder's 16 MFMA columns),
+  // so its pages are read once, not once per head group
+  constexpr bool kPairRow = kOneRow && D == 256 && 2 * HW <= 8;
+  const bool pair_row = kPairRow && HG == 2;
   int bx, j, b, split;               // (KV head, head group), sequence, block from the end, run
   if (zg == 0) {
     // compact work list (few query blocks per sequence): the workgroups
     // that find nothing are all at the end of the dispatch order
     int k;
     if (!find_item<C::NT, C::BM, C::BN, PS, C::NW, kOneRow>(
-            a, num_seqs, X0, (int)blockIdx.x,
+            a, num_seqs, X0, pair_row ? a.num_kv_heads : X0, (int)blockIdx.x,
             reinterpret_cast<int*>(reinterpret_cast<char*>(smem) + C::LDS_BYTES - 256), j, k))
       return;
-    const int Sj = seq_splits<C::BM, C::BN, PS, C::NW>(a, seq_geo<PS>(a, j));
-    bx = k % X0;
-    k /= X0;
+    const SeqGeo gj = seq_geo<PS>(a, j);
+    const int Sj = seq_splits<C::BM, C::BN, PS, C::NW>(a, gj);
+    const bool pr1 = pair_row && gj.Lq == 1;
+    const int Xj = pr1 ? a.num_kv_heads : X0;
+    bx = k % Xj;
+    if (pr1) bx *= HG;  // head group 0 of KV head bx
+    k /= Xj;
     split = k % Sj;
     b = k / Sj;
   } else {
@@ -363,10 +528,20 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   const int q_start = geo.q_start, Lq = geo.Lq, Lk = geo.Lk;
   if (Lq <= 1) {
     if constexpr (kOneRow) {
-      if (Lq == 1 && b == 0)
-        decode_row<D, PS, HW, C::NW>(a, j, hk, hk * a.group + hg * HW, q_start, Lk, split,
-                                     reinterpret_cast<float*>(smem), bx == 0,
-                                     reinterpret_cast<unsigned char*>(smem) + C::LDS_BYTES / 2);
+      if (Lq == 1 && b == 0) {
+        float* sm = reinterpret_cast<float*>(smem);
+        unsigned char* ks = reinterpret_cast<unsigned char*>(smem) + C::LDS_BYTES / 2;
+        if constexpr (kPairRow) {
+          if (pair_row) {  // head group 0 takes both; the other one has nothing
+            if (hg == 0)
+              decode_row<D, PS, 2 * HW, C::NW>(a, j, hk, hk * a.group, q_start, Lk, split, sm,
+                                               bx == 0, ks);
+            return;
+          }
+        }
+        decode_row<D, PS, HW, C::NW>(a, j, hk, hk * a.group + hg * HW, q_start, Lk, split, sm,
+                                     bx == 0, ks);
+      }
     }
     return;
   }

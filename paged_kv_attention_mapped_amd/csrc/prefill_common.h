@@ -128,10 +128,10 @@ __device__ __forceinline__ int2 row_pages(int L, int window, int ps) {
   const int first = window > 0 ? max(0, L - window) : 0;
   return make_int2(first / ps, (L + ps - 1) / ps);
 }
-// minimum units per run: 128 keys of a prefill block, four pages per wave
+// minimum units per run: 128 keys of a prefill block, two pages per wave
 // of a one-row sequence
 __device__ __forceinline__ int min_split_tiles(int bn) { return bn >= 128 ? 1 : 128 / bn; }
-__device__ __forceinline__ int min_split_pages(int nw) { return 4 * nw; }
+__device__ __forceinline__ int min_split_pages(int nw) { return 2 * nw; }
 
 }  // namespace prefill_detail
 }  // namespace pkv
