@@ -410,14 +410,15 @@ __device__ __forceinline__ int seq_splits(const PrefillArgs& a, const SeqGeo& g)
 // query blocks from the last (longest) to the first, each cut into S runs,
 // each run for every (KV head, head group) -- X0 items per run; a one-row
 // sequence has one block and X1 items per run (X1 = the KV heads when one
-// workgroup takes a KV head's whole group of heads).  Workgroup `item` scans the sequences' item
-// counts, NT at a time with a workgroup prefix sum, and finds its
-// sequence j and its index k among j's items; false past the end of the
-// list.  Without ONE_ROW one-row sequences have no items (another launch
-// takes them).  lds: NT/64 + 2 ints.
+// workgroup takes a KV head's whole group of heads).  Workgroup `item`
+// scans the sequences' item counts, NT at a time with a workgroup prefix
+// sum, and finds its sequence j, j's geometry and its index k among j's
+// items; false past the end of the list.  Without ONE_ROW one-row
+// sequences have no items (another launch takes them).  lds: NT/64 + 5
+// ints.
 template <int NT, int BM, int BN, int PS, int NW, bool ONE_ROW>
 __device__ bool find_item(const PrefillArgs& a, int num_seqs, int X0, int X1, int item, int* lds,
-                          int& j, int& k) {
+                          int& j, int& k, SeqGeo& geo) {
   constexpr int NWV = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   if (tid == 0) lds[NWV] = -1;
@@ -425,8 +426,9 @@ __device__ bool find_item(const PrefillArgs& a, int num_seqs, int X0, int X1, in
   for (int c0 = 0; c0 < num_seqs; c0 += NT) {
     const int t = c0 + tid;
     int cnt = 0;
+    SeqGeo g = {0, 0, 0};
     if (t < num_seqs) {
-      const SeqGeo g = seq_geo<PS>(a, t);
+      g = seq_geo<PS>(a, t);
       if (g.Lq > (ONE_ROW ? 0 : 1))
         cnt = (g.Lq == 1 ? X1 : (g.Lq + BM - 1) / BM * X0) * seq_splits<BM, BN, PS, NW>(a, g);
     }
@@ -449,11 +451,17 @@ __device__ bool find_item(const PrefillArgs& a, int num_seqs, int X0, int X1, in
     if (cnt > 0 && item >= lo && item < hi) {
       lds[NWV] = t;
       lds[NWV + 1] = item - lo;
+      lds[NWV + 2] = g.q_start;
+      lds[NWV + 3] = g.Lq;
+      lds[NWV + 4] = g.Lk;
     }
     __syncthreads();
     if (lds[NWV] >= 0) {
       j = lds[NWV];
       k = lds[NWV + 1];
+      geo = SeqGeo{__builtin_amdgcn_readfirstlane(lds[NWV + 2]),
+                   __builtin_amdgcn_readfirstlane(lds[NWV + 3]),
+                   __builtin_amdgcn_readfirstlane(lds[NWV + 4])};
       return true;
     }
     base += tot;
@@ -481,17 +489,17 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   constexpr bool kPairRow = kOneRow && D == 256 && 2 * HW <= 8;
   const bool pair_row = kPairRow && HG == 2;
   int bx, j, b, split;               // (KV head, head group), sequence, block from the end, run
+  SeqGeo geo;                        // sequence j's rows and keys
   if (zg == 0) {
     // compact work list (few query blocks per sequence): the workgroups
     // that find nothing are all at the end of the dispatch order
     int k;
     if (!find_item<C::NT, C::BM, C::BN, PS, C::NW, kOneRow>(
             a, num_seqs, X0, pair_row ? a.num_kv_heads : X0, (int)blockIdx.x,
-            reinterpret_cast<int*>(reinterpret_cast<char*>(smem) + C::LDS_BYTES - 256), j, k))
+            reinterpret_cast<int*>(reinterpret_cast<char*>(smem) + C::LDS_BYTES - 256), j, k, geo))
       return;
-    const SeqGeo gj = seq_geo<PS>(a, j);
-    const int Sj = seq_splits<C::BM, C::BN, PS, C::NW>(a, gj);
-    const bool pr1 = pair_row && gj.Lq == 1;
+    const int Sj = seq_splits<C::BM, C::BN, PS, C::NW>(a, geo);
+    const bool pr1 = pair_row && geo.Lq == 1;
     const int Xj = pr1 ? a.num_kv_heads : X0;
     bx = k % Xj;
     if (pr1) bx *= HG;  // head group 0 of KV head bx
@@ -524,7 +532,7 @@ __global__ __launch_bounds__((PrefillCfg<D, HW>::NT), 1) void prefill_kernel(Pre
   const int hk = bx / HG;
   const int hg = bx - hk * HG;
 
-  const SeqGeo geo = seq_geo<PS>(a, j);
+  if (zg != 0) geo = seq_geo<PS>(a, j);
   const int q_start = geo.q_start, Lq = geo.Lq, Lk = geo.Lk;
   if (Lq <= 1) {
     if constexpr (kOneRow) {
