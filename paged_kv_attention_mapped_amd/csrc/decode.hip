@@ -47,21 +47,20 @@ constexpr int occ(int o) { return D == 256 ? 1 : o; }
 template <int D, int PS, int G, bool SPLIT>
 __global__ __launch_bounds__(PKV_DECODE_WAVES * 64, occ<D>(PKV_DECODE_OCCUPANCY))
 void decode_kernel(DecodeArgs a) {
-  using W = WaveDecoder<D, PS, G, PKV_DECODE_UNIT, true>;
+  using W = RowDecoder<D, PS, G>;
   constexpr int NW = PKV_DECODE_WAVES;
   __shared__ float sm_m[NW][G];
   __shared__ float sm_l[NW][G];
-  __shared__ float sm_acc[NW][G][D];
-  // each wave's K rows pass through LDS into MFMA operand order
-  __shared__ __attribute__((aligned(16))) unsigned char sm_k[NW][W::UT * D * 2];
+  // each wave's K and V rows pass through LDS (RowDecoder); after its last
+  // step the wave's accumulator goes there, [G][D] floats
+  static_assert(G * D * 4 <= W::STAGE, "accumulator fits the stage");
+  __shared__ __attribute__((aligned(16))) unsigned char sm_st[NW][W::STAGE];
 
   const int s = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = a.group;
   W wd;
-  wd.init(lane);
-  wd.set_kstage(sm_k[w]);
-  wd.reset();
+  wd.init(lane, sm_st[w]);
   wd.load_q(a.q + ((int64_t)b * a.num_q_heads + hk * g) * D, g);
 
   const int Lraw = a.seq_lens[b];
@@ -101,7 +100,7 @@ void decode_kernel(DecodeArgs a) {
     row_of[slot] = row;
     const int t = L - 1 - tok_of[slot];
     tn_of[slot] = (fuse && ok_of[slot] && t >= 0 && t < W::UT) ? t : -1;
-    wd.load(bf, kh + row * D, vh + row * D);
+    wd.load(bf, kh + row * D, vh + row * D, true);
     // the row's new token: its lanes reload it from k_new / v_new (loads
     // return in issue order, so these land after the pool's)
     if (tn_of[slot] >= 0) {
@@ -129,16 +128,16 @@ void decode_kernel(DecodeArgs a) {
   }
 
   float M, lw;
-  wd.merge_rows(M, lw);
-  if (wd.jj == 0) {
-    if (wd.n < G) {
+  wd.finish(M, lw);
+  if (wd.n < G) {
+    if (wd.jj == 0) {
       sm_m[w][wd.n] = M;
       sm_l[w][wd.n] = lw;
     }
+    float* acc_w = reinterpret_cast<float*>(sm_st[w]);  // the wave is done with its stage
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < W::EPL; ++e) sm_acc[w][h][wd.dim_of(e)] = wd.acc[h][e];
+    for (int bb = 0; bb < W::DB; ++bb)
+      *reinterpret_cast<f32x4*>(acc_w + wd.n * D + 16 * bb + 4 * wd.jj) = wd.oacc[bb];
   }
   __syncthreads();
 
@@ -154,7 +153,7 @@ void decode_kernel(DecodeArgs a) {
         const float mw = sm_m[ww][h];
         if (mw == -INFINITY) continue;
         const float wt = fast_exp2(mw - Mx);
-        o = fmaf(wt, sm_acc[ww][h][d], o);
+        o = fmaf(wt, reinterpret_cast<const float*>(sm_st[ww])[h * D + d], o);
         lsum = fmaf(wt, sm_l[ww][h], lsum);
       }
     }

@@ -103,168 +103,10 @@ struct PrefillCfg {
   static_assert(QB >= 1, "more heads than waves");
 };
 
-// The wave decoder of a one-row sequence.  A step is 16 tokens of a page:
-//   S = K Q^T     v_mfma_f32_16x16x32_bf16 with K rows as A (read back from
-//                 LDS in operand order, row n of the tile being token
-//                 4(n%4) + n/4, so that score register r of lane row jj is
-//                 token 4r + jj) and the NH heads as columns;
-//   softmax       one running max and sum per head, the max taken over the
-//                 four lane rows (two exchanges per step);
-//   O^T += V^T P  v_mfma_f32_16x16x16_bf16 per 16 dims: lane (jj, n) holds
-//                 the probabilities of tokens jj, 4+jj, 8+jj, 12+jj for head
-//                 n, which is the B operand when k = 4jj + r stands for
-//                 token 4r + jj; V is staged row-major with token 4r + jj at
-//                 row 4jj + r, so one transposed read (ds_read_b64_tr_b16)
-//                 per 16 dims yields the matching A operand.
-// K and V arrive with whole-line loads (RPI rows per instruction) and go
-// through a per-wave LDS area, 16-byte chunks XOR-swizzled by row.  The
-// matrix cores take the PV products that would otherwise cost NH fused
-// multiply-adds per token and dim on the vector ALUs.
-template <int D, int PS, int NH>
-struct RowDecoder {
-  static constexpr int UT = 16;               // tokens per step
-  static constexpr int UPP = PS / UT;         // steps per page
-  static constexpr int KB = D / 32;           // k-steps of S
-  static constexpr int DB = D / 16;           // 16-dim blocks of O^T
-  static constexpr int CPR = D / 8;           // 16-byte chunks per row
-  static constexpr int RPI = 64 / CPR;        // rows per load instruction
-  static constexpr int NL = UT / RPI;         // load instructions per tensor per step
-  static constexpr int SWZ = CPR < 16 ? CPR - 1 : 15;
-  static constexpr int STAGE = 2 * UT * D * 2;  // LDS bytes per wave (K rows, V rows)
-  static_assert(NH <= 16 && PS % UT == 0 && UT % RPI == 0, "decoder shape");
-  struct Buf {
-    uint4 k[NL];
-    uint4 v[NL];
-  };
-
-  int jj, n, tok_a;
-  unsigned char* kst;
-  unsigned char* vst;
-  float m_run, l_run;
-  f32x4 oacc[DB];  // O^T: dims 16b + 4jj + r of head n
-  bf16x8 qop[KB];
-
-  __device__ __forceinline__ void init(int lane, unsigned char* stage) {
-    jj = lane >> 4;
-    n = lane & 15;
-    tok_a = 4 * (n & 3) + (n >> 2);
-    kst = stage;
-    vst = stage + UT * D * 2;
-    m_run = -INFINITY;
-    l_run = 0.f;
-#pragma unroll
-    for (int b = 0; b < DB; ++b) oacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  // Q^T as the B operand of S: lane (jj, n) holds q[head n][32kb + 8jj ..
-  // +7]; columns n >= NH are zero.
-  __device__ __forceinline__ void load_q(const uint16_t* qg) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (n < NH) v = *reinterpret_cast<const uint4*>(qg + n * D + 32 * kb + 8 * jj);
-      qop[kb] = as_bf16x8(v);
-    }
-  }
-
-  // The loads of one step (krow / vrow: its first token row).  With live
-  // false they go through an empty range: zeros, no memory read.
-  __device__ __forceinline__ void load(Buf& bf, const uint16_t* krow, const uint16_t* vrow,
-                                       bool live) const {
-    const auto kr = make_rsrc(krow, live ? UT * D * 2 : 0);
-    const auto vr = make_rsrc(vrow, live ? UT * D * 2 : 0);
-    const int lane = 16 * jj + n;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int off = 2 * ((RPI * i + lane / CPR) * D + 8 * (lane % CPR));
-      bf.k[i] = buffer_load16(kr, off);
-      bf.v[i] = buffer_load16(vr, off);
-    }
-  }
-
-  // Fold one step (tokens tok0 .. tok0+15; those outside [lo, hi) masked).
-  __device__ __forceinline__ void process(const Buf& bf, int tok0, int lo, int hi,
-                                          float scale_log2) {
-    const int lane = 16 * jj + n, c = lane % CPR;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int r = RPI * i + lane / CPR;
-      *reinterpret_cast<uint4*>(kst + r * (2 * D) + 16 * (c ^ (r & SWZ))) = bf.k[i];
-      const int pr = 4 * (r & 3) + (r >> 2);
-      *reinterpret_cast<uint4*>(vst + pr * (2 * D) + 16 * (c ^ (pr & SWZ))) = bf.v[i];
-    }
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const uint4 kop =
-          *reinterpret_cast<const uint4*>(kst + tok_a * (2 * D) + 16 * ((4 * kb + jj) ^ (tok_a & SWZ)));
-      sc = mfma16(as_bf16x8(kop), qop[kb], sc);
-    }
-    float x[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = sc[r] * scale_log2;
-    const bool partial = (tok0 < lo) || (tok0 + UT > hi);
-    uint32_t keep = 0xfu;
-    if (partial) {
-      keep = 0;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = tok0 + 4 * r + jj;
-        const bool ok = t >= lo && t < hi;
-        keep |= (ok ? 1u : 0u) << r;
-        x[r] = ok ? x[r] : -INFINITY;
-      }
-    }
-    float pmax = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-    pmax = fmaxf(pmax, __shfl_xor(pmax, 16));
-    pmax = fmaxf(pmax, __shfl_xor(pmax, 32));
-    const float m_new = fmaxf(m_run, pmax);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    float psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      x[r] = fast_exp2(x[r] - m_use);
-      psum += x[r];
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // p in [0, 1]: the hardware round-to-nearest conversion suffices
-    const bf16x2 p01 = {(__bf16)x[0], (__bf16)x[1]};
-    const bf16x2 p23 = {(__bf16)x[2], (__bf16)x[3]};
-    const s16x4 pop = __builtin_bit_cast(s16x4, make_uint2(__builtin_bit_cast(uint32_t, p01),
-                                                            __builtin_bit_cast(uint32_t, p23)));
-    // transposed reads: source lane n of lane row jj points at row
-    // 4jj + n/4, dims 16b + 4(n%4); lane n receives rows 4jj .. 4jj+3
-    // (tokens jj, 4+jj, 8+jj, 12+jj) of dim 16b + n
-    const int prow = 4 * jj + (n >> 2), a4 = n & 3;
-    unsigned char* vrow = vst + prow * (2 * D) + 8 * (a4 & 1);
-#pragma unroll
-    for (int b = 0; b < DB; ++b) {
-      s16x4 v4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4*)(__attribute__((address_space(3))) unsigned char*)(
-              vrow + 16 * ((2 * b + (a4 >> 1)) ^ (prow & SWZ))));
-      if (partial) {  // masked tokens' V rows may hold anything (NaN)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v4[r] = ((keep >> r) & 1u) ? v4[r] : (short)0;
-      }
-      oacc[b] *= alpha;
-      oacc[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v4, pop, oacc[b], 0, 0, 0);
-    }
-  }
-
-  // The step state after the last step: M (log2 units) and the sum of head
-  // n, the same in every lane row.
-  __device__ __forceinline__ void finish(float& M, float& lsum) const {
-    M = m_run;
-    lsum = l_run + __shfl_xor(l_run, 16);
-    lsum += __shfl_xor(lsum, 32);
-  }
-};
-
 // A sequence with a single query row (a decode row packed into the varlen
 // batch, or a one-token prompt): the workgroup's NW waves take the allowed
-// pages round-robin with RowDecoder (NH heads of one KV head) and merge
+// pages round-robin with RowDecoder (decode_core.h; NH heads of one KV
+// head) and merge
 // their softmax states through LDS, instead of running 32-row MFMA tiles
 // for one row.  A mixed batch of decode rows and prompts is thereby one
 // launch.
@@ -289,7 +131,7 @@ __device__ __forceinline__ void decode_row(const PrefillArgs& a, int j, int hk, 
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   W wd;
   wd.init(lane, kstage + w * W::STAGE);
-  wd.load_q(a.q + ((int64_t)q_row * a.num_q_heads + head0) * D);
+  wd.load_q(a.q + ((int64_t)q_row * a.num_q_heads + head0) * D, NH);
   const int first_key = a.window > 0 ? max(0, L - a.window) : 0;
   int p0 = pr.x, pend = pr.y;
   if (S > 1) {
