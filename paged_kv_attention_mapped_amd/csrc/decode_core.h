@@ -1,6 +1,7 @@
-// The per-wave decode machinery shared by the split-K and the stream-K
-// decode kernels: one wave attends the query-head group of one KV head over
-// a run of page steps and keeps an online softmax in registers.
+// The per-wave decode machinery of the stream-K decode kernel (WaveDecoder)
+// and of the direct decode kernel and the varlen kernel's one-row sequences
+// (RowDecoder, at the end): one wave attends the query-head group of one KV
+// head over a run of page steps and keeps an online softmax in registers.
 //
 // Layout of the work inside a wave.  A step is UT tokens of one page.
 //   * K is loaded in the A-operand layout of v_mfma_f32_16x16x32_bf16
@@ -44,12 +45,7 @@ __device__ __forceinline__ void unpack(const uint2& v, float* f) {
   f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
 }
 
-// KS: K is loaded with whole-line coalesced loads (each instruction covers
-// 1 KB of consecutive rows) and turned into MFMA operand order through a
-// per-wave LDS area (set_kstage) instead of being loaded in operand order,
-// where each instruction touches 16 rows x 64 bytes: those scattered
-// requests, not the bytes, set the pace of the vector memory path.
-template <int D, int PS, int G, int UT_, bool KS = false>
+template <int D, int PS, int G, int UT_>
 struct WaveDecoder {
   static constexpr int UT = UT_ < PS ? UT_ : PS;  // tokens per step
   static constexpr int UPP = PS / UT;             // steps per page
@@ -67,18 +63,10 @@ struct WaveDecoder {
     uint4 k[KT][KB];
     VChunk v[TPR][NCH];
   };
-  // staged K (KS): KT*KB whole-line loads per step, each RPI consecutive rows
-  static constexpr int CPR = D / 8;          // 16-byte chunks per row
-  static constexpr int RPI = 64 / CPR;       // rows per load instruction
-  static constexpr int SWZ = CPR < 16 ? CPR - 1 : 15;  // row bits XORed into the chunk position
-
   int jj, n, tok_a;
-  unsigned char* kst = nullptr;  // KS: this wave's UT*D*2 bytes of LDS
   float m_run, l_run;
   float acc[G][EPL];
   bf16x8 qop[KB];
-
-  __device__ __forceinline__ void set_kstage(unsigned char* p) { kst = p; }
 
   __device__ __forceinline__ void init(int lane) {
     jj = lane >> 4;
@@ -117,20 +105,11 @@ struct WaveDecoder {
                                        bool live = true) const {
     const auto kr = make_rsrc(krow, live ? UT * D * 2 : 0);
     const auto vr = make_rsrc(vrow, live ? UT * D * 2 : 0);
-    if constexpr (KS) {
-      // load i: rows RPI*i .. (lane / CPR picks the row), chunk lane % CPR
-      const int lane = 16 * jj + n;
 #pragma unroll
-      for (int i = 0; i < KT * KB; ++i)
-        bf.k[i / KB][i % KB] =
-            buffer_load16(kr, 2 * ((RPI * i + lane / CPR) * D + 8 * (lane % CPR)));
-    } else {
+    for (int ti = 0; ti < KT; ++ti)
 #pragma unroll
-      for (int ti = 0; ti < KT; ++ti)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          bf.k[ti][kb] = buffer_load16(kr, 2 * ((ti * 16 + tok_a) * D + 32 * kb + 8 * jj));
-    }
+      for (int kb = 0; kb < KB; ++kb)
+        bf.k[ti][kb] = buffer_load16(kr, 2 * ((ti * 16 + tok_a) * D + 32 * kb + 8 * jj));
 #pragma unroll
     for (int i = 0; i < TPR; ++i)
 #pragma unroll
@@ -143,34 +122,11 @@ struct WaveDecoder {
   __device__ __forceinline__ void process(const Buf& bf, int tok0, int lo, int hi,
                                           float scale_log2) {
     float x[TPR];
-    uint4 kop[KT][KB];
-    if constexpr (KS) {
-      // staged row r holds chunk c at 16-byte position c ^ (r & SWZ): the 16
-      // rows an operand read touches then fall on distinct banks
-      const int lane = 16 * jj + n;
-#pragma unroll
-      for (int i = 0; i < KT * KB; ++i) {
-        const int r = RPI * i + lane / CPR, c = lane % CPR;
-        *reinterpret_cast<uint4*>(kst + r * (2 * D) + 16 * (c ^ (r & SWZ))) = bf.k[i / KB][i % KB];
-      }
-#pragma unroll
-      for (int ti = 0; ti < KT; ++ti) {
-        const int r = 16 * ti + tok_a;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-          kop[ti][kb] = *reinterpret_cast<const uint4*>(kst + r * (2 * D) + 16 * ((4 * kb + jj) ^ (r & SWZ)));
-      }
-    } else {
-#pragma unroll
-      for (int ti = 0; ti < KT; ++ti)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kop[ti][kb] = bf.k[ti][kb];
-    }
 #pragma unroll
     for (int ti = 0; ti < KT; ++ti) {
       f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) c = mfma16(as_bf16x8(kop[ti][kb]), qop[kb], c);
+      for (int kb = 0; kb < KB; ++kb) c = mfma16(as_bf16x8(bf.k[ti][kb]), qop[kb], c);
 #pragma unroll
       for (int r = 0; r < 4; ++r) x[4 * ti + r] = c[r] * scale_log2;
     }
@@ -239,20 +195,11 @@ struct WaveDecoder {
                                          const uint16_t* vnew) const {
     const auto kr = make_rsrc(knew, D * 2);
     const auto vr = make_rsrc(vnew, D * 2);
-    if constexpr (KS) {
-      // staged layout: load i holds rows RPI*i .., lane l row RPI*i + l/CPR
-      const int lane = 16 * jj + n;
 #pragma unroll
-      for (int i = 0; i < KT * KB; ++i)
-        if (RPI * i + lane / CPR == tn)
-          bf.k[i / KB][i % KB] = buffer_load16(kr, 2 * 8 * (lane % CPR));
-    } else {
+    for (int ti = 0; ti < KT; ++ti)
+      if (16 * ti + tok_a == tn)
 #pragma unroll
-      for (int ti = 0; ti < KT; ++ti)
-        if (16 * ti + tok_a == tn)
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) bf.k[ti][kb] = buffer_load16(kr, 2 * (32 * kb + 8 * jj));
-    }
+        for (int kb = 0; kb < KB; ++kb) bf.k[ti][kb] = buffer_load16(kr, 2 * (32 * kb + 8 * jj));
 #pragma unroll
     for (int i = 0; i < TPR; ++i)
       if (4 * i + jj == tn)
@@ -266,18 +213,11 @@ struct WaveDecoder {
                                             uint16_t* vdst) const {
     const auto kr = make_rsrc(kdst, D * 2);
     const auto vr = make_rsrc(vdst, D * 2);
-    if constexpr (KS) {
-      const int lane = 16 * jj + n;
 #pragma unroll
-      for (int i = 0; i < KT * KB; ++i)
-        if (RPI * i + lane / CPR == tn) buffer_store(kr, 2 * 8 * (lane % CPR), bf.k[i / KB][i % KB]);
-    } else {
+    for (int ti = 0; ti < KT; ++ti)
+      if (16 * ti + tok_a == tn)
 #pragma unroll
-      for (int ti = 0; ti < KT; ++ti)
-        if (16 * ti + tok_a == tn)
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) buffer_store(kr, 2 * (32 * kb + 8 * jj), bf.k[ti][kb]);
-    }
+        for (int kb = 0; kb < KB; ++kb) buffer_store(kr, 2 * (32 * kb + 8 * jj), bf.k[ti][kb]);
 #pragma unroll
     for (int i = 0; i < TPR; ++i)
       if (4 * i + jj == tn)
