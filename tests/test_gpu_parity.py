@@ -240,6 +240,7 @@ DECODE_SHAPES = [  # name, Hq, Hkv, D, page, window
     ("d128_g7_p32", 7, 1, 128, 32, 0),
     ("d64_g8_p16", 8, 1, 64, 16, 0),
     ("d256_g6_p32_win", 6, 1, 256, 32, 200),
+    ("d256_g8_p16_kv2", 16, 2, 256, 16, 0),   # whole-group one-row workgroups, two KV heads
 ]
 
 
@@ -273,6 +274,13 @@ def test_decode_shapes(P, shape):
                            page_size=wl.page_size, scale=wl.scale, window=wl.window)
     torch.cuda.synchronize()
     check_close(host_bits(out), ref, f"{name} decode rows through the varlen entry")
+    # ... and cut into page runs by the split entry (partials merged)
+    out = P.prefill_varlen_split(dev_bits(qd), g.k, g.v, dev_i32(wl.block_tables[:wl.n_decode]),
+                                 dev_i32(wl.cu_lens(lq)), dev_i32(wl.cu_lens(lens)), 1,
+                                 int(lens.max()), page_size=wl.page_size, num_splits=3,
+                                 scale=wl.scale, window=wl.window)
+    torch.cuda.synchronize()
+    check_close(host_bits(out), ref, f"{name} decode rows through the split varlen entry")
 
 
 @pytest.mark.parametrize("name", ["mixed_step", "window_shared"])
